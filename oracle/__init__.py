@@ -1,0 +1,202 @@
+"""CPU reference ("oracle") for paged-KV decode attention and append.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library under ``paged_kv_cache_100_amd`` and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+output rows), compiled with gcc into ``liboracle.so`` next to it.  This module
+only marshals numpy arrays into that library.  ``brute.py`` holds a second,
+pure-Python statement of the same definition for tiny inputs, and the
+KV-cache size formula is ``kv_cache_bytes`` below (also computed in C).
+
+bf16 tensors cross this boundary as ``numpy.uint16`` arrays of raw bit
+patterns, so no rounding happens on the way in.
+
+Pins: every function here is checked in ``tests/test_oracle_*.py`` against
+facts printed on the pages (``tests/golden/``), closed forms, the pure-Python
+brute force, a library attention routine (torch CPU float64) and invariants,
+and a mutation test shows that each plausible slip in ``oracle.c`` fails at
+least one of those checks.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile ``src`` with gcc (-O2, OpenMP) into the shared library ``out``."""
+    stale = not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src)
+    if force or stale:
+        tmp = out + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                        "-Wall", "-Wextra", "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Open a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.oracle_append.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64]
+    lib.oracle_append.restype = i32
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, f32,
+                                  i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode.restype = i32
+    lib.oracle_decode_rows.argtypes = [P, P, P, i32, P, P, P, P, P, f32,
+                                       i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_rows.restype = i32
+    lib.oracle_decode_split.argtypes = [P, P, P, P, P, P, f32,
+                                        i32, i32, i32, i32, i32, i32, i64, i32,
+                                        P, P, P, i32]
+    lib.oracle_decode_split.restype = i32
+    lib.oracle_kv_cache_bytes.argtypes = [i64, i64, i64, i64, i64]
+    lib.oracle_kv_cache_bytes.restype = i64
+    return lib
+
+
+_default_lib = None
+
+
+def _load():
+    global _default_lib
+    if _default_lib is None:
+        _default_lib = load_library(build())
+    return _default_lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as(a, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def num_threads() -> int:
+    """Threads the OpenMP loops use (OMP_NUM_THREADS, else the affinity set)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def append(k, v, slot_mapping, key_cache, value_cache, lib=None) -> None:
+    """Bit copy of new K/V rows into the paged pools, in place.
+
+    k, v: uint16 [T, K, H]; slot_mapping: int64 [T] (negative = skip);
+    key_cache: uint16 [num_blocks, K, bs, H]; value_cache: uint16
+    [num_blocks, K, H, bs].  Raises ValueError on a slot outside the pool.
+    """
+    k = _as(k, np.uint16)
+    v = _as(v, np.uint16)
+    slot_mapping = _as(slot_mapping, np.int64)
+    if not (key_cache.flags.c_contiguous and value_cache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous (written in place)")
+    if key_cache.dtype != np.uint16 or value_cache.dtype != np.uint16:
+        raise TypeError("caches must be uint16 bit patterns")
+    T, K, H = k.shape
+    nb, K2, bs, H2 = key_cache.shape
+    if (K2, H2) != (K, H) or value_cache.shape != (nb, K, H, bs) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must have one entry per token")
+    rc = (lib or _load()).oracle_append(_ptr(k), _ptr(v), _ptr(slot_mapping),
+                                        _ptr(key_cache), _ptr(value_cache), T, K, H, bs, nb)
+    if rc:
+        raise ValueError("slot outside the pool")
+
+
+def _decode_args(q, key_cache, value_cache, block_tables, context_lens):
+    q = _as(q, np.uint16)
+    key_cache = _as(key_cache, np.uint16)
+    value_cache = _as(value_cache, np.uint16)
+    block_tables = _as(block_tables, np.int32)
+    context_lens = _as(context_lens, np.int32)
+    B, N, H = q.shape
+    nb, K, bs, H2 = key_cache.shape
+    if H2 != H or value_cache.shape != (nb, K, H, bs):
+        raise ValueError("cache shape mismatch")
+    if block_tables.ndim != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("table shape mismatch")
+    return q, key_cache, value_cache, block_tables, context_lens, (B, N, H, nb, K, bs)
+
+
+def _scratch(context_lens):
+    stride = max(1, int(context_lens.max()) if context_lens.size else 1)
+    return np.empty((num_threads() + 1) * stride, np.float64), stride
+
+
+def decode(q, key_cache, value_cache, block_tables, context_lens, scale,
+           lib=None) -> np.ndarray:
+    """softmax(q K^T * scale) V per (sequence, query head), float64 [B, N, H].
+
+    ``scale`` is an fp32 value (the library receives fp32); it is widened to
+    double exactly.  A sequence with context length 0 yields zeros.
+    """
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, key_cache, value_cache, block_tables, context_lens)
+    out = np.zeros((B, N, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode(
+        _ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(np.float32(scale)),
+        B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (block id, shape or context)")
+    return out
+
+
+def decode_rows(rows_b, rows_n, q, key_cache, value_cache, block_tables, context_lens,
+                scale, lib=None) -> np.ndarray:
+    """Rows (rows_b[r], rows_n[r]) of ``decode`` only, float64 [R, H]."""
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, key_cache, value_cache, block_tables, context_lens)
+    rb = _as(rows_b, np.int32)
+    rn = _as(rows_n, np.int32)
+    R = rb.shape[0]
+    out = np.zeros((R, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_rows(
+        _ptr(out), _ptr(rb), _ptr(rn), R, _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl),
+        float(np.float32(scale)), B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (row, block id, shape or context)")
+    return out
+
+
+def decode_split(q, key_cache, value_cache, block_tables, context_lens, scale,
+                 part: int, lib=None) -> np.ndarray:
+    """``decode`` computed piecewise over ``part``-token pieces + log-sum-exp merge."""
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, key_cache, value_cache, block_tables, context_lens)
+    out = np.zeros((B, N, H), np.float64)
+    max_pieces = max(1, -(-int(cl.max()) // part) if B else 1)
+    pm = np.empty(max_pieces, np.float64)
+    pl = np.empty(max_pieces, np.float64)
+    po = np.empty((max_pieces, H), np.float64)
+    rc = (lib or _load()).oracle_decode_split(
+        _ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), float(np.float32(scale)),
+        B, N, K, H, bs, bt.shape[1], nb, part, _ptr(pm), _ptr(pl), _ptr(po), max_pieces)
+    if rc:
+        raise ValueError("invalid decode arguments")
+    return out
+
+
+def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int,
+                   bytes_per_value: int = 2, lib=None) -> int:
+    """2 * L * K * H * S * bytes (KV-cache size formula), computed by the C oracle."""
+    return int((lib or _load()).oracle_kv_cache_bytes(layers, kv_heads, head_dim, tokens,
+                                                      bytes_per_value))

@@ -1,0 +1,78 @@
+"""Pure-Python brute force of decode attention and append, for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  A second statement of
+the definition, written independently of ``oracle.c``: plain nested loops over
+Python floats and ``math.exp``, with the block-table gather spelled out per
+position.  Sources:
+  * "Optimización de la inferencia" / "推理优化 (Inference Optimization)" lesson,
+    Build-It step 2 (attention with the KV cache): scaled scores, maximum
+    subtracted, exponentials normalised by their sum, weighted sum of V;
+  * same lesson, "PagedAttention" concept section, and "CS336 Lecture 10:
+    Inference", part 6: logical position t lives in block table[t // bs] at
+    offset t % bs;
+  * "CS336 Lecture 10: Inference", part 3 (GQA): N/K query heads per KV head.
+
+Inputs are Python lists/tuples of floats (already decoded from bf16) so that
+nothing here depends on the oracle's bit handling.
+"""
+from __future__ import annotations
+
+import math
+
+
+def attend_one(qrow, keys, values, scale):
+    """softmax(q . k_t * scale) weighted sum of v_t for one query row.
+
+    keys, values: lists of per-position vectors in logical order.
+    """
+    if not keys:
+        return [0.0] * len(qrow)
+    scores = [scale * sum(a * b for a, b in zip(qrow, k)) for k in keys]
+    top = max(scores)
+    weights = [math.exp(s - top) for s in scores]
+    total = sum(weights)
+    return [sum(w * v[h] for w, v in zip(weights, values)) / total
+            for h in range(len(qrow))]
+
+
+def paged_decode(q, key_cache, value_cache, block_tables, context_lens, scale):
+    """Decode attention with the block-table gather done position by position.
+
+    q[b][n][h]; key_cache[p][g][o][h]; value_cache[p][g][h][o];
+    block_tables[b][j]; context_lens[b].  Returns out[b][n][h].
+    """
+    B = len(q)
+    N = len(q[0]) if B else 0
+    K = len(key_cache[0]) if key_cache else 1
+    bs = len(key_cache[0][0]) if key_cache else 1
+    group = N // K
+    out = []
+    for b in range(B):
+        rows = []
+        for n in range(N):
+            g = n // group
+            keys, values = [], []
+            for t in range(context_lens[b]):
+                p = block_tables[b][t // bs]
+                o = t % bs
+                keys.append(list(key_cache[p][g][o]))
+                values.append([value_cache[p][g][h][o] for h in range(len(q[b][n]))])
+            rows.append(attend_one(q[b][n], keys, values, scale))
+        out.append(rows)
+    return out
+
+
+def paged_append(k, v, slot_mapping, key_cache, value_cache):
+    """Write k[i][g][:] / v[i][g][:] at slot_mapping[i]; negative slots skipped.
+
+    Caches are nested lists, modified in place (K rows; V columns).
+    """
+    bs = len(key_cache[0][0])
+    for i, s in enumerate(slot_mapping):
+        if s < 0:
+            continue
+        p, o = divmod(s, bs)
+        for g in range(len(k[i])):
+            for h in range(len(k[i][g])):
+                key_cache[p][g][o][h] = k[i][g][h]
+                value_cache[p][g][h][o] = v[i][g][h]

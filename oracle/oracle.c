@@ -1,0 +1,318 @@
+/*
+ * Plain CPU reference ("oracle") for paged-KV decode attention and the
+ * slot-mapped K/V append.  TEST INFRASTRUCTURE ONLY: the tests, the smoke
+ * check and the CPU-baseline leg of the benchmark call it; the product path
+ * never does.  It shares no code, header or constant with the HIP library.
+ *
+ * Everything is written as the plain definition, one output at a time, in
+ * double precision.  bf16 values are passed as their raw 16-bit patterns.
+ *
+ * What it follows:
+ *   - "Optimización de la inferencia" / "推理优化 (Inference Optimization)"
+ *     lesson, Build-It step 2 (attention with the KV cache): scores are
+ *     q.k divided by sqrt(head_dim), the row maximum is subtracted, the
+ *     exponentials are normalised by their sum, and the weights multiply V.
+ *     With a single query token no causal mask applies.
+ *   - same lesson, step 1 (KV cache from scratch): the new step's K/V are
+ *     written at the next position and the attention reads positions
+ *     [0, end).
+ *   - same lesson, "PagedAttention" concept section, and "CS336 Lecture 10:
+ *     Inference", part 6 (PagedAttention): the cache is split in fixed-size
+ *     blocks anywhere in memory, and a per-sequence table maps logical
+ *     block j of the sequence to a physical block.
+ *   - "CS336 Lecture 10: Inference", part 3 (GQA): each of the K key/value
+ *     heads serves N/K query heads.  Query head n uses KV head n / (N/K)
+ *     (consecutive grouping).
+ *
+ * Memory layouts (the pages leave them open; these are the library's):
+ *   key_cache   [num_blocks][K][block_size][H]   token rows of H values
+ *   value_cache [num_blocks][K][H][block_size]   one column per token
+ *   q           [B][N][H],  k/v new tokens [T][K][H]
+ *   block_tables[B][max_blocks_per_seq] int32, context_lens[B] int32
+ *   slot = physical_block * block_size + offset_in_block (int64)
+ *
+ * Return codes: 0 on success, -1 on an argument that makes the definition
+ * meaningless (a block id or slot outside the pool, N not divisible by K,
+ * a context longer than the block table).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int thread_id(void)
+{
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
+#endif
+}
+
+static double bf16_to_double(uint16_t bits)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Address of key element (block p, kv head g, offset o, dim h). */
+static size_t key_index(int64_t p, int g, int o, int h, int K, int bs, int H)
+{
+    return (((size_t)p * K + g) * bs + o) * H + h;
+}
+
+/* Address of value element (block p, kv head g, dim h, offset o). */
+static size_t value_index(int64_t p, int g, int h, int o, int K, int bs, int H)
+{
+    return (((size_t)p * K + g) * H + h) * bs + o;
+}
+
+/*
+ * Append (lesson step 1, in paged form): for each new token i whose slot is
+ * not negative, copy k[i][g][:] and v[i][g][:] bit for bit into the cache
+ * position (slot / bs, g, slot % bs).  Negative slots are padding and skipped.
+ */
+int oracle_append(const uint16_t *k, const uint16_t *v, const int64_t *slot_mapping,
+                  uint16_t *key_cache, uint16_t *value_cache,
+                  int T, int K, int H, int bs, int64_t num_blocks)
+{
+    for (int i = 0; i < T; i++) {
+        int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        if (s >= num_blocks * (int64_t)bs)
+            return -1;
+        int64_t p = s / bs;
+        int o = (int)(s % bs);
+        for (int g = 0; g < K; g++)
+            for (int h = 0; h < H; h++) {
+                size_t src = ((size_t)i * K + g) * H + h;
+                key_cache[key_index(p, g, o, h, K, bs, H)] = k[src];
+                value_cache[value_index(p, g, h, o, K, bs, H)] = v[src];
+            }
+    }
+    return 0;
+}
+
+/*
+ * One output row (sequence b, query head n): the definition of
+ * softmax(q K^T * scale) V over the sequence's ctx positions, gathering each
+ * position t through the block table.  `scores` is caller scratch of length
+ * ctx.  Writes H doubles to `row`.
+ */
+static int decode_row(double *row, double *scores,
+                      const uint16_t *q, const uint16_t *key_cache,
+                      const uint16_t *value_cache, const int32_t *block_tables,
+                      int ctx, int b, int n, float scale,
+                      int N, int K, int H, int bs, int max_blocks, int64_t num_blocks)
+{
+    int G = N / K;
+    int g = n / G;
+    const uint16_t *qrow = q + ((size_t)b * N + n) * H;
+    const int32_t *table = block_tables + (size_t)b * max_blocks;
+    double sc = (double)scale;
+
+    for (int h = 0; h < H; h++)
+        row[h] = 0.0;
+    if (ctx == 0)
+        return 0;
+
+    double m = -INFINITY;
+    for (int t = 0; t < ctx; t++) {
+        int64_t p = table[t / bs];
+        int o = t % bs;
+        if (p < 0 || p >= num_blocks)
+            return -1;
+        double dot = 0.0;
+        for (int h = 0; h < H; h++)
+            dot += bf16_to_double(qrow[h]) *
+                   bf16_to_double(key_cache[key_index(p, g, o, h, K, bs, H)]);
+        scores[t] = sc * dot;
+        if (scores[t] > m)
+            m = scores[t];
+    }
+    double z = 0.0;
+    for (int t = 0; t < ctx; t++) {
+        scores[t] = exp(scores[t] - m);
+        z += scores[t];
+    }
+    for (int t = 0; t < ctx; t++) {
+        int64_t p = table[t / bs];
+        int o = t % bs;
+        for (int h = 0; h < H; h++)
+            row[h] += scores[t] *
+                      bf16_to_double(value_cache[value_index(p, g, h, o, K, bs, H)]);
+    }
+    for (int h = 0; h < H; h++)
+        row[h] /= z;
+    return 0;
+}
+
+static int check_shape(const int32_t *context_lens, int B, int N, int K, int bs,
+                       int max_blocks)
+{
+    if (B < 0 || N <= 0 || K <= 0 || N % K != 0 || bs <= 0 || max_blocks < 0)
+        return -1;
+    for (int b = 0; b < B; b++)
+        if (context_lens[b] < 0 || context_lens[b] > (int64_t)max_blocks * bs)
+            return -1;
+    return 0;
+}
+
+/*
+ * Decode attention for every (sequence, query head): out[b][n][h], double.
+ * `scratch` must hold max(context_lens) doubles per OpenMP thread; the
+ * Python wrapper allocates it.
+ */
+int oracle_decode(double *out, const uint16_t *q, const uint16_t *key_cache,
+                  const uint16_t *value_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, float scale,
+                  int B, int N, int K, int H, int bs, int max_blocks,
+                  int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    if (check_shape(context_lens, B, N, K, bs, max_blocks))
+        return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int r = 0; r < B * N; r++) {
+        int b = r / N, n = r % N;
+        int tid = thread_id();
+        if (context_lens[b] > scratch_stride) {
+            status |= 1;
+            continue;
+        }
+        status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
+                             q, key_cache, value_cache, block_tables, context_lens[b],
+                             b, n, scale, N, K, H, bs, max_blocks, num_blocks) != 0;
+    }
+    return status ? -1 : 0;
+}
+
+/*
+ * The same rows, but only the R (b, n) pairs listed: lets a test check
+ * sampled outputs of a workload too large to recompute whole.
+ */
+int oracle_decode_rows(double *out_rows, const int32_t *rows_b, const int32_t *rows_n, int R,
+                       const uint16_t *q, const uint16_t *key_cache,
+                       const uint16_t *value_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale,
+                       int B, int N, int K, int H, int bs, int max_blocks,
+                       int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    if (check_shape(context_lens, B, N, K, bs, max_blocks))
+        return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int r = 0; r < R; r++) {
+        int b = rows_b[r], n = rows_n[r];
+        int tid = thread_id();
+        if (b < 0 || b >= B || n < 0 || n >= N || context_lens[b] > scratch_stride) {
+            status |= 1;
+            continue;
+        }
+        status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
+                             q, key_cache, value_cache, block_tables, context_lens[b],
+                             b, n, scale, N, K, H, bs, max_blocks, num_blocks) != 0;
+    }
+    return status ? -1 : 0;
+}
+
+/*
+ * Split-context form of the same result, used to pin the log-sum-exp merge
+ * ("CS336 Lecture 10: Inference", part 6, names FlashDecoding: the context
+ * is cut into pieces that are reduced separately and then combined).
+ * Piece j covers positions [j*part, min((j+1)*part, ctx)).  For each piece
+ * the oracle keeps its own maximum m_j, sum l_j = sum exp(s - m_j) and
+ * unnormalised o_j = sum exp(s - m_j) v; the pieces are then combined with
+ * M = max m_j, w_j = exp(m_j - M), out = sum w_j o_j / sum w_j l_j.
+ * Only used on small inputs; loops are serial.
+ */
+int oracle_decode_split(double *out, const uint16_t *q, const uint16_t *key_cache,
+                        const uint16_t *value_cache, const int32_t *block_tables,
+                        const int32_t *context_lens, float scale,
+                        int B, int N, int K, int H, int bs, int max_blocks,
+                        int64_t num_blocks, int part,
+                        double *piece_m, double *piece_l, double *piece_o, int max_pieces)
+{
+    if (check_shape(context_lens, B, N, K, bs, max_blocks) || part <= 0)
+        return -1;
+    int G = N / K;
+    double sc = (double)scale;
+    for (int b = 0; b < B; b++) {
+        int ctx = context_lens[b];
+        int pieces = (ctx + part - 1) / part;
+        if (pieces > max_pieces)
+            return -1;
+        const int32_t *table = block_tables + (size_t)b * max_blocks;
+        for (int n = 0; n < N; n++) {
+            int g = n / G;
+            const uint16_t *qrow = q + ((size_t)b * N + n) * H;
+            double *row = out + ((size_t)b * N + n) * H;
+            for (int j = 0; j < pieces; j++) {
+                int t0 = j * part, t1 = t0 + part < ctx ? t0 + part : ctx;
+                double m = -INFINITY;
+                for (int t = t0; t < t1; t++) {
+                    int64_t p = table[t / bs];
+                    if (p < 0 || p >= num_blocks)
+                        return -1;
+                    double dot = 0.0;
+                    for (int h = 0; h < H; h++)
+                        dot += bf16_to_double(qrow[h]) *
+                               bf16_to_double(key_cache[key_index(p, g, t % bs, h, K, bs, H)]);
+                    if (sc * dot > m)
+                        m = sc * dot;
+                }
+                double l = 0.0;
+                double *o = piece_o + (size_t)j * H;
+                for (int h = 0; h < H; h++)
+                    o[h] = 0.0;
+                for (int t = t0; t < t1; t++) {
+                    int64_t p = table[t / bs];
+                    double dot = 0.0;
+                    for (int h = 0; h < H; h++)
+                        dot += bf16_to_double(qrow[h]) *
+                               bf16_to_double(key_cache[key_index(p, g, t % bs, h, K, bs, H)]);
+                    double w = exp(sc * dot - m);
+                    l += w;
+                    for (int h = 0; h < H; h++)
+                        o[h] += w * bf16_to_double(
+                                        value_cache[value_index(p, g, h, t % bs, K, bs, H)]);
+                }
+                piece_m[j] = m;
+                piece_l[j] = l;
+            }
+            double M = -INFINITY;
+            for (int j = 0; j < pieces; j++)
+                if (piece_m[j] > M)
+                    M = piece_m[j];
+            double L = 0.0;
+            for (int h = 0; h < H; h++)
+                row[h] = 0.0;
+            for (int j = 0; j < pieces; j++) {
+                double w = exp(piece_m[j] - M);
+                L += w * piece_l[j];
+                for (int h = 0; h < H; h++)
+                    row[h] += w * piece_o[(size_t)j * H + h];
+            }
+            if (pieces > 0)
+                for (int h = 0; h < H; h++)
+                    row[h] /= L;
+        }
+    }
+    return 0;
+}
+
+/*
+ * KV-cache size formula, "Optimización de la inferencia" lesson, KV-cache
+ * concept section (and "Week 11. Inference", step 2): bytes =
+ * 2 (K and V) * layers * kv_heads * head_dim * tokens * bytes_per_value.
+ */
+int64_t oracle_kv_cache_bytes(int64_t layers, int64_t kv_heads, int64_t head_dim,
+                              int64_t tokens, int64_t bytes_per_value)
+{
+    return 2 * layers * kv_heads * head_dim * tokens * bytes_per_value;
+}

@@ -1,0 +1,339 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each ``check_*`` function raises AssertionError (or ValueError from the
+oracle's own argument checks) when the oracle library ``lib`` is wrong, and
+returns None otherwise.  ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutations.py`` runs them on deliberately broken copies of the
+oracle's C source to show that every plausible slip fails at least one.
+
+What each check compares against:
+  * the pure-Python brute force (``oracle/brute.py``), an independent
+    statement of the definition;
+  * torch's CPU float64 ``scaled_dot_product_attention`` (a library routine)
+    on K/V gathered into contiguous form -- the contiguous cache of the
+    "Optimización de la inferencia" lesson, Build-It steps 1-2;
+  * closed forms: one cached token returns its V; equal keys return the
+    mean of V; shifting every key by one vector, or V by a constant, moves the
+    output as the algebra says;
+  * invariances of paging: relabelling physical blocks, and sharing prefix
+    blocks instead of copying them, change nothing ("CS336 Lecture 10:
+    Inference", part 6; PagedAttention section of the lesson);
+  * GQA equals MHA with each KV head repeated N/K times ("CS336 Lecture 10:
+    Inference", part 3);
+  * the KV-cache sizes printed on the pages (``tests/golden``).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from oracle import brute
+
+from _util import bits_to_f64
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "kv_cache_facts.json")
+SPARE_BLOCKS = 2   # unreferenced pool blocks, so a wrong index stays inside the arrays
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """Round float values to bf16 (round-to-nearest-even via torch) -> bits."""
+    t = torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+class Case:
+    """A small paged decode problem with its tables drawn from a permutation."""
+
+    def __init__(self, seed, B=3, N=4, K=2, H=8, bs=4, ctx=None, max_ctx=40,
+                 grid=False, key_mult=1.0):
+        rng = np.random.default_rng(seed)
+        self.B, self.N, self.K, self.H, self.bs = B, N, K, H, bs
+        self.ctx = (np.array(ctx, np.int32) if ctx is not None
+                    else rng.integers(1, max_ctx + 1, B).astype(np.int32))
+        nblk = [-(-int(c) // bs) for c in self.ctx]
+        self.max_blocks = max([1] + nblk)
+        pool = sum(nblk) + 3
+        self.num_blocks = pool + SPARE_BLOCKS
+        perm = rng.permutation(pool)
+        self.tables = np.full((B, self.max_blocks), -1, np.int32)
+        i = 0
+        for b in range(B):
+            for j in range(nblk[b]):
+                self.tables[b, j] = perm[i]
+                i += 1
+
+        def draw(shape, mult=1.0):
+            if grid:   # multiples of 1/8 in [-4, 4]: sums with small integers stay exact
+                return to_bf16_bits(rng.integers(-32, 33, shape) / 8.0 * mult)
+            return to_bf16_bits(rng.standard_normal(shape) * mult)
+
+        self.q = draw((B, N, H))
+        self.kc = draw((self.num_blocks, K, bs, H), key_mult)
+        self.vc = draw((self.num_blocks, K, H, bs))
+        self.scale = float(np.float32(1.0 / math.sqrt(H)))
+
+    def args(self):
+        return (self.q, self.kc, self.vc, self.tables, self.ctx, self.scale)
+
+    def decode(self, lib):
+        return oracle.decode(*self.args(), lib=lib)
+
+    def brute(self, scale=None):
+        q = bits_to_f64(self.q).tolist()
+        kc = bits_to_f64(self.kc).tolist()
+        vc = bits_to_f64(self.vc).tolist()
+        return np.array(brute.paged_decode(q, kc, vc, self.tables.tolist(), self.ctx.tolist(),
+                                           self.scale if scale is None else scale))
+
+    def contiguous(self):
+        """K, V gathered per sequence into [ctx, K, H] float64 arrays."""
+        kf, vf = bits_to_f64(self.kc), bits_to_f64(self.vc)
+        out = []
+        for b in range(self.B):
+            t = np.arange(self.ctx[b])
+            p = self.tables[b, t // self.bs]
+            o = t % self.bs
+            out.append((kf[p, :, o, :], vf[p, :, :, o]))   # both [ctx, K, H]
+        return out
+
+
+def assert_close(a, b, tol, what):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- decode ----
+
+def check_brute_force(lib):
+    for seed, (N, K, bs, H) in enumerate([(4, 2, 4, 8), (4, 4, 16, 8), (6, 1, 4, 4),
+                                           (8, 2, 16, 16)]):
+        c = Case(seed, N=N, K=K, bs=bs, H=H, max_ctx=40)
+        assert_close(c.decode(lib), c.brute(), 1e-12, f"brute force (N={N},K={K},bs={bs})")
+
+
+def check_library_sdpa(lib):
+    c = Case(11, B=4, N=8, K=2, H=16, bs=16, max_ctx=70)
+    got = c.decode(lib)
+    G = c.N // c.K
+    for b, (k, v) in enumerate(c.contiguous()):
+        q = torch.from_numpy(bits_to_f64(c.q[b]))[:, None, :]                   # [N, 1, H]
+        kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)   # [N, ctx, H]
+        vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, scale=c.scale)
+        assert_close(got[b], ref[:, 0, :].numpy(), 1e-12, f"library SDPA, sequence {b}")
+
+
+def check_single_token_returns_v(lib):
+    c = Case(21, B=4, N=4, K=2, H=8, bs=4, ctx=[1, 1, 1, 1])
+    got = c.decode(lib)
+    vf = bits_to_f64(c.vc)
+    for b in range(c.B):
+        for n in range(c.N):
+            want = vf[c.tables[b, 0], n // (c.N // c.K), :, 0]
+            assert np.array_equal(got[b, n], want), "context length 1 must return V exactly"
+
+
+def check_equal_keys_mean_v(lib):
+    c = Case(31, B=2, N=4, K=2, H=8, bs=4, ctx=[13, 29])
+    c.kc[:] = c.kc[0, 0, 0][None, None, None, :]   # every key equal
+    got = c.decode(lib)
+    for b, (k, v) in enumerate(c.contiguous()):
+        for n in range(c.N):
+            g = n // (c.N // c.K)
+            assert_close(got[b, n], v[:, g, :].mean(axis=0), 1e-13, "equal keys -> mean of V")
+
+
+def check_empty_context(lib):
+    c = Case(41, B=3, ctx=[0, 5, 0])
+    got = c.decode(lib)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0), "context 0 must give zeros"
+    assert np.all(np.isfinite(got[1]))
+
+
+def check_block_permutation(lib):
+    c = Case(51, B=3, N=4, K=2, H=8, bs=4, max_ctx=30)
+    base = c.decode(lib)
+    rng = np.random.default_rng(5)
+    relabel = rng.permutation(c.num_blocks)            # old id -> new id
+    kc, vc = np.empty_like(c.kc), np.empty_like(c.vc)
+    kc[relabel], vc[relabel] = c.kc, c.vc
+    tables = np.where(c.tables >= 0, relabel[np.maximum(c.tables, 0)], -1).astype(np.int32)
+    got = oracle.decode(c.q, kc, vc, tables, c.ctx, c.scale, lib=lib)
+    assert np.array_equal(got, base), "relabelling physical blocks changed the output"
+
+
+def check_prefix_sharing(lib):
+    """Sequences 1 and 2 reuse sequence 0's first three blocks (shared) versus
+    private copies of them: identical outputs."""
+    c = Case(61, B=3, N=4, K=2, H=8, bs=4, ctx=[12, 21, 17])
+    shared = c.tables[0, :3].copy()
+    for b in (1, 2):   # give them private copies first, equal to the shared blocks
+        c.kc[c.tables[b, :3]] = c.kc[shared]
+        c.vc[c.tables[b, :3]] = c.vc[shared]
+    private = c.decode(lib)
+    t2 = c.tables.copy()
+    t2[1, :3] = shared
+    t2[2, :3] = shared
+    got = oracle.decode(c.q, c.kc, c.vc, t2, c.ctx, c.scale, lib=lib)
+    assert np.array_equal(got, private), "shared prefix blocks differ from private copies"
+
+
+def check_gqa_is_repeated_mha(lib):
+    c = Case(71, B=2, N=8, K=2, H=8, bs=4, max_ctx=25)
+    G = c.N // c.K
+    got = c.decode(lib)
+    kc = np.repeat(c.kc, G, axis=1)    # KV head g copied to heads g*G .. g*G+G-1
+    vc = np.repeat(c.vc, G, axis=1)
+    mha = oracle.decode(c.q, kc, vc, c.tables, c.ctx, c.scale, lib=lib)
+    assert np.array_equal(got, mha), "GQA differs from MHA with repeated KV heads"
+
+
+def check_key_shift(lib):
+    c = Case(81, B=2, N=4, K=2, H=8, bs=4, ctx=[9, 23], grid=True)
+    base = c.decode(lib)
+    shift = np.array([2, -1, 0, 1, -2, 1, 0, -1], np.float64)
+    kf = bits_to_f64(c.kc) + shift
+    kc = to_bf16_bits(kf)
+    assert np.array_equal(bits_to_f64(kc), kf)
+    got = oracle.decode(c.q, kc, c.vc, c.tables, c.ctx, c.scale, lib=lib)
+    assert_close(got, base, 1e-12, "adding one vector to every key")
+
+
+def check_value_affine(lib):
+    c = Case(91, B=2, N=4, K=2, H=8, bs=4, ctx=[7, 30], grid=True)
+    base = c.decode(lib)
+    vf = bits_to_f64(c.vc)
+    twice = oracle.decode(c.q, c.kc, to_bf16_bits(vf * 2), c.tables, c.ctx, c.scale, lib=lib)
+    assert np.array_equal(twice, base * 2), "doubling V must double the output"
+    moved = oracle.decode(c.q, c.kc, to_bf16_bits(vf + 3), c.tables, c.ctx, c.scale, lib=lib)
+    assert_close(moved, base + 3, 1e-12, "V + 3")
+    const = oracle.decode(c.q, c.kc, to_bf16_bits(np.full_like(vf, -1.25)), c.tables, c.ctx,
+                          c.scale, lib=lib)
+    assert_close(const, np.full_like(base, -1.25), 1e-14, "constant V")
+
+
+def check_large_logits(lib):
+    """Scores near +-1000: only a max-subtracted softmax stays finite."""
+    c = Case(101, B=2, N=4, K=2, H=8, bs=4, ctx=[11, 19], key_mult=4.0)
+    big = 60.0
+    got = oracle.decode(c.q, c.kc, c.vc, c.tables, c.ctx, big, lib=lib)
+    assert_close(got, c.brute(scale=big), 1e-9, "large logits")
+
+
+def check_scale_is_used(lib):
+    c = Case(111, B=2, N=4, K=2, H=16, bs=4, ctx=[15, 26])
+    got = c.decode(lib)
+    exact = c.brute(scale=1.0 / math.sqrt(c.H))     # the pages divide by sqrt(head_dim)
+    assert_close(got, exact, 1e-6, "scale 1/sqrt(H)")
+
+
+def check_split_merge(lib):
+    c = Case(121, B=4, N=4, K=2, H=8, bs=4, ctx=[1, 17, 40, 64])
+    whole = c.decode(lib)
+    for part in (1, 3, 16, 64, 100):
+        got = oracle.decode_split(*c.args(), part, lib=lib)
+        assert_close(got, whole, 1e-12, f"split into {part}-token pieces")
+
+
+def check_rows(lib):
+    c = Case(131, B=3, N=4, K=2, H=8, bs=4, max_ctx=30)
+    whole = c.decode(lib)
+    rb = np.array([2, 0, 1, 2], np.int32)
+    rn = np.array([3, 1, 0, 0], np.int32)
+    got = oracle.decode_rows(rb, rn, *c.args(), lib=lib)
+    assert np.array_equal(got, whole[rb, rn]), "row sampling differs from the full decode"
+
+
+# ---------------------------------------------------------------- append ----
+
+def _append_case(seed):
+    rng = np.random.default_rng(seed)
+    T, K, H, bs, nb = 5, 2, 8, 4, 9
+    k = to_bf16_bits(rng.standard_normal((T, K, H)))
+    v = to_bf16_bits(rng.standard_normal((T, K, H)))
+    slots = np.array([13, 0, -1, 35, 22], np.int64)
+    sentinel = np.uint16(0x7FA1)      # a NaN pattern no input can produce
+    kc = np.full((nb, K, bs, H), sentinel, np.uint16)
+    vc = np.full((nb, K, H, bs), sentinel, np.uint16)
+    return k, v, slots, kc, vc, sentinel
+
+
+def check_append_vs_brute(lib):
+    k, v, slots, kc, vc, sentinel = _append_case(141)
+    bk, bv = kc.astype(np.int64).tolist(), vc.astype(np.int64).tolist()
+    brute.paged_append(k.astype(np.int64).tolist(), v.astype(np.int64).tolist(),
+                       slots.tolist(), bk, bv)
+    oracle.append(k, v, slots, kc, vc, lib=lib)
+    assert np.array_equal(kc, np.array(bk, np.uint16)), "K append differs from brute force"
+    assert np.array_equal(vc, np.array(bv, np.uint16)), "V append differs from brute force"
+
+
+def check_append_skips_and_untouched(lib):
+    k, v, slots, kc, vc, sentinel = _append_case(151)
+    oracle.append(k, v, slots, kc, vc, lib=lib)
+    bs = kc.shape[2]
+    written = {int(s) for s in slots if s >= 0}
+    for blk in range(kc.shape[0]):
+        for o in range(bs):
+            s = blk * bs + o
+            if s in written:
+                continue
+            assert np.all(kc[blk, :, o, :] == sentinel), f"slot {s} of K touched"
+            assert np.all(vc[blk, :, :, o] == sentinel), f"slot {s} of V touched"
+    i = int(np.nonzero(slots == 35)[0][0])
+    assert np.array_equal(kc[35 // bs, :, 35 % bs, :], k[i])
+    assert np.array_equal(vc[35 // bs, :, :, 35 % bs], v[i])
+
+
+def check_append_then_decode_is_contiguous_update(lib):
+    """Paged append + decode equals the lesson's contiguous cache: write the new
+    K/V at position seq_len, then attend over positions [0, seq_len + 1)."""
+    c = Case(161, B=2, N=4, K=2, H=8, bs=4, ctx=[10, 19])
+    rng = np.random.default_rng(7)
+    k_new = to_bf16_bits(rng.standard_normal((c.B, c.K, c.H)))
+    v_new = to_bf16_bits(rng.standard_normal((c.B, c.K, c.H)))
+    last = c.ctx - 1
+    slots = np.array([c.tables[b, last[b] // c.bs] * c.bs + last[b] % c.bs
+                      for b in range(c.B)], np.int64)
+    before = c.contiguous()
+    oracle.append(k_new, v_new, slots, c.kc, c.vc, lib=lib)
+    got = c.decode(lib)
+    G = c.N // c.K
+    for b in range(c.B):
+        k, v = (a.copy() for a in before[b])     # contiguous [ctx, K, H]
+        k[last[b]] = bits_to_f64(k_new[b])
+        v[last[b]] = bits_to_f64(v_new[b])
+        q = torch.from_numpy(bits_to_f64(c.q[b]))[:, None, :]
+        kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q, kk, vv, scale=c.scale)
+        assert_close(got[b], ref[:, 0, :].numpy(), 1e-12, "append then decode")
+
+
+# ------------------------------------------------------------ accounting ----
+
+def check_printed_kv_sizes(lib):
+    facts = json.load(open(GOLDEN))
+    for f in facts["facts"]:
+        got = oracle.kv_cache_bytes(f["layers"], f["kv_heads"], f["head_dim"], f["tokens"],
+                                    f["bytes"], lib=lib)
+        assert got == f["exact"], f"{f['id']}: {got} != {f['exact']}"
+        shown = got / f["unit"]
+        assert abs(shown - f["printed"]) <= f["rel_tol"] * f["printed"] + 1e-12, \
+            f"{f['id']}: {shown} does not round to the printed {f['printed']}"
+    for r in facts["gqa_reduction"]:
+        mha = oracle.kv_cache_bytes(1, r["N"], 128, 1, 2, lib=lib)
+        gqa = oracle.kv_cache_bytes(1, r["K"], 128, 1, 2, lib=lib)
+        assert mha == r["factor"] * gqa
+
+
+ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

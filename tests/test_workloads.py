@@ -1,0 +1,113 @@
+"""The seeded input generator: shapes, determinism, paging structure.
+
+These checks are about the inputs only; they involve no attention arithmetic.
+The block-table structure is checked with plain set logic here, independently
+of how the generator builds it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_100_amd import workloads as W
+
+from _util import bits
+
+
+def test_full_size_layouts():
+    # Llama-3-8B: 64 x 8192 tokens, pool sized exactly to the batch (no spare).
+    lay = W.layout("llama3_8b_b64_ctx8k")
+    assert lay.context_lens == [8192] * 64
+    assert lay.num_blocks == 64 * 512 and lay.poison_block is None
+    ids = lay.block_tables.flatten().tolist()
+    assert sorted(ids) == list(range(64 * 512))          # a permutation of the pool
+    # 128K context: 4 x 8192 blocks.
+    lay = W.layout("llama3_70b_long_b4_ctx128k")
+    assert lay.block_tables.shape == (4, 8192) and lay.num_blocks == 32768
+    assert lay.spec.partition_size == 512
+    # 13B MHA batch sweep.
+    for B in (1, 64, 256):
+        lay = W.layout(f"llama2_13b_b{B}_ctx1k")
+        assert lay.block_tables.shape == (B, 64) and lay.num_blocks == 64 * B
+
+
+def test_ragged_shared_prefix_layout():
+    lay = W.layout("llama3_70b_ragged_b100")
+    ctx = np.array(lay.context_lens)
+    assert ctx.min() >= 16 and ctx.max() <= 8192
+    # median 2000 before clipping; the sample median stays near it
+    assert 1000 < np.median(ctx) < 4000
+    assert len(lay.sharer_ids) == 20
+    shared = lay.block_tables[lay.sharer_ids[0], :62].tolist()
+    for b in lay.sharer_ids:
+        assert ctx[b] > 1000
+        assert lay.block_tables[b, :62].tolist() == shared     # 62 whole blocks shared
+    # every other referenced block id appears exactly once
+    seen = {}
+    for b in range(100):
+        n = -(-int(ctx[b]) // 16)
+        for j in range(n):
+            if b in lay.sharer_ids and j < 62:
+                continue
+            pid = int(lay.block_tables[b, j])
+            assert pid not in seen and pid not in shared
+            seen[pid] = (b, j)
+    assert len(seen) + 62 == lay.num_blocks - 1                  # +1: the poison block
+    # the new token of every sequence lands in a private block
+    for b in range(100):
+        assert int(lay.slot_mapping[b]) // 16 not in shared
+
+
+def test_deterministic_and_layout_matches_make():
+    spec = W.small("llama3_70b_ragged_b100")
+    a, b = W.make(spec), W.make(spec)
+    for f in ("q", "k_new", "v_new", "key_cache", "value_cache"):
+        assert torch.equal(getattr(a, f).view(torch.int16), getattr(b, f).view(torch.int16))
+    lay = W.layout(spec)
+    assert torch.equal(lay.block_tables, a.block_tables)
+    assert torch.equal(lay.slot_mapping, a.slot_mapping)
+
+
+@pytest.mark.parametrize("name", sorted(W.SPECS))
+def test_small_variants(name):
+    w = W.make(W.small(name))
+    s = w.spec
+    assert w.q.shape == (s.B, s.N, s.H) and w.q.dtype == torch.bfloat16
+    assert w.key_cache.shape == (w.num_blocks, s.K, s.bs, s.H)
+    assert w.value_cache.shape == (w.num_blocks, s.K, s.H, s.bs)
+    ctx = w.context_lens.tolist()
+    for b in range(s.B):
+        last = ctx[b] - 1
+        slot = int(w.slot_mapping[b])
+        assert slot // s.bs == int(w.block_tables[b, last // s.bs]) and slot % s.bs == last % s.bs
+
+
+def test_poison_marks_every_unused_slot():
+    w = W.make(W.small("llama3_70b_ragged_b100"))
+    kb = bits(w.key_cache)
+    vb = bits(w.value_cache)
+    bs = w.spec.bs
+    valid = set()
+    for b, c in enumerate(w.context_lens.tolist()):
+        for t in range(c - 1):                       # the new token is not yet in the cache
+            valid.add(int(w.block_tables[b, t // bs]) * bs + t % bs)
+    for blk in range(w.num_blocks):
+        for o in range(bs):
+            poisoned = blk * bs + o not in valid
+            assert np.all(kb[blk, :, o, :] == W.BF16_NAN_BITS) == poisoned
+            assert np.all(vb[blk, :, :, o] == W.BF16_NAN_BITS) == poisoned
+
+
+def test_key_scaling_is_exact():
+    w = W.make(W.small("llama3_70b_ragged_b100"))
+    assert w.spec.key_scale == 2.0
+    k = w.k_new.float()
+    assert torch.equal((k / 2).to(torch.bfloat16).float() * 2, k)
+
+
+def test_workload_kv_bytes_match_oracle_formula():
+    # one layer of Llama-3-8B at B=64 x 8192: 2 GiB of K+V
+    lay = W.layout("llama3_8b_b64_ctx8k")
+    s = lay.spec
+    total = sum(oracle.kv_cache_bytes(1, s.K, s.H, c) for c in lay.context_lens)
+    assert total == 2 * 1024 ** 3
