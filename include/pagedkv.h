@@ -1,0 +1,188 @@
+/*
+ * pagedkv.h -- C ABI of the paged-KV decode-attention library (libpagedkv.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations make one decode step of one attention layer:
+ *
+ *   paged_kv_append         writes the step's new K/V rows into the paged
+ *                           cache at slot-mapped positions;
+ *   paged_decode_attention  computes, for every sequence and query head,
+ *                           softmax(q . K^T * scale) . V over the sequence's
+ *                           cached positions, gathered through its block table.
+ *
+ * What they compute is defined on these pages:
+ *   - "Optimización de la inferencia" (AI Engineering from Scratch, phase 10,
+ *     lesson 12; the same lesson in Chinese as "推理优化 (Inference
+ *     Optimization)"), Build-It step 1 (a KV cache: new keys/values are
+ *     written at the next position, attention reads every position so far)
+ *     and step 2 (attention with the cache: scaled scores, maximum
+ *     subtracted, normalised exponentials, weighted sum of V; one query token
+ *     needs no causal mask); and its PagedAttention section (the cache lives
+ *     in fixed-size pages anywhere in GPU memory, found through a
+ *     per-request page table, pages of 16 tokens being typical).
+ *   - "CS336 Lecture 10: Inference", part 1 (notation B, N, K, H; generation
+ *     attention reads the whole cache for one query token per sequence and is
+ *     memory bound), part 3 (GQA: each of K KV heads serves N/K query heads)
+ *     and part 6 (PagedAttention blocks, shared prefix blocks, a kernel that
+ *     fuses the block reads with attention).
+ *   - "Week 11. Inference", step 2 (a new token computes only its own q, k, v
+ *     and attends to the stored ones).
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer (HIP global memory) unless
+ *     stated otherwise.  The caller owns all memory; the library allocates
+ *     nothing and keeps no state except a per-device attribute cache.
+ *   - bf16 data is passed as raw 16-bit patterns (type-erased `void*`).
+ *   - `stream` is a hipStream_t passed as `void*` (NULL = the null stream).
+ *     Calls only enqueue work on that stream; they never synchronise, so
+ *     buffers must stay alive until the stream has run the work.
+ *   - Every argument check happens on the host before any launch.  The return
+ *     value is PKV_OK (0) or a negative pkv_status; nothing is enqueued when
+ *     a check fails.  Values stored in device memory (block ids, slots,
+ *     context lengths) cannot be checked without a device-to-host copy; the
+ *     kernels clamp them to stay inside the buffers, as documented per call,
+ *     but the numeric result for such a sequence is then unspecified.
+ *
+ * Memory layouts (the pages leave these open; the library fixes them)
+ *   key_cache   [num_blocks][K][block_size][H]   bf16: each token's key is a
+ *               contiguous row of H values.
+ *   value_cache [num_blocks][K][H][block_size]   bf16: each (head, dim) row
+ *               holds the block's tokens, so one value tile is stored
+ *               transposed (the layout the matrix-core operand wants).
+ *   A slot is physical_block * block_size + offset_in_block.
+ *   Query head n reads KV head n / (N / K).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+    PKV_OK = 0,
+    PKV_ERR_NULL = -1,        /* a required pointer is NULL                         */
+    PKV_ERR_SHAPE = -2,       /* sizes inconsistent or out of range                 */
+    PKV_ERR_UNSUPPORTED = -3, /* head_dim, block_size or group size not built in    */
+    PKV_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                   */
+    PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
+    PKV_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch                 */
+    PKV_ERR_DEVICE = -7       /* no HIP device / device query failed                */
+} pkv_status;
+
+/* Supported shapes (compile-time kernel variants). */
+#define PKV_BLOCK_SIZE 16          /* tokens per cache block                      */
+#define PKV_MAX_GROUP 16           /* largest N / K (query heads per KV head)     */
+#define PKV_PARTITION_GRAIN 32     /* partition sizes are multiples of this       */
+#define PKV_MAX_PARTITION 1024
+
+/*
+ * paged_kv_append -- write one decode step's keys and values into the cache.
+ *
+ *   k, v           [num_tokens][num_kv_heads][head_dim] bf16, contiguous.
+ *   slot_mapping   [num_tokens] int64: token i goes to slot slot_mapping[i];
+ *                  a negative slot means "padding, skip this token".
+ *   key_cache      [num_blocks][num_kv_heads][block_size][head_dim] bf16,
+ *   value_cache    [num_blocks][num_kv_heads][head_dim][block_size] bf16,
+ *                  both modified in place; positions not named by a slot are
+ *                  left untouched.
+ * The copy is bit exact.  Two tokens naming the same slot race (which one
+ * lands is unspecified).  A slot >= num_blocks * block_size is skipped (the
+ * kernel never writes outside the pools).
+ * Checks: NULL pointers (when num_tokens > 0), sizes, head_dim in {64, 128},
+ * block_size == 16, 16-byte alignment of k, v, key_cache, value_cache.
+ * Cites: the lesson's Build-It step 1 (write at the next position) in the
+ * paged form of its PagedAttention section.
+ */
+int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping,
+                    void *key_cache, void *value_cache,
+                    int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, void *stream);
+
+/*
+ * paged_decode_partition_size -- the context partition (tokens per split)
+ * that paged_decode_attention uses for this shape when called with
+ * partition_size == 0.  A multiple of 32 in [32, 1024].  Host-only, pure.
+ */
+int32_t paged_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_decode_workspace_size -- bytes of device workspace that
+ * paged_decode_attention needs for this shape (0 when one partition covers
+ * max_context_len and no merge is needed).  Host-only, pure.
+ */
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size);
+
+/*
+ * paged_decode_attention -- one decode step of attention over the paged cache.
+ *
+ *   out            [num_seqs][num_heads][head_dim] float32 (written).
+ *   q              [num_seqs][num_heads][head_dim] bf16 (one query token per
+ *                  sequence).
+ *   key_cache, value_cache   as in paged_kv_append, num_blocks blocks each.
+ *   block_tables   [num_seqs][max_blocks_per_seq] int32: logical block j of
+ *                  sequence b is physical block block_tables[b][j].  Entries
+ *                  past the sequence's last block are never read.
+ *   context_lens   [num_seqs] int32: tokens in each sequence's cache (append
+ *                  this step's token first and count it).  Values above
+ *                  max_context_len are treated as max_context_len, negative
+ *                  values as 0; a sequence of length 0 yields zeros.
+ *   scale          softmax scale applied to q . k (1/sqrt(head_dim) on the
+ *                  pages).
+ *   num_kv_heads   K; num_heads (N) must be a multiple with N/K <= 16.
+ *   block_size     must be 16.
+ *   max_blocks_per_seq   row stride of block_tables.
+ *   max_context_len      host-known upper bound of context_lens, at most
+ *                  max_blocks_per_seq * block_size.  It sizes the launch.
+ *   partition_size 0 = library choice (paged_decode_partition_size), else a
+ *                  multiple of 32 in [32, 1024]: the context is cut into
+ *                  pieces of this many tokens, each reduced separately to a
+ *                  running maximum, sum and weighted V, then merged with the
+ *                  log-sum-exp rule (split-K / FlashDecoding, named in
+ *                  "CS336 Lecture 10: Inference", part 6).
+ *   workspace, workspace_bytes   device scratch of at least
+ *                  paged_decode_workspace_size(...) bytes, 16-byte aligned;
+ *                  may be NULL when that size is 0.
+ * Block ids outside [0, num_blocks) are read as block 0 (no out-of-bounds
+ * access; that sequence's result is unspecified).
+ * Arithmetic: bf16 inputs, fp32 accumulation (matrix cores for q.K^T and
+ * P.V, with P carried as a two-term bf16 sum), fp32 output.  The result is
+ * bit-deterministic for given inputs and partition size: no atomics, and the
+ * reduction order depends only on logical positions.
+ */
+int paged_decode_attention(float *out, const void *q,
+                           const void *key_cache, const void *value_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           float scale, int32_t num_kv_heads, int32_t block_size,
+                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int64_t num_blocks, int32_t partition_size,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * pagedkv_stream_read -- measurement helper, not part of the method: reads
+ * `bytes` (a multiple of 16) from `src` with 16-byte loads and writes one
+ * 16-byte value per workgroup into `sink` ([gridDim] x 16 bytes; the size is
+ * returned by pagedkv_stream_read_sink_bytes).  Used to calibrate HBM byte
+ * counters and the achievable read bandwidth against the decode kernel.
+ */
+size_t pagedkv_stream_read_sink_bytes(size_t bytes);
+int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream);
+
+/* Human-readable name of a pkv_status value (static string, never NULL). */
+const char *pagedkv_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int pagedkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,1 +1,196 @@
-"""Paged-KV decode attention and K/V append for AMD MI355X (gfx950)."""
+"""Paged-KV decode attention and K/V append for AMD MI355X (gfx950).
+
+A thin Python binding over ``libpagedkv.so`` (C ABI in ``include/pagedkv.h``).
+It only checks tensor types, derives the size arguments from tensor shapes,
+and passes device pointers and torch's current HIP stream; every step of the
+computation runs in the library's HIP kernels.  The library must be built
+(``python -m paged_kv_cache_100_amd.build``); without it every call raises.
+
+    paged_kv_append(k, v, slot_mapping, key_cache, value_cache)
+    paged_decode_attention(out, q, key_cache, value_cache, block_tables,
+                           context_lens, scale, num_kv_heads, block_size)
+
+Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
+[num_blocks, K, 16, H] bf16; value_cache [num_blocks, K, H, 16] bf16;
+q [B, N, H] bf16; out [B, N, H] float32; block_tables [B, max_blocks] int32;
+context_lens [B] int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
+
+STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_UNSUPPORTED",
+          -4: "PKV_ERR_ALIGN", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH",
+          -7: "PKV_ERR_DEVICE"}
+
+_lib = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m paged_kv_cache_100_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    L.paged_kv_append.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, P]
+    L.paged_kv_append.restype = ctypes.c_int
+    L.paged_decode_partition_size.argtypes = [i32, i32, i32, i32]
+    L.paged_decode_partition_size.restype = i32
+    L.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.paged_decode_workspace_size.restype = sz
+    L.paged_decode_attention.argtypes = [P, P, P, P, P, P, f32, i32, i32, i32, i32, i32, i32,
+                                         i32, i64, i32, P, sz, P]
+    L.paged_decode_attention.restype = ctypes.c_int
+    L.pagedkv_stream_read_sink_bytes.argtypes = [sz]
+    L.pagedkv_stream_read_sink_bytes.restype = sz
+    L.pagedkv_stream_read.argtypes = [P, sz, P, P]
+    L.pagedkv_stream_read.restype = ctypes.c_int
+    L.pagedkv_status_string.argtypes = [ctypes.c_int]
+    L.pagedkv_status_string.restype = ctypes.c_char_p
+    L.pagedkv_version.argtypes = []
+    L.pagedkv_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().pagedkv_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise PagedKVError(rc, what)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def paged_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
+    """Write k[i], v[i] ([T, K, H] bf16) at slot slot_mapping[i] of the caches."""
+    pk = _dev(k, "k", torch.bfloat16)
+    pv = _dev(v, "v", torch.bfloat16)
+    ps = _dev(slot_mapping, "slot_mapping", torch.int64)
+    pkc = _dev(key_cache, "key_cache", torch.bfloat16)
+    pvc = _dev(value_cache, "value_cache", torch.bfloat16)
+    if k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("k and v must both be [T, K, H]")
+    T, K, H = k.shape
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be [num_blocks, K, block_size, H]")
+    nb, K2, bs, H2 = key_cache.shape
+    if (K2, H2) != (K, H) or value_cache.shape != (nb, K, H, bs):
+        raise ValueError("cache shapes do not match k/v ([nb,K,bs,H] and [nb,K,H,bs])")
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check(lib().paged_kv_append(pk, pv, ps, pkc, pvc, T, K, H, bs, nb, _stream(k.device)),
+           "paged_kv_append")
+
+
+def partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int,
+                   requested: int = 0) -> int:
+    return int(lib().paged_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
+                                                 requested))
+
+
+def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, partition: int = 0) -> int:
+    return int(lib().paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                 max_context_len, partition))
+
+
+def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                           block_size: int, max_context_len: Optional[int] = None,
+                           partition: int = 0,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b, n] = softmax(scale * q[b, n] . K_b^T) V_b over the paged cache.
+
+    ``max_context_len`` is a host-known bound of ``context_lens`` that sizes the
+    launch; by default the block-table capacity (max_blocks * block_size).
+    ``workspace`` (uint8, on the GPU) is allocated here when not given and the
+    shape needs one.  Returns ``out``.
+    """
+    po = _dev(out, "out", torch.float32)
+    pq = _dev(q, "q", torch.bfloat16)
+    pkc = _dev(key_cache, "key_cache", torch.bfloat16)
+    pvc = _dev(value_cache, "value_cache", torch.bfloat16)
+    pbt = _dev(block_tables, "block_tables", torch.int32)
+    pcl = _dev(context_lens, "context_lens", torch.int32)
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must both be [B, N, H]")
+    B, N, H = q.shape
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be [num_blocks, K, block_size, H]")
+    nb, K, bs, H2 = key_cache.shape
+    if K != num_kv_heads or bs != block_size or H2 != H or value_cache.shape != (nb, K, H, bs):
+        raise ValueError("cache shapes disagree with num_kv_heads / block_size / head_dim")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    need = workspace_size(B, N, K, H, max_context_len, partition) if B else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw, wbytes = 0, 0
+    if workspace is not None:
+        pw = _dev(workspace, "workspace", torch.uint8)
+        wbytes = workspace.numel()
+    _check(lib().paged_decode_attention(po, pq, pkc, pvc, pbt, pcl, float(scale), K, bs, B, N, H,
+                                        max_blocks, int(max_context_len), nb, int(partition),
+                                        pw, wbytes, _stream(q.device)),
+           "paged_decode_attention")
+    return out
+
+
+def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Measurement helper: read ``src`` once with 16-byte loads (no result)."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous GPU tensor")
+    need = int(lib().pagedkv_stream_read_sink_bytes(nbytes))
+    if sink is None:
+        sink = torch.empty(need, dtype=torch.uint8, device=src.device)
+    if sink.numel() * sink.element_size() < need:
+        raise ValueError("sink too small")
+    _check(lib().pagedkv_stream_read(src.data_ptr(), nbytes, sink.data_ptr(),
+                                     _stream(src.device)), "pagedkv_stream_read")
+    return sink
+
+
+def version() -> str:
+    v = lib().pagedkv_version()
+    return f"{v >> 16}.{v & 0xFFFF}"

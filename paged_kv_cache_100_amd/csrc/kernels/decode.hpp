@@ -1,0 +1,331 @@
+// Decode-phase attention over the paged KV cache, for gfx950 (CDNA4).
+//
+// What is computed (the attention-with-cache step of the "Optimización de la
+// inferencia" lesson, in the paged form of its PagedAttention section and of
+// "CS336 Lecture 10: Inference", parts 3 and 6): for every sequence b and
+// query head n = kvh * G + g,
+//     out[b][n] = sum_t softmax_t(scale * q[b][n] . k_t) v_t
+// over the sequence's cached positions t < ctx_b, where position t lives in
+// physical block block_tables[b][t / 16] at offset t % 16, and all G query
+// heads of a group read the same KV head kvh.
+//
+// Work decomposition.  One wavefront owns one (partition, KV head, sequence):
+// the G query heads of the group are the 16 columns of the matrix-core tiles
+// (G <= 16; unused columns compute on zero queries and are never stored), so
+// every key and value byte of the group is loaded from HBM exactly once.
+// The wave walks its partition 32 tokens (two cache blocks) at a time:
+//
+//   scores   S^T[32 x 16] = K_chunk[32 x H] . Q^T[H x 16]
+//            two v_mfma_f32_16x16x32_bf16 tiles per 32 k-values of H; each
+//            lane's A operand is 16 contiguous bytes of one key row, loaded
+//            straight from HBM into registers.
+//   softmax  online (running maximum m and sum l per query column, in log2
+//            units so one v_exp_f32 serves each score); the column maximum of
+//            a chunk is reduced across the four lane quads with two
+//            cross-lane shuffles.
+//   P.V      O^T[H x 16] += V^T[H x 32] . P^T[32 x 16], one tile per 16
+//            values of H.  The value tile is stored transposed ([H][16] per
+//            block), so each lane's A operand is again 16 contiguous bytes.
+//            P (in [0, 1]) is carried as p_hi + p_lo, both bf16, so the
+//            product keeps ~16 significant bits (relative error <= 2^-17)
+//            while V stays in bf16 with no conversion work.
+//
+// Row order inside a score tile is permuted so that the 4 scores a lane holds
+// in each of the two S^T tiles are 8 *consecutive* tokens -- exactly the 8
+// consecutive P^T values that lane must supply to the P.V tile: tile a, row
+// m holds token 8*(m/4) + 4*a + m%4.  No data moves between the two
+// products.
+//
+// Split-K ("FlashDecoding", named in "CS336 Lecture 10: Inference", part 6):
+// the context is cut into partitions of `part` tokens.  With one partition
+// the kernel normalises and writes `out` itself.  With several, each wave
+// writes its partial (m, l, unnormalised o) and merge_kernel combines them:
+//     M = max_j m_j,  out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.
+//
+// Masking.  Scores of positions >= ctx become -inf, and value elements of
+// those positions are zeroed before the matrix product (block tails may hold
+// anything, NaN included); a block past the sequence's last block is never
+// addressed (its table entry is not read).
+#pragma once
+
+#include "common.hpp"
+
+namespace pkv {
+
+constexpr int kChunk = 32;   // tokens per inner step (two cache blocks)
+
+struct DecodeParams {
+    float *out;                   // [B][N][H]
+    float *part_o;                // [B][N][P][H]   (split only)
+    float *part_ml;               // [B][N][P][2]   (split only)
+    const uint16_t *q;            // [B][N][H] bf16
+    const uint16_t *key_cache;    // [num_blocks][K][16][H]
+    const uint16_t *value_cache;  // [num_blocks][K][H][16]
+    const int32_t *block_tables;  // [B][max_blocks]
+    const int32_t *context_lens;  // [B]
+    float scale_log2;             // scale * log2(e)
+    int32_t num_heads;            // N
+    int32_t num_kv_heads;         // K
+    int32_t group;                // G = N / K
+    int32_t max_blocks;
+    int32_t max_ctx;
+    int32_t part;                 // tokens per partition (multiple of 32)
+    int32_t num_parts;            // P
+    int64_t num_blocks;
+};
+
+// Per-lane operand registers of one 32-token chunk.
+template <int H>
+struct ChunkRegs {
+    u32x4 k[2][H / 32];   // score tile a, k-step s
+    u32x4 v[H / 16];      // value tile c
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
+{
+    return (id >= 0 && (int64_t)id < num_blocks) ? id : 0;
+}
+
+template <int H>
+__device__ __forceinline__ void load_chunk(ChunkRegs<H> &r, const uint16_t *k_lo,
+                                           const uint16_t *k_hi, const uint16_t *v_lo,
+                                           const uint16_t *v_hi, int col, int quad)
+{
+    // Keys: tile a, row m=col -> token 8*(col/4) + 4a + col%4 of the chunk,
+    // i.e. block col/8, row 8*((col/4)&1) + 4a + (col&3); k-values 32s + 8quad.
+    const uint16_t *kb = (col >> 3) ? k_hi : k_lo;
+    const int krow = 8 * ((col >> 2) & 1) + (col & 3);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s)
+            r.k[a][s] = load16(kb + (krow + 4 * a) * H + 32 * s + 8 * quad);
+    // Values: tile c, lane (col, quad) -> dim 16c + col, tokens 8quad..8quad+7
+    // of the chunk, i.e. block quad/2, offsets 8*(quad&1)..+7 (contiguous).
+    const uint16_t *vb = (quad >> 1) ? v_hi : v_lo;
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c)
+        r.v[c] = load16(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
+}
+
+template <int H, bool kTail>
+__device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, const bf16x8 (&qf)[H / 32],
+                                             int rem, int quad, float scale_log2, float &m,
+                                             float &l, f32x4 (&acc)[H / 16])
+{
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < H / 32; ++s) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[0][s]), qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[1][s]), qf[s], s1, 0, 0, 0);
+    }
+    // Lane (col, quad) now holds the scores of tokens 8quad + e, e = 0..7.
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = s0[i] * scale_log2;
+        x[4 + i] = s1[i] * scale_log2;
+    }
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    if (kTail) {   // last, partial chunk of the partition: rem < 32 tokens valid
+        const int valid = min(max(rem - 8 * quad, 0), 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e >= valid)
+                x[e] = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            vmask[w] = (2 * w < valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first chunk
+
+    bf16x8 p_hi, p_lo;
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(x[e] - m_new);
+        psum += p;
+        const __bf16 hi = (__bf16)p;
+        p_hi[e] = hi;
+        p_lo[e] = (__bf16)(p - (float)hi);
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            acc[c] *= alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c) {
+        const bf16x8 vv = as_bf16x8(kTail ? (r.v[c] & vmask) : r.v[c]);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, acc[c], 0, 0, 0);
+    }
+}
+
+template <int H, bool kSplit>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeParams p)
+{
+    const int part_idx = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int col = lane & 15;    // query head within the group (tile column)
+    const int quad = lane >> 4;   // 0..3
+
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int start = part_idx * p.part;
+    const bool live = col < p.group;
+    const int n = kvh * p.group + col;
+
+    if (start >= ctx) {
+        if (!kSplit && part_idx == 0 && live) {   // empty sequence: zeros
+            float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+    const int end = min(start + p.part, ctx);
+
+    bf16x8 qf[H / 32];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)b * p.num_heads + (live ? n : 0)) * H;
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s) {
+            u32x4 raw = load16(qrow + 32 * s + 8 * quad);
+            if (!live)
+                raw = u32x4{0u, 0u, 0u, 0u};
+            qf[s] = as_bf16x8(raw);
+        }
+    }
+
+    // The partition's block ids (at most 64: partitions hold <= 1024 tokens),
+    // one per lane, so a chunk reads its two ids with v_readlane instead of a
+    // memory round trip.  Entries past the sequence's last block are not read.
+    const int first_block = start / kBlockSize;
+    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
+    int my_id = 0;
+    if (lane < n_blocks)
+        my_id = clamp_block(p.block_tables[(int64_t)b * p.max_blocks + first_block + lane],
+                            p.num_blocks);
+
+    const int64_t tile_elems = (int64_t)kBlockSize * H;              // one (block, head) tile
+    const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
+    const uint16_t *kbase = p.key_cache + kvh * tile_elems;
+    const uint16_t *vbase = p.value_cache + kvh * tile_elems;
+
+    // Issue the loads of chunk ci (tokens start + 32ci ...); its second block
+    // is addressed only if the chunk reaches into it.
+    auto issue = [&](ChunkRegs<H> &r, int ci) {
+        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
+        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
+                                                : id0;
+        load_chunk<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
+                      vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[H / 16];
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c)
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_full = (end - start) / kChunk;                // chunks of 32 valid tokens
+    const int n_chunks = n_full + ((end - start) % kChunk != 0);
+    const int tail_rem = end - start - n_full * kChunk;
+    auto attend = [&](const ChunkRegs<H> &r, int ci) {
+        if (ci < n_full)
+            attend_chunk<H, false>(r, qf, kChunk, quad, p.scale_log2, m, l, acc);
+        else
+            attend_chunk<H, true>(r, qf, tail_rem, quad, p.scale_log2, m, l, acc);
+    };
+
+    // Two register buffers: the next chunk's loads are in flight while the
+    // current chunk is computed.
+    ChunkRegs<H> ra, rb;
+    issue(ra, 0);
+    for (int ci = 0; ci < n_chunks; ci += 2) {
+        if (ci + 1 < n_chunks)
+            issue(rb, ci + 1);
+        attend(ra, ci);
+        if (ci + 1 >= n_chunks)
+            break;
+        if (ci + 2 < n_chunks)
+            issue(ra, ci + 2);
+        attend(rb, ci + 1);
+    }
+
+    // Each lane summed its own 8 tokens per chunk; add the four quads.
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (!live)
+        return;
+    // acc[c] holds O^T[16c + 4quad + i][col], i = 0..3.
+    if (!kSplit) {
+        const float inv = 1.0f / l;
+        float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
+    } else {
+        const int64_t slot = ((int64_t)b * p.num_heads + n) * p.num_parts + part_idx;
+        float *o = p.part_o + slot * H;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c];
+        if (quad == 0) {
+            p.part_ml[2 * slot] = m;
+            p.part_ml[2 * slot + 1] = l;
+        }
+    }
+}
+
+struct MergeParams {
+    float *out;                   // [B][N][H]
+    const float *part_o;          // [B][N][P][H]
+    const float *part_ml;         // [B][N][P][2]
+    const int32_t *context_lens;  // [B]
+    int32_t num_heads;
+    int32_t max_ctx;
+    int32_t part;
+    int32_t num_parts;
+};
+
+// Log-sum-exp merge of the partitions of one (sequence, head); one thread per
+// output value.  Partition maxima are in log2 units.
+template <int H>
+__global__ __launch_bounds__(H) void merge_kernel(MergeParams p)
+{
+    const int n = blockIdx.x;
+    const int b = blockIdx.y;
+    const int h = threadIdx.x;
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int parts = (ctx + p.part - 1) / p.part;
+    const int64_t row = (int64_t)b * p.num_heads + n;
+    const float *ml = p.part_ml + row * p.num_parts * 2;
+    const float *po = p.part_o + row * p.num_parts * H + h;
+
+    float big = -INFINITY;
+    for (int j = 0; j < parts; ++j)
+        big = fmaxf(big, ml[2 * j]);
+    float den = 0.f, num = 0.f;
+    for (int j = 0; j < parts; ++j) {
+        const float w = __builtin_amdgcn_exp2f(ml[2 * j] - big);
+        den += w * ml[2 * j + 1];
+        num += w * po[(int64_t)j * H];
+    }
+    p.out[row * H + h] = parts ? num / den : 0.f;
+}
+
+}  // namespace pkv

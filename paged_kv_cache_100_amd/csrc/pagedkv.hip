@@ -1,0 +1,274 @@
+// C ABI of the paged-KV library: host-side argument checks, launch shapes and
+// kernel launches.  Declarations and their documentation: include/pagedkv.h.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+#include "kernels/append.hpp"
+#include "kernels/decode.hpp"
+#include "kernels/stream_read.hpp"
+
+namespace {
+
+constexpr int kVersionMajor = 1;
+constexpr int kVersionMinor = 0;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Launch shape: with at least this many (partition, KV head, sequence) waves
+// the 256 CUs (1024 SIMDs) hold two to four rounds of resident waves.
+constexpr int64_t kTargetWaves = 4096;
+
+int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
+                         int32_t requested)
+{
+    if (requested > 0)
+        return requested;
+    static const int32_t kSizes[] = {512, 256, 128, 64};
+    for (int32_t part : kSizes)
+        if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_ctx, part) >= kTargetWaves)
+            return part;
+    return 32;
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                           int32_t max_ctx, int32_t part)
+{
+    const int64_t parts = ceil_div(max_ctx, part);
+    if (parts <= 1)
+        return 0;
+    const int64_t rows = (int64_t)num_seqs * num_heads * parts;
+    const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+    return (size_t)(o_bytes + rows * 2 * 4);
+}
+
+int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream)
+{
+    void *args[] = {params};
+    hipError_t err = hipLaunchKernel(kernel, grid, block, args, 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pagedkv_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+const char *pagedkv_status_string(int status)
+{
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "sizes inconsistent or out of range";
+    case PKV_ERR_UNSUPPORTED: return "head_dim, block_size or group size not supported";
+    case PKV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+    }
+}
+
+int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, void *key_cache,
+                    void *value_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, void *stream)
+{
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+        return PKV_ERR_SHAPE;
+    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_tokens == 0)
+        return PKV_OK;
+    if (!k || !v || !slot_mapping || !key_cache || !value_cache)
+        return PKV_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+        return PKV_ERR_ALIGN;
+
+    pkv::AppendParams p;
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.slot_mapping = slot_mapping;
+    p.key_cache = static_cast<uint16_t *>(key_cache);
+    p.value_cache = static_cast<uint16_t *>(value_cache);
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
+
+    const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+    const int64_t blocks = ceil_div(threads, 256);
+    if (blocks > INT32_MAX)
+        return PKV_ERR_SHAPE;
+    const void *kern = head_dim == 128 ? (const void *)pkv::append_kernel<128>
+                                       : (const void *)pkv::append_kernel<64>;
+    return launch(kern, dim3((unsigned)blocks), dim3(256), &p, stream);
+}
+
+int32_t paged_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len, int32_t partition_size)
+{
+    return choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+}
+
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len <= 0)
+        return 0;
+    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+    if (part <= 0)
+        return 0;
+    return workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, part);
+}
+
+int paged_decode_attention(float *out, const void *q, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, float scale, int32_t num_kv_heads,
+                           int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int64_t num_blocks, int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        max_context_len < 0 || num_blocks < 0)
+        return PKV_ERR_SHAPE;
+    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_heads % num_kv_heads != 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads / num_kv_heads > PKV_MAX_GROUP)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return PKV_ERR_SHAPE;
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return PKV_ERR_SHAPE;
+    if (partition_size != 0 &&
+        (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_PARTITION ||
+         partition_size % PKV_PARTITION_GRAIN != 0))
+        return PKV_ERR_SHAPE;
+    if (!isfinite(scale))
+        return PKV_ERR_SHAPE;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!out || !q || !block_tables || !context_lens)
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && (!key_cache || !value_cache))
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && num_blocks == 0)
+        return PKV_ERR_SHAPE;
+    if (!aligned16(out) || !aligned16(q) || (key_cache && !aligned16(key_cache)) ||
+        (value_cache && !aligned16(value_cache)) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return PKV_ERR_ALIGN;
+
+    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len > 0
+                                          ? max_context_len : 1, partition_size);
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
+    const bool split = parts > 1;
+    const size_t need = split ? workspace_bytes_for(num_seqs, num_heads, head_dim,
+                                                    max_context_len, part) : 0;
+    if (split) {
+        if (!workspace || workspace_bytes < need)
+            return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return PKV_ERR_ALIGN;
+    }
+
+    pkv::DecodeParams p;
+    p.out = out;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
+    if (split) {
+        const int64_t rows = (int64_t)num_seqs * num_heads * parts;
+        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+        p.part_o = static_cast<float *>(workspace);
+        p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    p.q = static_cast<const uint16_t *>(q);
+    p.key_cache = static_cast<const uint16_t *>(key_cache);
+    p.value_cache = static_cast<const uint16_t *>(value_cache);
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.max_ctx = max_context_len;
+    p.part = part;
+    p.num_parts = (int32_t)parts;
+    p.num_blocks = num_blocks;
+
+    const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
+    const void *kern;
+    if (head_dim == 128)
+        kern = split ? (const void *)pkv::decode_kernel<128, true>
+                     : (const void *)pkv::decode_kernel<128, false>;
+    else
+        kern = split ? (const void *)pkv::decode_kernel<64, true>
+                     : (const void *)pkv::decode_kernel<64, false>;
+    int rc = launch(kern, grid, dim3(pkv::kWave), &p, stream);
+    if (rc != PKV_OK || !split)
+        return rc;
+
+    pkv::MergeParams mp;
+    mp.out = out;
+    mp.part_o = p.part_o;
+    mp.part_ml = p.part_ml;
+    mp.context_lens = context_lens;
+    mp.num_heads = num_heads;
+    mp.max_ctx = max_context_len;
+    mp.part = part;
+    mp.num_parts = (int32_t)parts;
+    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
+                                     : (const void *)pkv::merge_kernel<64>;
+    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(head_dim), &mp, stream);
+}
+
+size_t pagedkv_stream_read_sink_bytes(size_t bytes)
+{
+    const int64_t n16 = (int64_t)(bytes / 16);
+    int64_t blocks = ceil_div(n16, pkv::kStreamThreads * 4);
+    if (blocks > pkv::kStreamBlocksMax)
+        blocks = pkv::kStreamBlocksMax;
+    if (blocks < 1)
+        blocks = 1;
+    return (size_t)blocks * 16;
+}
+
+int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream)
+{
+    if (bytes == 0)
+        return PKV_OK;
+    if (!src || !sink)
+        return PKV_ERR_NULL;
+    if (bytes % 16 != 0)
+        return PKV_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(sink))
+        return PKV_ERR_ALIGN;
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const unsigned blocks = (unsigned)(pagedkv_stream_read_sink_bytes(bytes) / 16);
+    struct {
+        const pkv::u32x4 *src;
+        int64_t n16;
+        pkv::u32x4 *sink;
+    } a = {static_cast<const pkv::u32x4 *>(src), n16, static_cast<pkv::u32x4 *>(sink)};
+    void *args[] = {&a.src, &a.n16, &a.sink};
+    hipError_t err = hipLaunchKernel((const void *)pkv::stream_read_kernel, dim3(blocks),
+                                     dim3(pkv::kStreamThreads), args, 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+"""Helpers for the GPU parity tests: run one decode step through the C ABI and
+the same step through the CPU oracle, then compare.
+
+The bar (from the method's statement of the target): append bit-exact;
+attention output within max abs error 2e-3 and max relative error 2e-3 of
+the fp64 oracle.  Relative error is taken row-normwise -- per (sequence,
+head) row, max_h |d| / max_h |ref| -- because an elementwise ratio is
+unbounded where the reference output is near zero.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_100_amd as pkv
+
+from _util import bits, oracle_inputs
+
+ABS_TOL = 2e-3
+REL_TOL = 2e-3
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_step(w, partition: int = 0, device: str = "cuda:0", max_context_len=None):
+    """Append then decode on the GPU.  Returns (out float32 cpu, gpu workload)."""
+    g = w.to(device)
+    pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+    out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=device)
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                               g.context_lens, w.scale, w.spec.K, w.spec.bs,
+                               max_context_len=mcl, partition=partition)
+    torch.cuda.synchronize()
+    return out.cpu(), g
+
+
+def oracle_step(w):
+    """Oracle append on host copies of the pools, then the oracle decode."""
+    inp = oracle_inputs(w)
+    oracle.append(bits(w.k_new), bits(w.v_new), w.slot_mapping.numpy(), inp["key_cache"],
+                  inp["value_cache"])
+    ref = oracle.decode(inp["q"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+                        inp["context_lens"], w.scale)
+    return ref, inp
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    d = np.abs(got - ref)
+    abs_err = float(d.max()) if d.size else 0.0
+    row_d = d.reshape(-1, d.shape[-1]).max(axis=1)
+    row_ref = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1)
+    live = row_ref > 0
+    rel = float((row_d[live] / row_ref[live]).max()) if live.any() else 0.0
+    zero_rows_ok = bool(np.all(row_d[~live] == 0)) if (~live).any() else True
+    return abs_err, rel, zero_rows_ok
+
+
+def assert_parity(got, ref, what: str):
+    got = np.asarray(got)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    abs_err, rel, zero_ok = errors(got, ref)
+    log(f"  {what}: max abs {abs_err:.2e}, max row rel {rel:.2e}")
+    assert abs_err <= ABS_TOL, f"{what}: max abs error {abs_err:.3e} > {ABS_TOL}"
+    assert rel <= REL_TOL, f"{what}: max row-normwise rel error {rel:.3e} > {REL_TOL}"
+    assert zero_ok, f"{what}: rows whose reference is zero are not zero"
+
+
+def assert_append_exact(g, inp, what: str):
+    kc = bits(g.key_cache)
+    vc = bits(g.value_cache)
+    assert np.array_equal(kc, inp["key_cache"]), f"{what}: key cache differs after append"
+    assert np.array_equal(vc, inp["value_cache"]), f"{what}: value cache differs after append"
+
+
+class Timer:
+    def __init__(self, what):
+        self.what = what
+
+    def __enter__(self):
+        self.t = time.time()
+        return self
+
+    def __exit__(self, *a):
+        log(f"  {self.what}: {time.time() - self.t:.1f}s")
