@@ -1,0 +1,234 @@
+"""Benchmark: one decode step of paged-KV attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path for one attention layer: append the step's B new
+K/V rows into the paged cache (paged_kv_append), then decode attention for the
+B query tokens over every cached position (paged_decode_attention: schedule,
+decode and log-sum-exp merge kernels).  Inputs are generated on the CPU from a
+seed, copied to HBM, and stay resident while the K timed steps run.
+
+Prints one JSON line.  ``value`` is the KV-read bandwidth of the whole step:
+the bytes of K and V the method must read (sum of contexts x K x H x 2 bytes x
+2) divided by the measured step time.  ``roofline`` is for the attention call
+(its HIP events bracket all of its kernels), against the
+MI355X's 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV-read HBM GB/s (% of MI355X peak) and tokens/s per layer"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "llama3_8b_b64_ctx8k"
+KERNEL_SOURCES = ["paged_kv_cache_100_amd/csrc/kernels/decode.hpp",
+                  "paged_kv_cache_100_amd/csrc/kernels/decode_balanced.hpp",
+                  "paged_kv_cache_100_amd/csrc/kernels/common.hpp",
+                  "paged_kv_cache_100_amd/csrc/pagedkv.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, part: int) -> dict:
+    """Bytes the method must move for one step (not what the kernels move)."""
+    s = w.spec
+    ctx = [int(c) for c in w.context_lens.tolist()]
+    kv = sum(ctx) * s.K * s.H * 2 * 2                  # K and V, bf16
+    q = s.B * s.N * s.H * 2
+    out = s.B * s.N * s.H * 4
+    tables = sum(-(-c // s.bs) for c in ctx) * 4 + s.B * 4
+    append = 2 * (s.B * s.K * s.H * 2) * 2              # read k, v; write them into the pools
+    return {"kv": kv, "q": q, "out": out, "tables": tables, "attention": kv + q + out + tables,
+            "append": append}
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per attention call from a committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The CPU oracle, untuned, on a growing prefix of the batch until about
+    ``budget_s`` seconds of work; reported as tokens/s per layer (one decode
+    token per sequence) and KV GB/s."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def u16(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    q, kc, vc = u16(w.q), u16(w.key_cache), u16(w.value_cache)
+    bt, cl = w.block_tables.numpy(), w.context_lens.numpy()
+    # append first so the cache holds the step's token, as on the GPU
+    kc, vc = kc.copy(), vc.copy()
+    oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
+    B = w.spec.B
+    n, spent, done_seqs, done_tokens = 1, 0.0, 0, 0
+    while True:
+        n = min(n, B)
+        t0 = time.perf_counter()
+        oracle.decode(q[:n], kc, vc, bt[:n], cl[:n], w.scale)
+        dt = time.perf_counter() - t0
+        spent, done_seqs, done_tokens = dt, n, int(cl[:n].sum())
+        if dt >= budget_s / 3 or n == B:
+            break
+        n *= 2
+    kv_bytes = done_tokens * w.spec.K * w.spec.H * 4
+    return {"value": done_seqs / spent, "unit": "tokens/s per layer", "cores": oracle.num_threads(),
+            "kind": "oracle", "kv_GBps": kv_bytes / spent / 1e9,
+            "sample": f"first {done_seqs} of {B} sequences ({done_tokens} cached tokens), "
+                      f"fp64 C oracle with OpenMP, {spent:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="tokens per fixed split; 0 = token-balanced schedule "
+                         "(default: the workload's own, else 0)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_100_amd as pkv
+    from paged_kv_cache_100_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    pkv.lib()                                   # fail loudly if the library is not built
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    w = W.make(args.workload, poison=False)
+    s = w.spec
+    gen_s = time.time() - t0
+    g = w.to(dev)
+    part = s.partition_size if args.partition is None else args.partition
+    mcl = w.max_context_len
+    ws_bytes = pkv.workspace_size(s.B, s.N, s.K, s.H, mcl, part)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((s.B, s.N, s.H), dtype=torch.float32, device=dev)
+
+    def append():
+        pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+
+    def attend():
+        pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                   g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
+                                   partition=part, workspace=workspace)
+
+    # achievable read bandwidth: one plain 16-byte streaming read of 2 GiB
+    probe_src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    sink = pkv.stream_read(probe_src)
+    torch.cuda.synchronize()
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe_ms = []
+    for _ in range(6):
+        pe0.record()
+        pkv.stream_read(probe_src, sink)
+        pe1.record()
+        torch.cuda.synchronize()
+        probe_ms.append(pe0.elapsed_time(pe1))
+    probe_gbps = (1 << 31) / (sorted(probe_ms)[len(probe_ms) // 2] * 1e-3) / 1e9
+    del probe_src
+
+    for _ in range(args.warmup):
+        append()
+        attend()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        append()
+        ev[i][1].record()
+        attend()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    append_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_per_step = wall * 1e3 / K
+    attn_avg = sum(attn_ms) / K
+    nbytes = algorithmic_bytes(w, part)
+    achieved = nbytes["attention"] / (attn_avg * 1e-3) / 1e9
+    value = nbytes["kv"] / (ms_per_step * 1e-3) / 1e9
+    traffic = traffic_from_profile(args.workload)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 q/k/v, block tables from a seeded permutation",
+        "config": {"workload": args.workload, "B": s.B, "N": s.N, "K": s.K, "H": s.H,
+                   "block_size": s.bs, "sum_context": int(w.context_lens.sum()),
+                   "max_context": mcl, "partition": part, "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s_per_layer": round(s.B / (ms_per_step * 1e-3), 1),
+        "attention_tokens_per_s_per_layer": round(s.B / (attn_avg * 1e-3), 1),
+        "attention_ms": round(attn_avg, 5),
+        "append_ms": round(sum(append_ms) / K, 5),
+        "probe_read_GBps": round(probe_gbps, 1),
+        "roofline": {"kernel": "paged_decode_attention (all kernels of the call)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_call": nbytes["attention"],
+                     "kernel_hash": kernel_hash()},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    rec["setup_s"] = round(gen_s, 1)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -103,17 +103,10 @@ int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping,
                     int32_t block_size, int64_t num_blocks, void *stream);
 
 /*
- * paged_decode_partition_size -- the context partition (tokens per split)
- * that paged_decode_attention uses for this shape when called with
- * partition_size == 0.  A multiple of 32 in [32, 1024].  Host-only, pure.
- */
-int32_t paged_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                    int32_t max_context_len, int32_t partition_size);
-
-/*
  * paged_decode_workspace_size -- bytes of device workspace that
- * paged_decode_attention needs for this shape (0 when one partition covers
- * max_context_len and no merge is needed).  Host-only, pure.
+ * paged_decode_attention needs for this shape and partition_size (0 when no
+ * workspace is needed).  Host-only and pure: the same arguments always give
+ * the same size, on any device.
  */
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t max_context_len,
@@ -128,7 +121,7 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  *   key_cache, value_cache   as in paged_kv_append, num_blocks blocks each.
  *   block_tables   [num_seqs][max_blocks_per_seq] int32: logical block j of
  *                  sequence b is physical block block_tables[b][j].  Entries
- *                  past the sequence's last block are never read.
+ *                  past the sequence's last block do not affect the result.
  *   context_lens   [num_seqs] int32: tokens in each sequence's cache (append
  *                  this step's token first and count it).  Values above
  *                  max_context_len are treated as max_context_len, negative
@@ -139,22 +132,31 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  *   block_size     must be 16.
  *   max_blocks_per_seq   row stride of block_tables.
  *   max_context_len      host-known upper bound of context_lens, at most
- *                  max_blocks_per_seq * block_size.  It sizes the launch.
- *   partition_size 0 = library choice (paged_decode_partition_size), else a
- *                  multiple of 32 in [32, 1024]: the context is cut into
- *                  pieces of this many tokens, each reduced separately to a
- *                  running maximum, sum and weighted V, then merged with the
- *                  log-sum-exp rule (split-K / FlashDecoding, named in
- *                  "CS336 Lecture 10: Inference", part 6).
+ *                  max_blocks_per_seq * block_size.
+ *   num_blocks     blocks in each cache pool.
+ *   partition_size how the context is split across waves (the split-K of
+ *                  FlashDecoding, named in "CS336 Lecture 10: Inference",
+ *                  part 6; partial results are merged with the log-sum-exp
+ *                  rule):
+ *                  0  token-balanced schedule: the cached tokens of the whole
+ *                     batch are divided evenly over as many waves as the GPU
+ *                     holds at once, whatever the mix of context lengths
+ *                     (three kernel launches);
+ *                  P  fixed partitions of P tokens (a multiple of 32 in
+ *                     [32, 1024]) of each sequence, one wave each (two
+ *                     launches; one when a single partition covers
+ *                     max_context_len).
  *   workspace, workspace_bytes   device scratch of at least
  *                  paged_decode_workspace_size(...) bytes, 16-byte aligned;
- *                  may be NULL when that size is 0.
+ *                  may be NULL when that size is 0.  Its contents on entry
+ *                  do not matter; calls sharing one workspace must not run
+ *                  concurrently.
  * Block ids outside [0, num_blocks) are read as block 0 (no out-of-bounds
  * access; that sequence's result is unspecified).
  * Arithmetic: bf16 inputs, fp32 accumulation (matrix cores for q.K^T and
  * P.V, with P carried as a two-term bf16 sum), fp32 output.  The result is
- * bit-deterministic for given inputs and partition size: no atomics, and the
- * reduction order depends only on logical positions.
+ * bit-deterministic for given inputs, partition_size and device: no atomics,
+ * and the reduction order depends only on logical positions.
  */
 int paged_decode_attention(float *out, const void *q,
                            const void *key_cache, const void *value_cache,

@@ -52,8 +52,6 @@ def lib() -> ctypes.CDLL:
                             ctypes.c_size_t)
     L.paged_kv_append.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, P]
     L.paged_kv_append.restype = ctypes.c_int
-    L.paged_decode_partition_size.argtypes = [i32, i32, i32, i32]
-    L.paged_decode_partition_size.restype = i32
     L.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.paged_decode_workspace_size.restype = sz
     L.paged_decode_attention.argtypes = [P, P, P, P, P, P, f32, i32, i32, i32, i32, i32, i32,
@@ -118,12 +116,6 @@ def paged_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
            "paged_kv_append")
 
 
-def partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int,
-                   requested: int = 0) -> int:
-    return int(lib().paged_decode_partition_size(num_seqs, num_kv_heads, max_context_len,
-                                                 requested))
-
-
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
                    max_context_len: int, partition: int = 0) -> int:
     return int(lib().paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
@@ -138,10 +130,11 @@ def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[b, n] = softmax(scale * q[b, n] . K_b^T) V_b over the paged cache.
 
-    ``max_context_len`` is a host-known bound of ``context_lens`` that sizes the
-    launch; by default the block-table capacity (max_blocks * block_size).
+    ``max_context_len`` is a host-known bound of ``context_lens``; by default
+    the block-table capacity (max_blocks * block_size).  ``partition`` 0 uses
+    the token-balanced schedule, P > 0 fixed P-token partitions.
     ``workspace`` (uint8, on the GPU) is allocated here when not given and the
-    shape needs one.  Returns ``out``.
+    call needs one.  Returns ``out``.
     """
     po = _dev(out, "out", torch.float32)
     pq = _dev(q, "q", torch.bfloat16)

@@ -15,6 +15,12 @@ constexpr int kWave = 64;        // CDNA wavefront width
 
 // 16-byte global load / store of raw bits.
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// 16-byte load with the non-temporal hint: data read once (the KV cache
+// stream) should not displace reusable lines from the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 }  // namespace pkv

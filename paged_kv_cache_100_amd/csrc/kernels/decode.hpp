@@ -101,25 +101,27 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<H> &r, const uint16_t *k_lo
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int s = 0; s < H / 32; ++s)
-            r.k[a][s] = load16(kb + (krow + 4 * a) * H + 32 * s + 8 * quad);
+            r.k[a][s] = load16_stream(kb + (krow + 4 * a) * H + 32 * s + 8 * quad);
     // Values: tile c, lane (col, quad) -> dim 16c + col, tokens 8quad..8quad+7
     // of the chunk, i.e. block quad/2, offsets 8*(quad&1)..+7 (contiguous).
     const uint16_t *vb = (quad >> 1) ? v_hi : v_lo;
 #pragma unroll
     for (int c = 0; c < H / 16; ++c)
-        r.v[c] = load16(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
+        r.v[c] = load16_stream(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
 }
 
-template <int H, bool kTail>
-__device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, const bf16x8 (&qf)[H / 32],
-                                             int rem, int quad, float scale_log2, float &m,
-                                             float &l, f32x4 (&acc)[H / 16])
+// `qf(s)` yields the lane's query operand for k-step s (from registers or LDS).
+template <int H, bool kTail, class QFrag>
+__device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, int rem, int quad,
+                                             float scale_log2, float &m, float &l,
+                                             f32x4 (&acc)[H / 16])
 {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < H / 32; ++s) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[0][s]), qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[1][s]), qf[s], s1, 0, 0, 0);
+        const bf16x8 q = qf(s);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[0][s]), q, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[1][s]), q, s1, 0, 0, 0);
     }
     // Lane (col, quad) now holds the scores of tokens 8quad + e, e = 0..7.
     float x[8];
@@ -171,8 +173,48 @@ __device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, const bf16x8
     }
 }
 
+// Depth of the register ring: chunks issued ahead of the one being computed
+// is kRing - 1 (16 KiB each).  One wave per SIMD owns up to 512 registers,
+// enough for four 64-register chunk buffers next to the accumulators.
+constexpr int kRing = 4;
+
+// Runs chunks 0 .. total-1 (total >= 1) through a ring of kRing register
+// buffers: issue(buf, k) starts the loads of chunk k, attend(buf, k) consumes
+// them.  The steady-state loop has no branch between an issue and the attend
+// that follows it, so the compiler's wait counts are exact there: computing
+// chunk k waits for chunk k's loads only, with chunks k+1 .. k+kRing-1 in
+// flight.  The last (up to 2*kRing - 1) chunks run through a guarded copy.
+template <class Buf, class Issue, class Attend>
+__device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&issue,
+                                         Attend &&attend)
+{
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u)
+        if (u < total)
+            issue(buf[u], u);
+    int k = 0;
+    for (; k + 2 * kRing - 2 < total; k += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            issue(buf[(u + kRing - 1) % kRing], k + u + kRing - 1);
+            attend(buf[u], k + u);
+        }
+    }
+    for (;; k += kRing) {
+#pragma unroll
+        for (int u = 0; u < kRing; ++u) {
+            const int c = k + u;
+            if (c + kRing - 1 < total)
+                issue(buf[(u + kRing - 1) % kRing], c + kRing - 1);
+            attend(buf[u], c);
+            if (c + 1 >= total)
+                return;
+        }
+    }
+}
+
 template <int H, bool kSplit>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
     const int part_idx = blockIdx.x;
@@ -182,8 +224,20 @@ void decode_kernel(DecodeParams p)
     const int col = lane & 15;    // query head within the group (tile column)
     const int quad = lane >> 4;   // 0..3
 
-    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+    // The partition's block ids (at most 64: partitions hold <= 1024 tokens),
+    // one per lane, so a chunk reads its two ids with v_readlane instead of a
+    // memory round trip.  They are fetched before the context length is known
+    // (every entry up to the table row's end is in bounds), so the two loads
+    // overlap; entries past the sequence's last block are loaded but unused.
     const int start = part_idx * p.part;
+    const int first_block = start / kBlockSize;
+    const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks + first_block;
+    const int table_avail = min(p.part / kBlockSize, p.max_blocks - first_block);
+    int my_id = 0;
+    if (lane < table_avail)
+        my_id = table[lane];
+
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
     const bool live = col < p.group;
     const int n = kvh * p.group + col;
 
@@ -197,6 +251,8 @@ void decode_kernel(DecodeParams p)
         return;
     }
     const int end = min(start + p.part, ctx);
+    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
+    my_id = clamp_block(my_id, p.num_blocks);
 
     bf16x8 qf[H / 32];
     {
@@ -209,16 +265,6 @@ void decode_kernel(DecodeParams p)
             qf[s] = as_bf16x8(raw);
         }
     }
-
-    // The partition's block ids (at most 64: partitions hold <= 1024 tokens),
-    // one per lane, so a chunk reads its two ids with v_readlane instead of a
-    // memory round trip.  Entries past the sequence's last block are not read.
-    const int first_block = start / kBlockSize;
-    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
-    int my_id = 0;
-    if (lane < n_blocks)
-        my_id = clamp_block(p.block_tables[(int64_t)b * p.max_blocks + first_block + lane],
-                            p.num_blocks);
 
     const int64_t tile_elems = (int64_t)kBlockSize * H;              // one (block, head) tile
     const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
@@ -244,27 +290,16 @@ void decode_kernel(DecodeParams p)
     const int n_full = (end - start) / kChunk;                // chunks of 32 valid tokens
     const int n_chunks = n_full + ((end - start) % kChunk != 0);
     const int tail_rem = end - start - n_full * kChunk;
+    auto qfrag = [&](int s) { return qf[s]; };
     auto attend = [&](const ChunkRegs<H> &r, int ci) {
         if (ci < n_full)
-            attend_chunk<H, false>(r, qf, kChunk, quad, p.scale_log2, m, l, acc);
+            attend_chunk<H, false>(r, qfrag, kChunk, quad, p.scale_log2, m, l, acc);
         else
-            attend_chunk<H, true>(r, qf, tail_rem, quad, p.scale_log2, m, l, acc);
+            attend_chunk<H, true>(r, qfrag, tail_rem, quad, p.scale_log2, m, l, acc);
     };
 
-    // Two register buffers: the next chunk's loads are in flight while the
-    // current chunk is computed.
-    ChunkRegs<H> ra, rb;
-    issue(ra, 0);
-    for (int ci = 0; ci < n_chunks; ci += 2) {
-        if (ci + 1 < n_chunks)
-            issue(rb, ci + 1);
-        attend(ra, ci);
-        if (ci + 1 >= n_chunks)
-            break;
-        if (ci + 2 < n_chunks)
-            issue(ra, ci + 2);
-        attend(rb, ci + 1);
-    }
+    ChunkRegs<H> ring[kRing];
+    run_ring(n_chunks, ring, issue, attend);
 
     // Each lane summed its own 8 tokens per chunk; add the four quads.
     l += __shfl_xor(l, 16);
@@ -302,30 +337,74 @@ struct MergeParams {
     int32_t num_parts;
 };
 
-// Log-sum-exp merge of the partitions of one (sequence, head); one thread per
-// output value.  Partition maxima are in log2 units.
-template <int H>
-__global__ __launch_bounds__(H) void merge_kernel(MergeParams p)
+constexpr int kMergeThreads = 256;
+
+// Sum (or max) over the 256 threads of a workgroup; every thread gets the result.
+template <bool kMax>
+__device__ __forceinline__ float block_reduce(float v, float *scratch)
 {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(v, off);
+        v = kMax ? fmaxf(v, o) : v + o;
+    }
+    const int wave = threadIdx.x / kWave;
+    __syncthreads();                       // scratch may still be read by a previous call
+    if ((threadIdx.x % kWave) == 0)
+        scratch[wave] = v;
+    __syncthreads();
+    v = scratch[0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / kWave; ++w)
+        v = kMax ? fmaxf(v, scratch[w]) : v + scratch[w];
+    return v;
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head), one
+// workgroup each: the partition maxima and weighted sums are reduced across
+// the threads, then kMergeThreads / H groups of H threads each accumulate a
+// strided subset of the partitions' o vectors, combined through LDS.
+// Partition maxima are in log2 units.
+template <int H>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
+{
+    constexpr int kGroups = kMergeThreads / H;
+    __shared__ float red[kMergeThreads / kWave];
+    __shared__ float part_sum[kGroups][H];
+
     const int n = blockIdx.x;
     const int b = blockIdx.y;
-    const int h = threadIdx.x;
+    const int tid = threadIdx.x;
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
     const int parts = (ctx + p.part - 1) / p.part;
     const int64_t row = (int64_t)b * p.num_heads + n;
     const float *ml = p.part_ml + row * p.num_parts * 2;
-    const float *po = p.part_o + row * p.num_parts * H + h;
+    const float *po = p.part_o + row * p.num_parts * H;
 
     float big = -INFINITY;
-    for (int j = 0; j < parts; ++j)
+    for (int j = tid; j < parts; j += kMergeThreads)
         big = fmaxf(big, ml[2 * j]);
-    float den = 0.f, num = 0.f;
-    for (int j = 0; j < parts; ++j) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * j] - big);
-        den += w * ml[2 * j + 1];
-        num += w * po[(int64_t)j * H];
+    big = block_reduce<true>(big, red);
+    float den = 0.f;
+    for (int j = tid; j < parts; j += kMergeThreads)
+        den += __builtin_amdgcn_exp2f(ml[2 * j] - big) * ml[2 * j + 1];
+    den = block_reduce<false>(den, red);
+
+    const int h = tid % H;
+    const int grp = tid / H;
+    float num = 0.f;
+#pragma unroll 4
+    for (int j = grp; j < parts; j += kGroups)
+        num += __builtin_amdgcn_exp2f(ml[2 * j] - big) * po[(int64_t)j * H + h];
+    part_sum[grp][h] = num;
+    __syncthreads();
+    if (grp == 0) {
+        float total = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < kGroups; ++g2)
+            total += part_sum[g2][h];
+        p.out[row * H + h] = parts ? total / den : 0.f;
     }
-    p.out[row * H + h] = parts ? num / den : 0.f;
 }
 
 }  // namespace pkv

@@ -1,0 +1,510 @@
+// Token-balanced decode attention for ragged batches (continuous batching).
+//
+// The fixed-partition launch of decode.hpp gives every (partition, KV head,
+// sequence) its own wave.  With ragged contexts -- the continuous-batching mix
+// of "CS336 Lecture 10: Inference", part 6 -- that leaves a tail of unequal
+// waves and pays the start-up latency of every wave (context length, block
+// ids, first loads) once per partition.  Here the grid is exactly the number
+// of waves the chip holds at once, and the work is cut by tokens instead:
+//
+//   * segments s = (sequence b, KV head kvh), in order b-major; segment s has
+//     nc_b = ceil(ctx_b / 32) chunks of 32 tokens;
+//   * the flattened chunk list [0, T), T = K * sum_b nc_b, is split evenly:
+//     wave w gets chunks [floor(w T / W), floor((w+1) T / W));
+//   * a wave walks its chunks in order, crossing segment boundaries without
+//     draining its load pipeline; each (wave, segment) intersection is a
+//     "piece" with its own running maximum, sum and weighted V.
+//
+// A piece that is a whole segment is normalised and written to `out` by its
+// wave.  Other pieces go to the workspace at slot w + s (unique: along the
+// flattened list every wave or segment boundary starts a new piece) and the
+// merge kernel combines them with the log-sum-exp rule.
+//
+// A one-workgroup schedule kernel runs first: it scans the context lengths
+// into chunk offsets cs[b] (exclusive prefix sum of nc_b) and writes each
+// wave's starting (b, kvh, chunk) so that a wave needs one load to begin.
+#pragma once
+
+#include "decode.hpp"
+
+namespace pkv {
+
+constexpr int kScheduleThreads = 1024;
+constexpr int kWindowChunks = 32;   // chunks whose block ids one window holds (64 ids)
+constexpr int kMaxBalancedWaves = 4096;
+
+struct BalancedParams {
+    DecodeParams d;               // shapes, pointers, scale (part/num_parts unused)
+    int32_t *chunk_start;         // [B + 1]: exclusive prefix sum of nc_b (schedule output)
+    int32_t *total_chunks;        // [1]: T = K * chunk_start[B]
+    int4 *wave_start;             // [W]: (b, kvh, chunk in segment, unused)
+    float *piece_o;               // [W + B*K][G][H]
+    float *piece_ml;              // [W + B*K][G][2]
+    int32_t num_waves;            // W (grid size of the decode kernel), a power of two
+    int32_t log2_waves;           // log2(W)
+    int32_t num_seqs;             // B
+    int32_t inline_schedule;      // 1: small batch, waves scan the context lengths themselves
+};
+
+constexpr int kInlineScheduleSeqs = 256;   // largest B scanned inside every wave
+
+__device__ __forceinline__ int chunks_of(int ctx) { return (ctx + kChunk - 1) / kChunk; }
+
+// Uniform (scalar) value of a load whose address is the same in every lane.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int seq_ctx(const DecodeParams &d, int b)
+{
+    return min(max(d.context_lens[b], 0), d.max_ctx);
+}
+
+// seq_ctx for a sequence index that is the same in every lane of the wave.
+__device__ __forceinline__ int seq_ctx_uniform(const DecodeParams &d, int b)
+{
+    return min(max(uniform(d.context_lens[b]), 0), d.max_ctx);
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off)
+            v += t;
+    }
+    return v;
+}
+
+// Small batches: total chunk count T / K (sum of nc_b), by one wave.
+__device__ __forceinline__ int wave_total_chunks(const DecodeParams &d, int B, int lane)
+{
+    int total = 0;
+    for (int base = 0; base < B; base += kWave) {
+        const int b = base + lane;
+        total += wave_sum(b < B ? chunks_of(seq_ctx(d, b)) : 0);
+    }
+    return total;
+}
+
+// floor(w * T / W): first chunk of wave w (W = 2^log2W, so no division).
+__device__ __forceinline__ int wave_begin(int64_t w, int64_t T, int log2W)
+{
+    return (int)((w * T) >> log2W);
+}
+// The wave whose range holds chunk c < T: the largest w with wave_begin(w) <= c.
+// A floating-point estimate, corrected exactly with integer comparisons.
+__device__ __forceinline__ int wave_of(int64_t c, int64_t T, int log2W)
+{
+    const int W = 1 << log2W;
+    int w = (int)(((double)c + 1.0) * (double)W / (double)T) - 1;
+    w = min(max(w, 0), W - 1);
+    while (w + 1 < W && wave_begin(w + 1, T, log2W) <= c)
+        ++w;
+    while (w > 0 && wave_begin(w, T, log2W) > c)
+        --w;
+    return w;
+}
+
+// ---------------------------------------------------------------- schedule --
+
+__global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedParams p)
+{
+    __shared__ int32_t incl[kScheduleThreads];   // inclusive prefix of nc within the tile
+    __shared__ int32_t excl[kScheduleThreads];   // exclusive prefix of nc within the tile
+    __shared__ int32_t carry_s;
+    const int tid = threadIdx.x;
+    const int B = p.num_seqs;
+    const int K = p.d.num_kv_heads;
+    const int W = p.num_waves;
+    const int lg = p.log2_waves;
+
+    // Pass 1: T = K * sum_b nc_b (needed to place the wave boundaries).
+    int mine = 0;
+    for (int b = tid; b < B; b += kScheduleThreads)
+        mine += chunks_of(seq_ctx(p.d, b));
+    incl[tid] = mine;
+    __syncthreads();
+    for (int off = kScheduleThreads / 2; off >= 1; off >>= 1) {
+        if (tid < off)
+            incl[tid] += incl[tid + off];
+        __syncthreads();
+    }
+    const int total_seq = incl[0];
+    const int64_t T = (int64_t)total_seq * K;
+    if (tid == 0) {
+        carry_s = 0;
+        p.total_chunks[0] = (int32_t)T;
+        p.chunk_start[B] = total_seq;
+    }
+    __syncthreads();
+
+    // Pass 2, one tile of sequences at a time: exclusive prefix sums (written
+    // out for the merge), then the start of every wave whose first chunk
+    // falls in this tile, found by binary search over the tile's prefix sums.
+    for (int base = 0; base < B; base += kScheduleThreads) {
+        const int b = base + tid;
+        const int nc = b < B ? chunks_of(seq_ctx(p.d, b)) : 0;
+        incl[tid] = nc;
+        __syncthreads();
+        for (int off = 1; off < kScheduleThreads; off <<= 1) {   // Hillis-Steele scan
+            const int v = tid >= off ? incl[tid - off] : 0;
+            __syncthreads();
+            incl[tid] += v;
+            __syncthreads();
+        }
+        excl[tid] = incl[tid] - nc;
+        const int carry = carry_s;
+        if (b < B)
+            p.chunk_start[b] = carry + incl[tid] - nc;
+        __syncthreads();
+        const int tile_n = min(kScheduleThreads, B - base);
+        const int64_t lo = (int64_t)carry * K;
+        const int64_t hi = (int64_t)(carry + incl[tile_n - 1]) * K;
+        for (int w = tid; w < W; w += kScheduleThreads) {
+            const int64_t c0 = wave_begin(w, T, lg);
+            if (c0 < lo || c0 >= hi)
+                continue;
+            // largest i with (carry + excl[i]) * K <= c0: the sequence holding c0
+            int left = 0, right = tile_n - 1;
+            while (left < right) {
+                const int mid = (left + right + 1) >> 1;
+                if ((int64_t)(carry + excl[mid]) * K <= c0)
+                    left = mid;
+                else
+                    right = mid - 1;
+            }
+            const int ncb = incl[left] - excl[left];
+            const int local = (int)(c0 - (int64_t)(carry + excl[left]) * K);
+            const int kvh = local / ncb;
+            p.wave_start[w] = make_int4(base + left, kvh, local - kvh * ncb, 0);
+        }
+        __syncthreads();
+        if (tid == tile_n - 1)
+            carry_s = carry + incl[tid];
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ decode --
+
+// Position of one chunk in the flattened order: segment (b, kvh), chunk j of
+// the nc chunks of sequence b (ctx tokens).
+struct Pos {
+    int b, kvh, j, nc, ctx;
+};
+
+// One ring slot: the chunk's key/value operands, plus the group's query
+// rows when the chunk opens a segment (or is the wave's first chunk).
+template <int H>
+struct BalancedBuf {
+    ChunkRegs<H> kv;
+    u32x4 q[H / 32];
+};
+
+template <int H>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_balanced_kernel(BalancedParams p)
+{
+    const DecodeParams &d = p.d;
+    const int wv = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+    const int K = d.num_kv_heads;
+    const int B = p.num_seqs;
+    const bool live = col < d.group;
+
+    const int64_t T = p.inline_schedule ? (int64_t)uniform(wave_total_chunks(d, B, lane)) * K
+                                        : (int64_t)uniform(p.total_chunks[0]);
+    if (T == 0)
+        return;
+    const int c_begin = wave_begin(wv, T, p.log2_waves);
+    const int c_end = wave_begin(wv + 1, T, p.log2_waves);
+    if (c_begin >= c_end)
+        return;
+    int4 st;
+    if (p.inline_schedule) {
+        // Find the sequence holding chunk c_begin: the last b whose chunks
+        // start at or before it (empty sequences start where the next one does).
+        int carry = 0;
+        st = make_int4(0, 0, 0, 0);
+        for (int base = 0; base < B; base += kWave) {
+            const int b = base + lane;
+            const int nc = b < B ? chunks_of(seq_ctx(d, b)) : 0;
+            const int incl = wave_inclusive_scan(nc, lane);
+            const int tile_total = __shfl(incl, kWave - 1);
+            if ((int64_t)(carry + tile_total) * K > c_begin) {
+                const int excl = carry + incl - nc;
+                const uint64_t mask =
+                    __builtin_amdgcn_ballot_w64(b < B && (int64_t)excl * K <= c_begin);
+                const int src = 63 - __builtin_clzll(mask);
+                const int ncb = __shfl(nc, src);
+                const int local = c_begin - __shfl(excl, src) * K;
+                const int kvh = local / ncb;
+                st = make_int4(base + src, kvh, local - kvh * ncb, 0);
+                break;
+            }
+            carry += tile_total;
+        }
+    } else {
+        st = p.wave_start[wv];
+    }
+    const int total = c_end - c_begin;           // chunks of this wave
+
+    Pos start;
+    start.b = uniform(st.x);
+    start.kvh = uniform(st.y);
+    start.j = uniform(st.z);
+    start.ctx = seq_ctx_uniform(d, start.b);
+    start.nc = chunks_of(start.ctx);
+    if (start.j >= start.nc)          // cannot happen for a consistent schedule
+        return;
+
+    // The chunk after q in flattened order (the caller knows one exists).
+    auto next_seq = [&](int b) {      // next sequence after b with tokens
+        int nb = b + 1;
+        int ctx = nb < B ? seq_ctx_uniform(d, nb) : 0;
+        while (ctx == 0 && nb + 1 < B) {
+            ++nb;
+            ctx = seq_ctx_uniform(d, nb);
+        }
+        return make_int2(nb, ctx);
+    };
+    auto next_pos = [&](Pos &q) {
+        if (++q.j < q.nc)
+            return;
+        q.j = 0;
+        if (++q.kvh < K)
+            return;
+        q.kvh = 0;
+        const int2 nx = next_seq(q.b);
+        q.b = nx.x;
+        q.ctx = nx.y;
+        q.nc = chunks_of(q.ctx);
+    };
+
+    const int64_t tile_elems = (int64_t)kBlockSize * H;
+    const int64_t block_elems = (int64_t)K * tile_elems;
+
+    // ---- issue side: its own cursor and a window of block ids ----
+    // Lane i of `ids` holds block 2*wj + i of sequence wb (windows of 32
+    // chunks, aligned); the window after it in issue order is prefetched.
+    Pos ip = start;
+    int wb = -1, wj = 0, ids = 0;
+    int pb = -1, pj = 0, ids_pre = 0;
+    auto fetch_ids = [&](int b, int j0, int ctx) {
+        const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+        int id = 0;
+        if (lane < min(2 * kWindowChunks, nblk - 2 * j0))
+            id = d.block_tables[(int64_t)b * d.max_blocks + 2 * j0 + lane];
+        return clamp_block(id, d.num_blocks);
+    };
+    auto issue = [&](BalancedBuf<H> &r, int k) {
+        if (k > 0)
+            next_pos(ip);
+        const int J = ip.j & ~(kWindowChunks - 1);
+        if (ip.b != wb || J != wj) {
+            ids = (ip.b == pb && J == pj) ? ids_pre : fetch_ids(ip.b, J, ip.ctx);
+            wb = ip.b;
+            wj = J;
+            // the window that follows (wb, wj) in issue order
+            int nb = wb, nj = wj + kWindowChunks, nctx = ip.ctx;
+            if (nj >= ip.nc) {
+                nj = 0;
+                if (ip.kvh + 1 >= K) {
+                    const int2 nx = next_seq(wb);
+                    nb = nx.x;
+                    nctx = nx.y;
+                }
+            }
+            pb = -1;
+            if ((nb != wb || nj != wj) && nb < B && nctx > 0) {
+                pb = nb;
+                pj = nj;
+                ids_pre = fetch_ids(nb, nj, nctx);
+            }
+        }
+        const int nblk = (ip.ctx + kBlockSize - 1) / kBlockSize;
+        const int slot = 2 * (ip.j - wj);
+        const int id0 = __builtin_amdgcn_readlane(ids, slot);
+        const int id1 = (2 * ip.j + 1 < nblk) ? __builtin_amdgcn_readlane(ids, slot + 1) : id0;
+        const uint16_t *kb = d.key_cache + ip.kvh * tile_elems;
+        const uint16_t *vb = d.value_cache + ip.kvh * tile_elems;
+        load_chunk<H>(r.kv, kb + id0 * block_elems, kb + id1 * block_elems,
+                      vb + id0 * block_elems, vb + id1 * block_elems, col, quad);
+        if (k == 0 || ip.j == 0) {    // the chunk opens a segment: bring its queries
+            const int n = ip.kvh * d.group + (live ? col : 0);
+            const uint16_t *qrow = d.q + ((int64_t)ip.b * d.num_heads + n) * H;
+#pragma unroll
+            for (int s = 0; s < H / 32; ++s) {
+                r.q[s] = load16(qrow + 32 * s + 8 * quad);
+                if (!live)
+                    r.q[s] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    // ---- attend side: its own cursor, the running softmax state ----
+    Pos ap = start;
+    u32x4 qcur[H / 32];
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[H / 16];
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c)
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool piece_from_start = start.j == 0;   // this wave's piece began at the segment start
+    auto qfrag = [&](int s) { return as_bf16x8(qcur[s]); };
+
+    auto attend = [&](const BalancedBuf<H> &r, int k) {
+        if (k > 0)
+            next_pos(ap);
+        if (k == 0 || ap.j == 0) {
+#pragma unroll
+            for (int s = 0; s < H / 32; ++s)
+                qcur[s] = r.q[s];
+        }
+        const bool seg_end = ap.j + 1 == ap.nc;
+        if (!seg_end || ap.ctx % kChunk == 0)
+            attend_chunk<H, false>(r.kv, qfrag, kChunk, quad, d.scale_log2, m, l, acc);
+        else
+            attend_chunk<H, true>(r.kv, qfrag, ap.ctx - kChunk * ap.j, quad, d.scale_log2, m, l,
+                                  acc);
+        if (!seg_end && k + 1 < total)
+            return;
+        // The piece ends here (segment end, or the wave's last chunk).
+        float lt = l + __shfl_xor(l, 16);
+        lt += __shfl_xor(lt, 32);
+        const int n = ap.kvh * d.group + col;
+        if (live) {
+            if (piece_from_start && seg_end) {          // the whole segment: final output
+                const float inv = 1.0f / lt;
+                float *o = d.out + ((int64_t)ap.b * d.num_heads + n) * H;
+#pragma unroll
+                for (int c = 0; c < H / 16; ++c)
+                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
+            } else {
+                const int64_t slot = ((int64_t)wv + (int64_t)ap.b * K + ap.kvh) * d.group + col;
+                float *o = p.piece_o + slot * H;
+#pragma unroll
+                for (int c = 0; c < H / 16; ++c)
+                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c];
+                if (quad == 0) {
+                    p.piece_ml[2 * slot] = m;
+                    p.piece_ml[2 * slot + 1] = lt;
+                }
+            }
+        }
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        piece_from_start = true;                    // the next piece opens a segment
+    };
+
+    BalancedBuf<H> ring[kRing];
+    run_ring(total, ring, issue, attend);
+}
+
+// ------------------------------------------------------------------- merge --
+
+// One wave per (sequence, query head): combines the pieces of its segment,
+// or writes zeros for an empty sequence.  Segments held whole by one wave
+// were written by that wave and are skipped.  Waves between the segment's
+// first and last may own no chunk at all (when the batch has fewer chunks
+// than waves); they wrote no piece.  The pieces' weights 2^(m - M) go
+// through LDS; the o vectors are then summed with one load per piece and lane.
+template <int H>
+__global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
+{
+    const DecodeParams &d = p.d;
+    const int n = blockIdx.x;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int K = d.num_kv_heads;
+    const int kvh = n / d.group;
+    const int g = n % d.group;
+    const int nc = chunks_of(seq_ctx(d, b));
+    float *o = d.out + ((int64_t)b * d.num_heads + n) * H;
+    if (nc == 0) {
+        for (int h = lane; h < H; h += kWave)
+            o[h] = 0.f;
+        return;
+    }
+    const int lg = p.log2_waves;
+    int64_t T;
+    int64_t seq_first;                    // chunk_start[b]
+    if (p.inline_schedule) {
+        int carry = 0, before = 0;
+        for (int base = 0; base < p.num_seqs; base += kWave) {
+            const int bb = base + lane;
+            const int c = bb < p.num_seqs ? chunks_of(seq_ctx(d, bb)) : 0;
+            carry += wave_sum(c);
+            before += wave_sum(bb < b ? c : 0);
+        }
+        T = (int64_t)carry * K;
+        seq_first = before;
+    } else {
+        T = p.total_chunks[0];
+        seq_first = p.chunk_start[b];
+    }
+    const int64_t first = seq_first * K + (int64_t)kvh * nc;
+    const int w_first = wave_of(first, T, lg);
+    const int w_last = wave_of(first + nc - 1, T, lg);
+    if (w_first == w_last)
+        return;
+    const int64_t seg = (int64_t)b * K + kvh;
+    const int count = w_last - w_first + 1;
+    auto empty = [&](int w) { return wave_begin(w, T, lg) == wave_begin(w + 1, T, lg); };
+    auto slot_of = [&](int w) { return ((int64_t)w + seg) * d.group + g; };
+
+    float big = -INFINITY;
+    for (int i = lane; i < count; i += kWave)
+        if (!empty(w_first + i))
+            big = fmaxf(big, p.piece_ml[2 * slot_of(w_first + i)]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        big = fmaxf(big, __shfl_xor(big, off));
+
+    // Pieces in tiles of 64: lane i holds the weight 2^(m - M) of piece i.
+    float den = 0.f;
+    float num[H / kWave];
+#pragma unroll
+    for (int k = 0; k < H / kWave; ++k)
+        num[k] = 0.f;
+    for (int base = 0; base < count; base += kWave) {
+        float wt = 0.f;
+        const int i = base + lane;
+        if (i < count && !empty(w_first + i)) {
+            const int64_t slot = slot_of(w_first + i);
+            wt = __builtin_amdgcn_exp2f(p.piece_ml[2 * slot] - big);
+            den += wt * p.piece_ml[2 * slot + 1];
+        }
+        const int n_tile = min(kWave, count - base);
+        for (int t = 0; t < n_tile; ++t) {
+            const float wt_t = __shfl(wt, t);
+            if (wt_t == 0.f)
+                continue;   // empty wave (or a piece that underflows to 0)
+            const float *po = p.piece_o + slot_of(w_first + base + t) * H;
+#pragma unroll
+            for (int k = 0; k < H / kWave; ++k)
+                num[k] += wt_t * po[lane + kWave * k];
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        den += __shfl_xor(den, off);
+#pragma unroll
+    for (int k = 0; k < H / kWave; ++k)
+        o[lane + kWave * k] = num[k] / den;
+}
+
+}  // namespace pkv

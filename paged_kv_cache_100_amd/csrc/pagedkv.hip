@@ -9,6 +9,7 @@
 #include "pagedkv.h"
 #include "kernels/append.hpp"
 #include "kernels/decode.hpp"
+#include "kernels/decode_balanced.hpp"
 #include "kernels/stream_read.hpp"
 
 namespace {
@@ -21,24 +22,10 @@ bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Launch shape: with at least this many (partition, KV head, sequence) waves
-// the 256 CUs (1024 SIMDs) hold two to four rounds of resident waves.
-constexpr int64_t kTargetWaves = 4096;
-
-int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
-                         int32_t requested)
-{
-    if (requested > 0)
-        return requested;
-    static const int32_t kSizes[] = {512, 256, 128, 64};
-    for (int32_t part : kSizes)
-        if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_ctx, part) >= kTargetWaves)
-            return part;
-    return 32;
-}
-
-size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                           int32_t max_ctx, int32_t part)
+// Fixed-partition mode: bytes of partial results ([B][N][P][H] o, then
+// [B][N][P][2] (m, l)); 0 when one partition covers the context.
+size_t fixed_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                             int32_t max_ctx, int32_t part)
 {
     const int64_t parts = ceil_div(max_ctx, part);
     if (parts <= 1)
@@ -46,6 +33,63 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim
     const int64_t rows = (int64_t)num_seqs * num_heads * parts;
     const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
     return (size_t)(o_bytes + rows * 2 * 4);
+}
+
+// Token-balanced mode: the layout of its workspace, sized for the largest
+// wave count any device uses (so the size does not depend on the device).
+struct BalancedLayout {
+    size_t total, chunk_start, total_chunks, wave_start, piece_ml, piece_o;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim)
+{
+    const int64_t group = num_heads / num_kv_heads;
+    const int64_t pieces = (int64_t)pkv::kMaxBalancedWaves + (int64_t)num_seqs * num_kv_heads;
+    BalancedLayout L;
+    size_t off = 0;
+    L.total_chunks = off;
+    off = align256(off + 16);
+    L.chunk_start = off;
+    off = align256(off + (size_t)(num_seqs + 1) * 4);
+    L.wave_start = off;
+    off = align256(off + (size_t)pkv::kMaxBalancedWaves * 16);
+    L.piece_ml = off;
+    off = align256(off + (size_t)(pieces * group * 2 * 4));
+    L.piece_o = off;
+    off = align256(off + (size_t)(pieces * group * head_dim * 4));
+    L.total = off;
+    return L;
+}
+
+// Waves the decode kernel keeps resident: one per SIMD, four SIMDs per CU.
+// The balanced schedule uses the largest power of two not above that, so
+// that wave boundaries need no division.
+constexpr int kWavesPerCU = 4;
+
+int device_waves(int *log2_waves)
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return PKV_ERR_DEVICE;
+    if (dev < 64 && cached[dev] > 0) {
+        *log2_waves = cached[dev];
+        return PKV_OK;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return PKV_ERR_DEVICE;
+    int lg = 0;
+    while ((2 << lg) <= cus * kWavesPerCU && (2 << lg) <= pkv::kMaxBalancedWaves)
+        ++lg;
+    if (dev < 64)
+        cached[dev] = lg;
+    *log2_waves = lg;
+    return PKV_OK;
 }
 
 int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream)
@@ -112,23 +156,16 @@ int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, v
     return launch(kern, dim3((unsigned)blocks), dim3(256), &p, stream);
 }
 
-int32_t paged_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads,
-                                    int32_t max_context_len, int32_t partition_size)
-{
-    return choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
-}
-
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                    int32_t head_dim, int32_t max_context_len,
                                    int32_t partition_size)
 {
     if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_context_len <= 0)
+        max_context_len <= 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
         return 0;
-    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
-    if (part <= 0)
-        return 0;
-    return workspace_bytes_for(num_seqs, num_heads, head_dim, max_context_len, part);
+    if (partition_size == 0)
+        return balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim).total;
+    return fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
 }
 
 int paged_decode_attention(float *out, const void *q, const void *key_cache,
@@ -172,29 +209,10 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
         (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return PKV_ERR_ALIGN;
 
-    const int32_t part = choose_partition(num_seqs, num_kv_heads, max_context_len > 0
-                                          ? max_context_len : 1, partition_size);
-    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
-    const bool split = parts > 1;
-    const size_t need = split ? workspace_bytes_for(num_seqs, num_heads, head_dim,
-                                                    max_context_len, part) : 0;
-    if (split) {
-        if (!workspace || workspace_bytes < need)
-            return PKV_ERR_WORKSPACE;
-        if (!aligned16(workspace))
-            return PKV_ERR_ALIGN;
-    }
-
     pkv::DecodeParams p;
     p.out = out;
     p.part_o = nullptr;
     p.part_ml = nullptr;
-    if (split) {
-        const int64_t rows = (int64_t)num_seqs * num_heads * parts;
-        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
-        p.part_o = static_cast<float *>(workspace);
-        p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
-    }
     p.q = static_cast<const uint16_t *>(q);
     p.key_cache = static_cast<const uint16_t *>(key_cache);
     p.value_cache = static_cast<const uint16_t *>(value_cache);
@@ -206,9 +224,70 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
     p.group = num_heads / num_kv_heads;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
-    p.part = part;
-    p.num_parts = (int32_t)parts;
+    p.part = partition_size;
+    p.num_parts = 1;
     p.num_blocks = num_blocks;
+
+    if (partition_size == 0) {
+        // Token-balanced: schedule, persistent decode, merge of split segments.
+        if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
+            return PKV_ERR_SHAPE;
+        const BalancedLayout L = balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim);
+        if (!workspace || workspace_bytes < L.total)
+            return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return PKV_ERR_ALIGN;
+        int log2_waves = 0;
+        int rc = device_waves(&log2_waves);
+        if (rc != PKV_OK)
+            return rc;
+        const int waves = 1 << log2_waves;
+        char *ws = static_cast<char *>(workspace);
+        pkv::BalancedParams bp;
+        bp.d = p;
+        bp.total_chunks = reinterpret_cast<int32_t *>(ws + L.total_chunks);
+        bp.chunk_start = reinterpret_cast<int32_t *>(ws + L.chunk_start);
+        bp.wave_start = reinterpret_cast<int4 *>(ws + L.wave_start);
+        bp.piece_ml = reinterpret_cast<float *>(ws + L.piece_ml);
+        bp.piece_o = reinterpret_cast<float *>(ws + L.piece_o);
+        bp.num_waves = waves;
+        bp.log2_waves = log2_waves;
+        bp.num_seqs = num_seqs;
+        bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
+        if (!bp.inline_schedule) {
+            rc = launch((const void *)pkv::schedule_kernel, dim3(1), dim3(pkv::kScheduleThreads),
+                        &bp, stream);
+            if (rc != PKV_OK)
+                return rc;
+        }
+        const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<128>
+                                         : (const void *)pkv::decode_balanced_kernel<64>;
+        rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
+        if (rc != PKV_OK)
+            return rc;
+        const void *mk = head_dim == 128 ? (const void *)pkv::merge_pieces_kernel<128>
+                                         : (const void *)pkv::merge_pieces_kernel<64>;
+        return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kWave), &bp,
+                      stream);
+    }
+
+    // Fixed partitions of partition_size tokens, one wave each.
+    const int32_t part = partition_size;
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
+    const bool split = parts > 1;
+    if (split) {
+        const size_t need = fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                                  part);
+        if (!workspace || workspace_bytes < need)
+            return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return PKV_ERR_ALIGN;
+        const int64_t rows = (int64_t)num_seqs * num_heads * parts;
+        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+        p.part_o = static_cast<float *>(workspace);
+        p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    p.num_parts = (int32_t)parts;
 
     const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
     const void *kern;
@@ -233,7 +312,8 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
     mp.num_parts = (int32_t)parts;
     const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
                                      : (const void *)pkv::merge_kernel<64>;
-    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(head_dim), &mp, stream);
+    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads), &mp,
+                  stream);
 }
 
 size_t pagedkv_stream_read_sink_bytes(size_t bytes)

@@ -32,7 +32,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
-            "paged_decode_partition_size", "pagedkv_status_string", "pagedkv_version",
+            "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in pagedkv.h but not exported"
@@ -90,17 +90,17 @@ def test_decode_checks(L):
     assert decode(L, ws=MIS, part=32) == ALIGN
 
 
-def test_partition_and_workspace_sizes(L):
-    # Llama-3-8B shape: 64 x 8 groups x 16 partitions of 512 >= 4096 waves
-    assert pkv.partition_size(64, 8, 8192) == 512
-    # Llama-2-13B, B = 1: small batch -> short partitions for more waves
-    assert pkv.partition_size(1, 40, 1024) == 32
-    assert pkv.partition_size(4, 8, 131072, 512) == 512
-    # one partition: no workspace
-    assert pkv.workspace_size(4, 8, 2, 64, 32) == 0
-    # B=4, N=64, H=128, 256 partitions: o (B*N*P*H*4) + (m, l) (B*N*P*2*4)
+def test_workspace_sizes(L):
+    # fixed partitions: one partition covers the context -> no workspace
+    assert pkv.workspace_size(4, 8, 2, 64, 32, 32) == 0
+    # B=4, N=64, H=128, 256 partitions of 512: o (B*N*P*H*4) then (m, l) (B*N*P*2*4)
     rows = 4 * 64 * 256
     assert pkv.workspace_size(4, 64, 8, 128, 131072, 512) == rows * 128 * 4 + rows * 8
+    # token-balanced: independent of the context bound, grows with B*K
+    a = pkv.workspace_size(64, 32, 8, 128, 8192, 0)
+    assert a > 0 and a == pkv.workspace_size(64, 32, 8, 128, 100, 0)
+    assert pkv.workspace_size(128, 32, 8, 128, 8192, 0) > a
+    assert pkv.workspace_size(0, 32, 8, 128, 8192, 0) == 0
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -15,16 +15,18 @@ pytestmark = pytest.mark.gpu
 SPEC = W.Spec("inv", B=6, N=32, K=8, H=128, ctx=[1000, 37, 1600, 513, 64, 2048], seed=23)
 
 
-def test_rerun_is_bit_identical():
+@pytest.mark.parametrize("partition", [0, 256])
+def test_rerun_is_bit_identical(partition):
     w = W.make(SPEC)
-    a, _ = H.gpu_step(w, partition=256)
-    b, _ = H.gpu_step(w, partition=256)
+    a, _ = H.gpu_step(w, partition=partition)
+    b, _ = H.gpu_step(w, partition=partition)
     assert torch.equal(a, b)
 
 
-def test_block_relabelling_is_bit_identical():
+@pytest.mark.parametrize("partition", [0, 256])
+def test_block_relabelling_is_bit_identical(partition):
     w = W.make(SPEC)
-    base, _ = H.gpu_step(w, partition=256)
+    base, _ = H.gpu_step(w, partition=partition)
     g = torch.Generator().manual_seed(5)
     relabel = torch.randperm(w.num_blocks, generator=g)          # old id -> new id
     w2 = W.make(SPEC)
@@ -32,16 +34,17 @@ def test_block_relabelling_is_bit_identical():
     w2.value_cache[relabel] = w.value_cache.clone()
     w2.block_tables = relabel[w.block_tables.long()].to(torch.int32)
     w2.slot_mapping = relabel[w.slot_mapping // 16] * 16 + w.slot_mapping % 16
-    got, _ = H.gpu_step(w2, partition=256)
+    got, _ = H.gpu_step(w2, partition=partition)
     assert torch.equal(got, base)
 
 
-def test_shared_prefix_is_bit_identical_to_copies():
+@pytest.mark.parametrize("partition", [0, 512])
+def test_shared_prefix_is_bit_identical_to_copies(partition):
     spec = W.Spec("share", B=5, N=64, K=8, H=128, ctx=[1500, 1200, 40, 2100, 1001],
                   shared_prefix=1000, sharers=3, key_scale=2.0, seed=29)
     w = W.make(spec)
     assert len(w.sharer_ids) == 3 and len(w.shared_blocks) == 62
-    shared, _ = H.gpu_step(w, partition=512)
+    shared, _ = H.gpu_step(w, partition=partition)
     # give each later sharer private copies of the shared blocks
     w2 = W.make(spec)
     nb = w2.num_blocks
@@ -55,14 +58,15 @@ def test_shared_prefix_is_bit_identical_to_copies():
         vc[ids] = w2.value_cache[src]
         w2.block_tables[b, :62] = ids.to(torch.int32)
     w2.key_cache, w2.value_cache = kc, vc
-    copied, _ = H.gpu_step(w2, partition=512)
+    copied, _ = H.gpu_step(w2, partition=partition)
     assert torch.equal(shared, copied)
 
 
-def test_larger_launch_bound_is_bit_identical():
+@pytest.mark.parametrize("partition", [0, 128])
+def test_larger_launch_bound_is_bit_identical(partition):
     w = W.make(SPEC)
-    a, _ = H.gpu_step(w, partition=128)
-    b, _ = H.gpu_step(w, partition=128, max_context_len=w.block_tables.shape[1] * 16)
+    a, _ = H.gpu_step(w, partition=partition)
+    b, _ = H.gpu_step(w, partition=partition, max_context_len=w.block_tables.shape[1] * 16)
     assert torch.equal(a, b)
 
 
@@ -70,6 +74,7 @@ def test_single_pass_matches_split():
     spec = W.Spec("sp", B=4, N=32, K=8, H=128, ctx=[1024, 999, 33, 512], seed=31)
     w = W.make(spec)
     one, _ = H.gpu_step(w, partition=1024)
-    many, _ = H.gpu_step(w, partition=32)
-    abs_err, rel, _ = H.errors(one.numpy(), many.numpy())
-    assert abs_err < 1e-4 and rel < 1e-4
+    for other in (32, 0):
+        many, _ = H.gpu_step(w, partition=other)
+        abs_err, rel, _ = H.errors(one.numpy(), many.numpy())
+        assert abs_err < 1e-4 and rel < 1e-4

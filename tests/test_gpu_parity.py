@@ -69,3 +69,18 @@ def test_single_pass_path():
     # one partition covers every context: the kernel normalises and writes out itself
     spec = W.Spec("single", B=5, N=32, K=8, H=128, ctx=[1, 30, 200, 640, 1024], seed=17)
     run_case(spec, partition=1024, what="single pass")
+
+
+def test_many_sequences_and_empty_ones():
+    # more sequences than the schedule kernel's tile of 1024, empty sequences
+    # in between, and far fewer chunks than resident waves in places
+    ctx = [(37 * i) % 90 if i % 7 else 0 for i in range(1300)]
+    spec = W.Spec("many", B=1300, N=8, K=2, H=64, ctx=ctx, max_blocks=6, seed=37)
+    for partition in (0, 32):
+        run_case(spec, partition=partition, what=f"B=1300 part {partition}")
+
+
+def test_one_long_sequence_among_short_ones():
+    # one segment spread over many waves, the others each inside one wave
+    spec = W.Spec("skew", B=9, N=64, K=8, H=128, ctx=[6000] + [40] * 8, seed=41)
+    run_case(spec, partition=0, what="skewed")
