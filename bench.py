@@ -72,9 +72,11 @@ def traffic_from_profile(workload: str):
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The CPU oracle, untuned, on a growing prefix of the batch until about
-    ``budget_s`` seconds of work; reported as tokens/s per layer (one decode
-    token per sequence) and KV GB/s."""
+    """The CPU oracle, untuned, on this host: the workload's decode step (after
+    the oracle's own append) repeated until about ``budget_s`` seconds of
+    work, or -- when one full step takes longer -- a prefix of the batch
+    grown until it does.  Reported as tokens/s per layer (one decode token per
+    sequence) and KV GB/s."""
     import numpy as np
     import torch
     import oracle
@@ -84,25 +86,31 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
 
     q, kc, vc = u16(w.q), u16(w.key_cache), u16(w.value_cache)
     bt, cl = w.block_tables.numpy(), w.context_lens.numpy()
-    # append first so the cache holds the step's token, as on the GPU
     kc, vc = kc.copy(), vc.copy()
     oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
     B = w.spec.B
-    n, spent, done_seqs, done_tokens = 1, 0.0, 0, 0
-    while True:
-        n = min(n, B)
+    n = 1
+    while True:                       # smallest prefix that takes >= budget/10
         t0 = time.perf_counter()
         oracle.decode(q[:n], kc, vc, bt[:n], cl[:n], w.scale)
         dt = time.perf_counter() - t0
-        spent, done_seqs, done_tokens = dt, n, int(cl[:n].sum())
-        if dt >= budget_s / 3 or n == B:
+        if dt >= budget_s / 10 or n == B:
             break
-        n *= 2
-    kv_bytes = done_tokens * w.spec.K * w.spec.H * 4
-    return {"value": done_seqs / spent, "unit": "tokens/s per layer", "cores": oracle.num_threads(),
-            "kind": "oracle", "kv_GBps": kv_bytes / spent / 1e9,
-            "sample": f"first {done_seqs} of {B} sequences ({done_tokens} cached tokens), "
-                      f"fp64 C oracle with OpenMP, {spent:.2f} s"}
+        n = min(2 * n, B)
+    reps, spent = 1, dt
+    while spent < budget_s and n == B:
+        t0 = time.perf_counter()
+        oracle.decode(q, kc, vc, bt, cl, w.scale)
+        spent += time.perf_counter() - t0
+        reps += 1
+    tokens = int(cl[:n].sum()) * reps
+    kv_bytes = tokens * w.spec.K * w.spec.H * 4
+    what = (f"the full batch of {B} sequences, {reps} times" if n == B
+            else f"the first {n} of {B} sequences")
+    return {"value": n * reps / spent, "unit": "tokens/s per layer",
+            "cores": oracle.num_threads(), "kind": "oracle", "kv_GBps": kv_bytes / spent / 1e9,
+            "sample": f"{what} ({tokens} cached tokens attended), fp64 C oracle with OpenMP, "
+                      f"{spent:.1f} s"}
 
 
 def main() -> int:
@@ -152,20 +160,31 @@ def main() -> int:
                                    g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
                                    partition=part, workspace=workspace)
 
-    # achievable read bandwidth: one plain 16-byte streaming read of 2 GiB
-    probe_src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    # Achievable bandwidth: plain 16-byte streaming read of 1 GiB, and a 1 GiB
+    # copy (its known read and write sizes also scale the HBM byte counters
+    # in a profiler run of this script).
+    probe_bytes = 1 << 30
+    probe_src = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
+    probe_dst = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
     sink = pkv.stream_read(probe_src)
+    pkv.stream_copy(probe_src, probe_dst)
     torch.cuda.synchronize()
-    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    probe_ms = []
-    for _ in range(6):
-        pe0.record()
-        pkv.stream_read(probe_src, sink)
-        pe1.record()
-        torch.cuda.synchronize()
-        probe_ms.append(pe0.elapsed_time(pe1))
-    probe_gbps = (1 << 31) / (sorted(probe_ms)[len(probe_ms) // 2] * 1e-3) / 1e9
-    del probe_src
+
+    def median_ms(fn, reps=5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    probe_read_gbps = probe_bytes / (median_ms(lambda: pkv.stream_read(probe_src, sink)) * 1e-3) / 1e9
+    probe_copy_gbps = 2 * probe_bytes / (median_ms(lambda: pkv.stream_copy(probe_src, probe_dst))
+                                         * 1e-3) / 1e9
+    del probe_src, probe_dst
 
     for _ in range(args.warmup):
         append()
@@ -215,7 +234,8 @@ def main() -> int:
         "attention_tokens_per_s_per_layer": round(s.B / (attn_avg * 1e-3), 1),
         "attention_ms": round(attn_avg, 5),
         "append_ms": round(sum(append_ms) / K, 5),
-        "probe_read_GBps": round(probe_gbps, 1),
+        "probe_read_GBps": round(probe_read_gbps, 1),
+        "probe_copy_GBps": round(probe_copy_gbps, 1),
         "roofline": {"kernel": "paged_decode_attention (all kernels of the call)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -177,6 +177,14 @@ int paged_decode_attention(float *out, const void *q,
 size_t pagedkv_stream_read_sink_bytes(size_t bytes);
 int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream);
 
+/*
+ * pagedkv_stream_copy -- measurement helper, not part of the method: copies
+ * `bytes` (a multiple of 16) from src to dst (non-overlapping, 16-byte
+ * aligned) with 16-byte loads and stores.  A launch that reads and writes a
+ * known number of bytes, for scaling HBM read/write counters.
+ */
+int pagedkv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* Human-readable name of a pkv_status value (static string, never NULL). */
 const char *pagedkv_status_string(int status);
 

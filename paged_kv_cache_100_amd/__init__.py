@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.pagedkv_stream_read_sink_bytes.restype = sz
     L.pagedkv_stream_read.argtypes = [P, sz, P, P]
     L.pagedkv_stream_read.restype = ctypes.c_int
+    L.pagedkv_stream_copy.argtypes = [P, P, sz, P]
+    L.pagedkv_stream_copy.restype = ctypes.c_int
     L.pagedkv_status_string.argtypes = [ctypes.c_int]
     L.pagedkv_status_string.restype = ctypes.c_char_p
     L.pagedkv_version.argtypes = []
@@ -182,6 +184,18 @@ def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch
     _check(lib().pagedkv_stream_read(src.data_ptr(), nbytes, sink.data_ptr(),
                                      _stream(src.device)), "pagedkv_stream_read")
     return sink
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Measurement helper: copy ``src`` into ``dst`` with 16-byte accesses."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous GPU tensors")
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().pagedkv_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                     _stream(src.device)), "pagedkv_stream_copy")
+    return dst
 
 
 def version() -> str:

@@ -351,4 +351,27 @@ int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream)
     return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
+int pagedkv_stream_copy(const void *src, void *dst, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return PKV_OK;
+    if (!src || !dst)
+        return PKV_ERR_NULL;
+    if (bytes % 16 != 0)
+        return PKV_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(dst))
+        return PKV_ERR_ALIGN;
+    struct {
+        const pkv::u32x4 *src;
+        pkv::u32x4 *dst;
+        int64_t n16;
+    } a = {static_cast<const pkv::u32x4 *>(src), static_cast<pkv::u32x4 *>(dst),
+           (int64_t)(bytes / 16)};
+    void *args[] = {&a.src, &a.dst, &a.n16};
+    hipError_t err = hipLaunchKernel((const void *)pkv::stream_copy_kernel,
+                                     dim3(pkv::kStreamBlocksMax), dim3(pkv::kStreamThreads), args,
+                                     0, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
 }  // extern "C"

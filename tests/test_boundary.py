@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
             "pagedkv_status_string", "pagedkv_version",
-            "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes"} <= set(names)
+            "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
+            "pagedkv_stream_copy"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in pagedkv.h but not exported"
 
