@@ -23,4 +23,33 @@ __device__ __forceinline__ u32x4 load16_stream(const void *p)
 }
 __device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
+// Load of a value that is the same for every lane and does not change while
+// the kernel runs (context lengths, block-table entries): through the
+// constant address space it becomes a scalar-unit load, which neither waits
+// for nor holds up the wave's vector-memory (K/V) loads.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int32_t scalar_load(const int32_t *p) { return *(const const_i32 *)p; }
+
+// Lane-pair reductions across the four 16-lane rows with VALU permutes
+// (no LDS round trip): max / sum of v over lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float max_over_rows(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_over_rows(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 }  // namespace pkv

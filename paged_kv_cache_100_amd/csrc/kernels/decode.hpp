@@ -143,8 +143,7 @@ __device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, 
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_rows(mx);
     const float m_new = fmaxf(m, mx);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first chunk
 
@@ -176,7 +175,7 @@ __device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, 
 // Depth of the register ring: chunks issued ahead of the one being computed
 // is kRing - 1 (16 KiB each).  One wave per SIMD owns up to 512 registers,
 // enough for four 64-register chunk buffers next to the accumulators.
-constexpr int kRing = 4;
+constexpr int kRingDepth = 4;
 
 // Runs chunks 0 .. total-1 (total >= 1) through a ring of kRing register
 // buffers: issue(buf, k) starts the loads of chunk k, attend(buf, k) consumes
@@ -184,7 +183,7 @@ constexpr int kRing = 4;
 // that follows it, so the compiler's wait counts are exact there: computing
 // chunk k waits for chunk k's loads only, with chunks k+1 .. k+kRing-1 in
 // flight.  The last (up to 2*kRing - 1) chunks run through a guarded copy.
-template <class Buf, class Issue, class Attend>
+template <int kRing, class Buf, class Issue, class Attend>
 __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&issue,
                                          Attend &&attend)
 {
@@ -298,12 +297,11 @@ void decode_kernel(DecodeParams p)
             attend_chunk<H, true>(r, qfrag, tail_rem, quad, p.scale_log2, m, l, acc);
     };
 
-    ChunkRegs<H> ring[kRing];
-    run_ring(n_chunks, ring, issue, attend);
+    ChunkRegs<H> ring[kRingDepth];
+    run_ring<kRingDepth>(n_chunks, ring, issue, attend);
 
     // Each lane summed its own 8 tokens per chunk; add the four quads.
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_over_rows(l);
     if (!live)
         return;
     // acc[c] holds O^T[16c + 4quad + i][col], i = 0..3.

@@ -26,18 +26,19 @@
 #pragma once
 
 #include "decode.hpp"
+#include "pagedkv.h"
 
 namespace pkv {
 
 constexpr int kScheduleThreads = 1024;
-constexpr int kWindowChunks = 32;   // chunks whose block ids one window holds (64 ids)
 constexpr int kMaxBalancedWaves = 4096;
+constexpr int kBalancedRing = 3;
 
 struct BalancedParams {
     DecodeParams d;               // shapes, pointers, scale (part/num_parts unused)
     int32_t *chunk_start;         // [B + 1]: exclusive prefix sum of nc_b (schedule output)
     int32_t *total_chunks;        // [1]: T = K * chunk_start[B]
-    int4 *wave_start;             // [W]: (b, kvh, chunk in segment, unused)
+    int4 *wave_start;             // [W]: (b, kvh, chunk in segment, ctx of b)
     float *piece_o;               // [W + B*K][G][H]
     float *piece_ml;              // [W + B*K][G][2]
     int32_t num_waves;            // W (grid size of the decode kernel), a power of two
@@ -61,7 +62,7 @@ __device__ __forceinline__ int seq_ctx(const DecodeParams &d, int b)
 // seq_ctx for a sequence index that is the same in every lane of the wave.
 __device__ __forceinline__ int seq_ctx_uniform(const DecodeParams &d, int b)
 {
-    return min(max(uniform(d.context_lens[b]), 0), d.max_ctx);
+    return min(max(scalar_load(d.context_lens + b), 0), d.max_ctx);
 }
 
 __device__ __forceinline__ int wave_sum(int v)
@@ -81,17 +82,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane)
             v += t;
     }
     return v;
-}
-
-// Small batches: total chunk count T / K (sum of nc_b), by one wave.
-__device__ __forceinline__ int wave_total_chunks(const DecodeParams &d, int B, int lane)
-{
-    int total = 0;
-    for (int base = 0; base < B; base += kWave) {
-        const int b = base + lane;
-        total += wave_sum(b < B ? chunks_of(seq_ctx(d, b)) : 0);
-    }
-    return total;
 }
 
 // floor(w * T / W): first chunk of wave w (W = 2^log2W, so no division).
@@ -184,7 +174,8 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
             const int ncb = incl[left] - excl[left];
             const int local = (int)(c0 - (int64_t)(carry + excl[left]) * K);
             const int kvh = local / ncb;
-            p.wave_start[w] = make_int4(base + left, kvh, local - kvh * ncb, 0);
+            p.wave_start[w] = make_int4(base + left, kvh, local - kvh * ncb,
+                                        seq_ctx(p.d, base + left));
         }
         __syncthreads();
         if (tid == tile_n - 1)
@@ -222,39 +213,62 @@ void decode_balanced_kernel(BalancedParams p)
     const int B = p.num_seqs;
     const bool live = col < d.group;
 
-    const int64_t T = p.inline_schedule ? (int64_t)uniform(wave_total_chunks(d, B, lane)) * K
-                                        : (int64_t)uniform(p.total_chunks[0]);
-    if (T == 0)
-        return;
-    const int c_begin = wave_begin(wv, T, p.log2_waves);
-    const int c_end = wave_begin(wv + 1, T, p.log2_waves);
-    if (c_begin >= c_end)
-        return;
-    int4 st;
+    // Where this wave starts: (sequence, KV head, chunk) and that sequence's
+    // context length.  Small batches: every wave loads all context lengths
+    // at once (one round trip) and scans them; large ones: the schedule
+    // kernel's table.
+    int64_t T;
+    int4 st = make_int4(0, 0, 0, 0);
+    int c_begin, c_end;
     if (p.inline_schedule) {
-        // Find the sequence holding chunk c_begin: the last b whose chunks
-        // start at or before it (empty sequences start where the next one does).
+        constexpr int kTiles = kInlineScheduleSeqs / kWave;
+        int cx[kTiles];
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            const int b = t * kWave + lane;
+            cx[t] = b < B ? seq_ctx(d, b) : 0;
+        }
+        int total_seq = 0;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+            total_seq += wave_sum(chunks_of(cx[t]));
+        T = (int64_t)uniform(total_seq) * K;
+        if (T == 0)
+            return;
+        c_begin = wave_begin(wv, T, p.log2_waves);
+        c_end = wave_begin(wv + 1, T, p.log2_waves);
+        if (c_begin >= c_end)
+            return;
+        // The sequence holding chunk c_begin: the last b whose chunks start at
+        // or before it (empty sequences start where the next one does).
         int carry = 0;
-        st = make_int4(0, 0, 0, 0);
-        for (int base = 0; base < B; base += kWave) {
-            const int b = base + lane;
-            const int nc = b < B ? chunks_of(seq_ctx(d, b)) : 0;
+        bool found = false;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            const int nc = chunks_of(cx[t]);
             const int incl = wave_inclusive_scan(nc, lane);
             const int tile_total = __shfl(incl, kWave - 1);
-            if ((int64_t)(carry + tile_total) * K > c_begin) {
+            if (!found && (int64_t)(carry + tile_total) * K > c_begin) {
                 const int excl = carry + incl - nc;
-                const uint64_t mask =
-                    __builtin_amdgcn_ballot_w64(b < B && (int64_t)excl * K <= c_begin);
+                const uint64_t mask = __builtin_amdgcn_ballot_w64(t * kWave + lane < B &&
+                                                                  (int64_t)excl * K <= c_begin);
                 const int src = 63 - __builtin_clzll(mask);
                 const int ncb = __shfl(nc, src);
                 const int local = c_begin - __shfl(excl, src) * K;
                 const int kvh = local / ncb;
-                st = make_int4(base + src, kvh, local - kvh * ncb, 0);
-                break;
+                st = make_int4(t * kWave + src, kvh, local - kvh * ncb, __shfl(cx[t], src));
+                found = true;
             }
             carry += tile_total;
         }
     } else {
+        T = (int64_t)uniform(p.total_chunks[0]);
+        if (T == 0)
+            return;
+        c_begin = wave_begin(wv, T, p.log2_waves);
+        c_end = wave_begin(wv + 1, T, p.log2_waves);
+        if (c_begin >= c_end)
+            return;
         st = p.wave_start[wv];
     }
     const int total = c_end - c_begin;           // chunks of this wave
@@ -263,7 +277,7 @@ void decode_balanced_kernel(BalancedParams p)
     start.b = uniform(st.x);
     start.kvh = uniform(st.y);
     start.j = uniform(st.z);
-    start.ctx = seq_ctx_uniform(d, start.b);
+    start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
     start.nc = chunks_of(start.ctx);
     if (start.j >= start.nc)          // cannot happen for a consistent schedule
         return;
@@ -294,61 +308,35 @@ void decode_balanced_kernel(BalancedParams p)
     const int64_t tile_elems = (int64_t)kBlockSize * H;
     const int64_t block_elems = (int64_t)K * tile_elems;
 
-    // ---- issue side: its own cursor and a window of block ids ----
-    // Lane i of `ids` holds block 2*wj + i of sequence wb (windows of 32
-    // chunks, aligned); the window after it in issue order is prefetched.
+    // ---- issue side: its own cursor; each chunk's two block ids come from
+    // scalar loads made one chunk ahead ----
     Pos ip = start;
-    int wb = -1, wj = 0, ids = 0;
-    int pb = -1, pj = 0, ids_pre = 0;
-    auto fetch_ids = [&](int b, int j0, int ctx) {
-        const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-        int id = 0;
-        if (lane < min(2 * kWindowChunks, nblk - 2 * j0))
-            id = d.block_tables[(int64_t)b * d.max_blocks + 2 * j0 + lane];
-        return clamp_block(id, d.num_blocks);
+    int id0 = 0, id1 = 0;
+    auto load_ids = [&](const Pos &q) {
+        const int32_t *row = d.block_tables + (int64_t)q.b * d.max_blocks + 2 * q.j;
+        const int nblk = (q.ctx + kBlockSize - 1) / kBlockSize;
+        id0 = clamp_block(scalar_load(row), d.num_blocks);
+        id1 = 2 * q.j + 1 < nblk ? clamp_block(scalar_load(row + 1), d.num_blocks) : id0;
     };
+    load_ids(ip);
     auto issue = [&](BalancedBuf<H> &r, int k) {
-        if (k > 0)
-            next_pos(ip);
-        const int J = ip.j & ~(kWindowChunks - 1);
-        if (ip.b != wb || J != wj) {
-            ids = (ip.b == pb && J == pj) ? ids_pre : fetch_ids(ip.b, J, ip.ctx);
-            wb = ip.b;
-            wj = J;
-            // the window that follows (wb, wj) in issue order
-            int nb = wb, nj = wj + kWindowChunks, nctx = ip.ctx;
-            if (nj >= ip.nc) {
-                nj = 0;
-                if (ip.kvh + 1 >= K) {
-                    const int2 nx = next_seq(wb);
-                    nb = nx.x;
-                    nctx = nx.y;
-                }
-            }
-            pb = -1;
-            if ((nb != wb || nj != wj) && nb < B && nctx > 0) {
-                pb = nb;
-                pj = nj;
-                ids_pre = fetch_ids(nb, nj, nctx);
-            }
-        }
-        const int nblk = (ip.ctx + kBlockSize - 1) / kBlockSize;
-        const int slot = 2 * (ip.j - wj);
-        const int id0 = __builtin_amdgcn_readlane(ids, slot);
-        const int id1 = (2 * ip.j + 1 < nblk) ? __builtin_amdgcn_readlane(ids, slot + 1) : id0;
+        // ip is chunk k; (id0, id1) are its blocks
         const uint16_t *kb = d.key_cache + ip.kvh * tile_elems;
         const uint16_t *vb = d.value_cache + ip.kvh * tile_elems;
         load_chunk<H>(r.kv, kb + id0 * block_elems, kb + id1 * block_elems,
                       vb + id0 * block_elems, vb + id1 * block_elems, col, quad);
         if (k == 0 || ip.j == 0) {    // the chunk opens a segment: bring its queries
-            const int n = ip.kvh * d.group + (live ? col : 0);
+            // Columns past the group repeat its last query; their results are
+            // never stored.
+            const int n = ip.kvh * d.group + min(col, d.group - 1);
             const uint16_t *qrow = d.q + ((int64_t)ip.b * d.num_heads + n) * H;
 #pragma unroll
-            for (int s = 0; s < H / 32; ++s) {
+            for (int s = 0; s < H / 32; ++s)
                 r.q[s] = load16(qrow + 32 * s + 8 * quad);
-                if (!live)
-                    r.q[s] = u32x4{0u, 0u, 0u, 0u};
-            }
+        }
+        if (k + 1 < total) {          // step to chunk k + 1 and fetch its block ids
+            next_pos(ip);
+            load_ids(ip);
         }
     };
 
@@ -380,8 +368,7 @@ void decode_balanced_kernel(BalancedParams p)
         if (!seg_end && k + 1 < total)
             return;
         // The piece ends here (segment end, or the wave's last chunk).
-        float lt = l + __shfl_xor(l, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = sum_over_rows(l);
         const int n = ap.kvh * d.group + col;
         if (live) {
             if (piece_from_start && seg_end) {          // the whole segment: final output
@@ -410,51 +397,66 @@ void decode_balanced_kernel(BalancedParams p)
         piece_from_start = true;                    // the next piece opens a segment
     };
 
-    BalancedBuf<H> ring[kRing];
-    run_ring(total, ring, issue, attend);
+    BalancedBuf<H> ring[kBalancedRing];
+    run_ring<kBalancedRing>(total, ring, issue, attend);
 }
 
 // ------------------------------------------------------------------- merge --
 
-// One wave per (sequence, query head): combines the pieces of its segment,
-// or writes zeros for an empty sequence.  Segments held whole by one wave
+// One workgroup per segment (sequence, KV head), one wave per query head of
+// its group: combines the pieces of the segment, or writes zeros for an
+// empty sequence.  Segments held whole by one wave
 // were written by that wave and are skipped.  Waves between the segment's
 // first and last may own no chunk at all (when the batch has fewer chunks
-// than waves); they wrote no piece.  The pieces' weights 2^(m - M) go
-// through LDS; the o vectors are then summed with one load per piece and lane.
+// than waves); they wrote no piece.  Loads are issued in groups before any
+// of their results is used, so the kernel is a few memory round trips long.
 template <int H>
-__global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
+__global__ __launch_bounds__(kWave * PKV_MAX_GROUP) void merge_pieces_kernel(BalancedParams p)
 {
+    constexpr int kTiles = kInlineScheduleSeqs / kWave;
+    constexpr int kGroup = 4;      // o vectors loaded before they are summed
     const DecodeParams &d = p.d;
-    const int n = blockIdx.x;
+    const int kvh = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x % kWave;
+    const int g = threadIdx.x / kWave;
+    const int n = kvh * d.group + g;
     const int K = d.num_kv_heads;
-    const int kvh = n / d.group;
-    const int g = n % d.group;
-    const int nc = chunks_of(seq_ctx(d, b));
+    const int B = p.num_seqs;
+    const int lg = p.log2_waves;
+
+    int nc;
+    int64_t T, seq_first;                 // total chunks, chunk_start[b]
+    if (p.inline_schedule) {
+        int c[kTiles];
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            const int bb = t * kWave + lane;
+            c[t] = bb < B ? chunks_of(seq_ctx(d, bb)) : 0;
+        }
+        int total = 0, before = 0;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+            total += wave_sum(c[t]);
+            before += wave_sum(t * kWave + lane < b ? c[t] : 0);
+        }
+        int mine = 0;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+            mine = (t == b / kWave) ? __shfl(c[t], b % kWave) : mine;
+        nc = mine;
+        T = (int64_t)total * K;
+        seq_first = before;
+    } else {
+        nc = chunks_of(seq_ctx(d, b));
+        T = p.total_chunks[0];
+        seq_first = p.chunk_start[b];
+    }
     float *o = d.out + ((int64_t)b * d.num_heads + n) * H;
     if (nc == 0) {
         for (int h = lane; h < H; h += kWave)
             o[h] = 0.f;
         return;
-    }
-    const int lg = p.log2_waves;
-    int64_t T;
-    int64_t seq_first;                    // chunk_start[b]
-    if (p.inline_schedule) {
-        int carry = 0, before = 0;
-        for (int base = 0; base < p.num_seqs; base += kWave) {
-            const int bb = base + lane;
-            const int c = bb < p.num_seqs ? chunks_of(seq_ctx(d, bb)) : 0;
-            carry += wave_sum(c);
-            before += wave_sum(bb < b ? c : 0);
-        }
-        T = (int64_t)carry * K;
-        seq_first = before;
-    } else {
-        T = p.total_chunks[0];
-        seq_first = p.chunk_start[b];
     }
     const int64_t first = seq_first * K + (int64_t)kvh * nc;
     const int w_first = wave_of(first, T, lg);
@@ -464,8 +466,47 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     const int64_t seg = (int64_t)b * K + kvh;
     const int count = w_last - w_first + 1;
     auto empty = [&](int w) { return wave_begin(w, T, lg) == wave_begin(w + 1, T, lg); };
-    auto slot_of = [&](int w) { return ((int64_t)w + seg) * d.group + g; };
+    auto slot_of = [&](int w) { return ((int64_t)min(w, w_last) + seg) * d.group + g; };
 
+    if (count <= kGroup) {
+        // Common case (a segment over at most four waves): every load in one
+        // round trip, then the log-sum-exp combination in registers.
+        float mv[kGroup], lv[kGroup], ov[kGroup][H / kWave];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const int64_t slot = slot_of(w_first + u);
+            mv[u] = p.piece_ml[2 * slot];
+            lv[u] = p.piece_ml[2 * slot + 1];
+#pragma unroll
+            for (int k = 0; k < H / kWave; ++k)
+                ov[u][k] = p.piece_o[slot * H + lane + kWave * k];
+        }
+        bool use[kGroup];
+        float big = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            use[u] = u < count && !empty(w_first + u);
+            big = use[u] ? fmaxf(big, mv[u]) : big;
+        }
+        float den = 0.f, num[H / kWave];
+#pragma unroll
+        for (int k = 0; k < H / kWave; ++k)
+            num[k] = 0.f;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+            const float wt = use[u] ? __builtin_amdgcn_exp2f(mv[u] - big) : 0.f;
+            den += use[u] ? wt * lv[u] : 0.f;
+#pragma unroll
+            for (int k = 0; k < H / kWave; ++k)
+                num[k] += use[u] ? wt * ov[u][k] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < H / kWave; ++k)
+            o[lane + kWave * k] = num[k] / den;
+        return;
+    }
+
+    // Piece i of the segment sits with lane i % 64; maxima first.
     float big = -INFINITY;
     for (int i = lane; i < count; i += kWave)
         if (!empty(w_first + i))
@@ -474,7 +515,6 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     for (int off = 32; off >= 1; off >>= 1)
         big = fmaxf(big, __shfl_xor(big, off));
 
-    // Pieces in tiles of 64: lane i holds the weight 2^(m - M) of piece i.
     float den = 0.f;
     float num[H / kWave];
 #pragma unroll
@@ -489,14 +529,23 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
             den += wt * p.piece_ml[2 * slot + 1];
         }
         const int n_tile = min(kWave, count - base);
-        for (int t = 0; t < n_tile; ++t) {
-            const float wt_t = __shfl(wt, t);
-            if (wt_t == 0.f)
-                continue;   // empty wave (or a piece that underflows to 0)
-            const float *po = p.piece_o + slot_of(w_first + base + t) * H;
+        for (int t = 0; t < n_tile; t += kGroup) {
+            float v[kGroup][H / kWave];
 #pragma unroll
-            for (int k = 0; k < H / kWave; ++k)
-                num[k] += wt_t * po[lane + kWave * k];
+            for (int u = 0; u < kGroup; ++u) {     // in-bounds even past the segment's end
+                const float *po = p.piece_o + slot_of(w_first + base + t + u) * H;
+#pragma unroll
+                for (int k = 0; k < H / kWave; ++k)
+                    v[u][k] = po[lane + kWave * k];
+            }
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const float wt_u = __shfl(wt, min(t + u, kWave - 1));
+                const bool use = t + u < n_tile && wt_u != 0.f;   // 0: empty wave or underflow
+#pragma unroll
+                for (int k = 0; k < H / kWave; ++k)
+                    num[k] += use ? wt_u * v[u][k] : 0.f;
+            }
         }
     }
 #pragma unroll

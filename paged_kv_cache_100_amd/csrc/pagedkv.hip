@@ -267,8 +267,8 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
             return rc;
         const void *mk = head_dim == 128 ? (const void *)pkv::merge_pieces_kernel<128>
                                          : (const void *)pkv::merge_pieces_kernel<64>;
-        return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kWave), &bp,
-                      stream);
+        return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)num_seqs),
+                      dim3(pkv::kWave * (num_heads / num_kv_heads)), &bp, stream);
     }
 
     // Fixed partitions of partition_size tokens, one wave each.
