@@ -403,24 +403,28 @@ void decode_balanced_kernel(BalancedParams p)
 
 // ------------------------------------------------------------------- merge --
 
-// One workgroup per segment (sequence, KV head), one wave per query head of
-// its group: combines the pieces of the segment, or writes zeros for an
-// empty sequence.  Segments held whole by one wave
-// were written by that wave and are skipped.  Waves between the segment's
-// first and last may own no chunk at all (when the batch has fewer chunks
-// than waves); they wrote no piece.  Loads are issued in groups before any
-// of their results is used, so the kernel is a few memory round trips long.
-template <int H>
-__global__ __launch_bounds__(kWave * PKV_MAX_GROUP) void merge_pieces_kernel(BalancedParams p)
+// One wave per segment (sequence, KV head): combines the pieces of the
+// segment for all G query heads of its group, or writes zeros for an empty
+// sequence.  Segments held whole by one wave were written by that wave and
+// are skipped.  Waves between the segment's first and last may own no chunk
+// at all (when the batch has fewer chunks than waves); they wrote no piece.
+// Lane layout: heads padded to Gp (a power of two >= G), 64/Gp lanes per
+// head, each lane VPL = H*Gp/64 consecutive values of its head's row; a
+// piece's G rows are contiguous, so each piece is one coalesced read.
+template <int H, int Gp>
+__global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 {
+    constexpr int kLanesPerHead = kWave / Gp;
+    constexpr int kVals = H / kLanesPerHead;      // values per lane (multiple of 4)
     constexpr int kTiles = kInlineScheduleSeqs / kWave;
-    constexpr int kGroup = 4;      // o vectors loaded before they are summed
+    constexpr int kFast = 4;                      // pieces combined in one round trip
     const DecodeParams &d = p.d;
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
-    const int lane = threadIdx.x % kWave;
-    const int g = threadIdx.x / kWave;
-    const int n = kvh * d.group + g;
+    const int lane = threadIdx.x;
+    const int g = lane / kLanesPerHead;
+    const int h0 = (lane % kLanesPerHead) * kVals;
+    const bool live = g < d.group;
     const int K = d.num_kv_heads;
     const int B = p.num_seqs;
     const int lg = p.log2_waves;
@@ -434,28 +438,27 @@ __global__ __launch_bounds__(kWave * PKV_MAX_GROUP) void merge_pieces_kernel(Bal
             const int bb = t * kWave + lane;
             c[t] = bb < B ? chunks_of(seq_ctx(d, bb)) : 0;
         }
-        int total = 0, before = 0;
+        int total = 0, before = 0, mine = 0;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             total += wave_sum(c[t]);
             before += wave_sum(t * kWave + lane < b ? c[t] : 0);
-        }
-        int mine = 0;
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t)
             mine = (t == b / kWave) ? __shfl(c[t], b % kWave) : mine;
+        }
         nc = mine;
         T = (int64_t)total * K;
         seq_first = before;
     } else {
-        nc = chunks_of(seq_ctx(d, b));
-        T = p.total_chunks[0];
-        seq_first = p.chunk_start[b];
+        nc = chunks_of(seq_ctx_uniform(d, b));
+        T = scalar_load(p.total_chunks);
+        seq_first = scalar_load(p.chunk_start + b);
     }
-    float *o = d.out + ((int64_t)b * d.num_heads + n) * H;
+    float *o = d.out + ((int64_t)b * d.num_heads + kvh * d.group + g) * H + h0;
     if (nc == 0) {
-        for (int h = lane; h < H; h += kWave)
-            o[h] = 0.f;
+        if (live)
+#pragma unroll
+            for (int v = 0; v < kVals; v += 4)
+                *reinterpret_cast<f32x4 *>(o + v) = f32x4{0.f, 0.f, 0.f, 0.f};
         return;
     }
     const int64_t first = seq_first * K + (int64_t)kvh * nc;
@@ -465,95 +468,65 @@ __global__ __launch_bounds__(kWave * PKV_MAX_GROUP) void merge_pieces_kernel(Bal
         return;
     const int64_t seg = (int64_t)b * K + kvh;
     const int count = w_last - w_first + 1;
+    const int gg = live ? g : 0;
     auto empty = [&](int w) { return wave_begin(w, T, lg) == wave_begin(w + 1, T, lg); };
-    auto slot_of = [&](int w) { return ((int64_t)min(w, w_last) + seg) * d.group + g; };
+    // piece (w, seg): rows (w + seg) * G + g' for the group's heads g'
+    auto row_of = [&](int w) { return ((int64_t)min(w, w_last) + seg) * d.group + gg; };
 
-    if (count <= kGroup) {
+    float big = -INFINITY, den = 0.f;
+    f32x4 num[kVals / 4];
+#pragma unroll
+    for (int v = 0; v < kVals / 4; ++v)
+        num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (count <= kFast) {
         // Common case (a segment over at most four waves): every load in one
         // round trip, then the log-sum-exp combination in registers.
-        float mv[kGroup], lv[kGroup], ov[kGroup][H / kWave];
+        float mv[kFast], lv[kFast];
+        f32x4 ov[kFast][kVals / 4];
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
-            const int64_t slot = slot_of(w_first + u);
-            mv[u] = p.piece_ml[2 * slot];
-            lv[u] = p.piece_ml[2 * slot + 1];
+        for (int u = 0; u < kFast; ++u) {
+            const int64_t r = row_of(w_first + u);
+            mv[u] = p.piece_ml[2 * r];
+            lv[u] = p.piece_ml[2 * r + 1];
 #pragma unroll
-            for (int k = 0; k < H / kWave; ++k)
-                ov[u][k] = p.piece_o[slot * H + lane + kWave * k];
+            for (int v = 0; v < kVals / 4; ++v)
+                ov[u][v] = *reinterpret_cast<const f32x4 *>(p.piece_o + r * H + h0 + 4 * v);
         }
-        bool use[kGroup];
-        float big = -INFINITY;
+        bool use[kFast];
 #pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
+        for (int u = 0; u < kFast; ++u) {
             use[u] = u < count && !empty(w_first + u);
             big = use[u] ? fmaxf(big, mv[u]) : big;
         }
-        float den = 0.f, num[H / kWave];
 #pragma unroll
-        for (int k = 0; k < H / kWave; ++k)
-            num[k] = 0.f;
-#pragma unroll
-        for (int u = 0; u < kGroup; ++u) {
+        for (int u = 0; u < kFast; ++u) {
             const float wt = use[u] ? __builtin_amdgcn_exp2f(mv[u] - big) : 0.f;
             den += use[u] ? wt * lv[u] : 0.f;
 #pragma unroll
-            for (int k = 0; k < H / kWave; ++k)
-                num[k] += use[u] ? wt * ov[u][k] : 0.f;
+            for (int v = 0; v < kVals / 4; ++v)
+                num[v] += use[u] ? wt * ov[u][v] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    } else {
+        for (int i = 0; i < count; ++i)
+            if (!empty(w_first + i))
+                big = fmaxf(big, p.piece_ml[2 * row_of(w_first + i)]);
+        for (int i = 0; i < count; ++i) {
+            if (empty(w_first + i))
+                continue;
+            const int64_t r = row_of(w_first + i);
+            const float wt = __builtin_amdgcn_exp2f(p.piece_ml[2 * r] - big);
+            den += wt * p.piece_ml[2 * r + 1];
 #pragma unroll
-        for (int k = 0; k < H / kWave; ++k)
-            o[lane + kWave * k] = num[k] / den;
-        return;
-    }
-
-    // Piece i of the segment sits with lane i % 64; maxima first.
-    float big = -INFINITY;
-    for (int i = lane; i < count; i += kWave)
-        if (!empty(w_first + i))
-            big = fmaxf(big, p.piece_ml[2 * slot_of(w_first + i)]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        big = fmaxf(big, __shfl_xor(big, off));
-
-    float den = 0.f;
-    float num[H / kWave];
-#pragma unroll
-    for (int k = 0; k < H / kWave; ++k)
-        num[k] = 0.f;
-    for (int base = 0; base < count; base += kWave) {
-        float wt = 0.f;
-        const int i = base + lane;
-        if (i < count && !empty(w_first + i)) {
-            const int64_t slot = slot_of(w_first + i);
-            wt = __builtin_amdgcn_exp2f(p.piece_ml[2 * slot] - big);
-            den += wt * p.piece_ml[2 * slot + 1];
-        }
-        const int n_tile = min(kWave, count - base);
-        for (int t = 0; t < n_tile; t += kGroup) {
-            float v[kGroup][H / kWave];
-#pragma unroll
-            for (int u = 0; u < kGroup; ++u) {     // in-bounds even past the segment's end
-                const float *po = p.piece_o + slot_of(w_first + base + t + u) * H;
-#pragma unroll
-                for (int k = 0; k < H / kWave; ++k)
-                    v[u][k] = po[lane + kWave * k];
-            }
-#pragma unroll
-            for (int u = 0; u < kGroup; ++u) {
-                const float wt_u = __shfl(wt, min(t + u, kWave - 1));
-                const bool use = t + u < n_tile && wt_u != 0.f;   // 0: empty wave or underflow
-#pragma unroll
-                for (int k = 0; k < H / kWave; ++k)
-                    num[k] += use ? wt_u * v[u][k] : 0.f;
-            }
+            for (int v = 0; v < kVals / 4; ++v)
+                num[v] += wt * *reinterpret_cast<const f32x4 *>(p.piece_o + r * H + h0 + 4 * v);
         }
     }
+    if (live) {
+        const float inv = 1.0f / den;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        den += __shfl_xor(den, off);
-#pragma unroll
-    for (int k = 0; k < H / kWave; ++k)
-        o[lane + kWave * k] = num[k] / den;
+        for (int v = 0; v < kVals / 4; ++v)
+            *reinterpret_cast<f32x4 *>(o + 4 * v) = num[v] * inv;
+    }
 }
 
 }  // namespace pkv

@@ -92,6 +92,27 @@ int device_waves(int *log2_waves)
     return PKV_OK;
 }
 
+// Merge kernel of the balanced schedule for a head dim and group size: the
+// group is padded to a power of two, and to at least 256/H so that every
+// lane owns a whole 16-byte slice of a row.
+template <int H>
+const void *merge_pieces_h(int group)
+{
+    constexpr int kMin = 256 / H;
+    const int gp = group <= kMin ? kMin : group <= 4 ? 4 : group <= 8 ? 8 : 16;
+    switch (gp) {
+    case 2: return (const void *)pkv::merge_pieces_kernel<H, (kMin > 2 ? kMin : 2)>;
+    case 4: return (const void *)pkv::merge_pieces_kernel<H, 4>;
+    case 8: return (const void *)pkv::merge_pieces_kernel<H, 8>;
+    default: return (const void *)pkv::merge_pieces_kernel<H, 16>;
+    }
+}
+
+const void *merge_pieces_for(int head_dim, int group)
+{
+    return head_dim == 128 ? merge_pieces_h<128>(group) : merge_pieces_h<64>(group);
+}
+
 int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream)
 {
     void *args[] = {params};
@@ -265,10 +286,9 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
         rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
         if (rc != PKV_OK)
             return rc;
-        const void *mk = head_dim == 128 ? (const void *)pkv::merge_pieces_kernel<128>
-                                         : (const void *)pkv::merge_pieces_kernel<64>;
-        return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)num_seqs),
-                      dim3(pkv::kWave * (num_heads / num_kv_heads)), &bp, stream);
+        const void *mk = merge_pieces_for(head_dim, num_heads / num_kv_heads);
+        return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)num_seqs), dim3(pkv::kWave), &bp,
+                      stream);
     }
 
     // Fixed partitions of partition_size tokens, one wave each.
