@@ -62,6 +62,18 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_decode_split.restype = i32
     lib.oracle_kv_cache_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.oracle_kv_cache_bytes.restype = i64
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_quantize.argtypes = [ctypes.c_uint16, f32]
+    lib.oracle_e4m3_quantize.restype = ctypes.c_uint8
+    lib.oracle_append_fp8.argtypes = [P, P, P, P, P, f32, f32, i32, i32, i32, i32, i64]
+    lib.oracle_append_fp8.restype = i32
+    lib.oracle_decode_fp8.argtypes = [P, P, P, P, f32, f32, P, P, f32,
+                                      i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_fp8.restype = i32
+    lib.oracle_decode_rows_fp8.argtypes = [P, P, P, i32, P, P, P, f32, f32, P, P, f32,
+                                           i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_rows_fp8.restype = i32
     return lib
 
 
@@ -120,10 +132,10 @@ def append(k, v, slot_mapping, key_cache, value_cache, lib=None) -> None:
         raise ValueError("slot outside the pool")
 
 
-def _decode_args(q, key_cache, value_cache, block_tables, context_lens):
+def _decode_args(q, key_cache, value_cache, block_tables, context_lens, cache_dtype=np.uint16):
     q = _as(q, np.uint16)
-    key_cache = _as(key_cache, np.uint16)
-    value_cache = _as(value_cache, np.uint16)
+    key_cache = _as(key_cache, cache_dtype)
+    value_cache = _as(value_cache, cache_dtype)
     block_tables = _as(block_tables, np.int32)
     context_lens = _as(context_lens, np.int32)
     B, N, H = q.shape
@@ -200,3 +212,76 @@ def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int,
     """2 * L * K * H * S * bytes (KV-cache size formula), computed by the C oracle."""
     return int((lib or _load()).oracle_kv_cache_bytes(layers, kv_heads, head_dim, tokens,
                                                       bytes_per_value))
+
+
+# ---------------------------------------------------------------- FP8 ----
+# OCP FP8 E4M3 pools: uint8 codes; a code c stands for e4m3_value(c) * scale.
+
+def fp32_inverse(scale: float) -> float:
+    """1/scale rounded to fp32 (the inverse the append multiplies by)."""
+    return float(np.float32(1.0) / np.float32(scale))
+
+
+def e4m3_value(code: int, lib=None) -> float:
+    """Exact value of an E4M3 code (NaN for 0x7F / 0xFF)."""
+    return float((lib or _load()).oracle_e4m3_value(int(code) & 0xFF))
+
+
+def e4m3_quantize(bits: int, inv_scale: float, lib=None) -> int:
+    """Code stored for the bf16 value with these bits, given the fp32 inverse scale."""
+    return int((lib or _load()).oracle_e4m3_quantize(int(bits) & 0xFFFF, float(inv_scale)))
+
+
+def append_fp8(k, v, slot_mapping, key_cache, value_cache, k_scale, v_scale, lib=None) -> None:
+    """Quantise new K/V rows (bf16 bits) into FP8 pools (uint8 codes), in place."""
+    k = _as(k, np.uint16)
+    v = _as(v, np.uint16)
+    slot_mapping = _as(slot_mapping, np.int64)
+    if not (key_cache.flags.c_contiguous and value_cache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous (written in place)")
+    if key_cache.dtype != np.uint8 or value_cache.dtype != np.uint8:
+        raise TypeError("FP8 caches must be uint8 codes")
+    T, K, H = k.shape
+    nb, K2, bs, H2 = key_cache.shape
+    if (K2, H2) != (K, H) or value_cache.shape != (nb, K, H, bs) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    rc = (lib or _load()).oracle_append_fp8(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(key_cache), _ptr(value_cache),
+        fp32_inverse(k_scale), fp32_inverse(v_scale), T, K, H, bs, nb)
+    if rc:
+        raise ValueError("slot outside the pool")
+
+
+def decode_fp8(q, key_cache, value_cache, block_tables, context_lens, scale, k_scale, v_scale,
+               lib=None) -> np.ndarray:
+    """``decode`` over FP8 pools, float64 [B, N, H]."""
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, key_cache, value_cache, block_tables, context_lens, np.uint8)
+    out = np.zeros((B, N, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_fp8(
+        _ptr(out), _ptr(q), _ptr(kc), _ptr(vc), float(np.float32(k_scale)),
+        float(np.float32(v_scale)), _ptr(bt), _ptr(cl), float(np.float32(scale)),
+        B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (block id, shape or context)")
+    return out
+
+
+def decode_rows_fp8(rows_b, rows_n, q, key_cache, value_cache, block_tables, context_lens,
+                    scale, k_scale, v_scale, lib=None) -> np.ndarray:
+    """Rows (rows_b[r], rows_n[r]) of ``decode_fp8`` only, float64 [R, H]."""
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, key_cache, value_cache, block_tables, context_lens, np.uint8)
+    rb = _as(rows_b, np.int32)
+    rn = _as(rows_n, np.int32)
+    R = rb.shape[0]
+    out = np.zeros((R, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_rows_fp8(
+        _ptr(out), _ptr(rb), _ptr(rn), R, _ptr(q), _ptr(kc), _ptr(vc),
+        float(np.float32(k_scale)), float(np.float32(v_scale)), _ptr(bt), _ptr(cl),
+        float(np.float32(scale)), B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (row, block id, shape or context)")
+    return out

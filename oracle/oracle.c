@@ -31,6 +31,15 @@
  *   block_tables[B][max_blocks_per_seq] int32, context_lens[B] int32
  *   slot = physical_block * block_size + offset_in_block (int64)
  *
+ * FP8 caches ("Week 11. Inference", step 2, names quantising the cache to 8
+ * bits as a way to halve it): the same layouts holding one-byte OCP FP8 E4M3
+ * codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN) with one scale per pool: a stored code c
+ * stands for decode(c) * scale.  Appending value x stores the code nearest to
+ * x * inv_scale (inv_scale = 1/scale rounded to fp32; product in fp32), after
+ * clamping that product to +-448, the largest finite code; ties go to the
+ * even code; NaN stores 0xFF.
+ *
  * Return codes: 0 on success, -1 on an argument that makes the definition
  * meaningless (a block id or slot outside the pool, N not divisible by K,
  * a context longer than the block table).
@@ -57,6 +66,64 @@ static double bf16_to_double(uint16_t bits)
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* Value of an OCP FP8 E4M3 code, exactly. */
+double oracle_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);             /* subnormal: m/8 * 2^-6 */
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* Code nearest to y (ties to the even code), y finite with |y| <= 448:
+ * the 127 non-negative finite codes are in increasing order of value. */
+static uint8_t e4m3_nearest(float y)
+{
+    double a = fabs((double)y);
+    int lo = 0;
+    while (lo < 126 && oracle_e4m3_value((uint8_t)(lo + 1)) <= a)
+        lo++;
+    int code = lo;
+    if (lo < 126) {
+        double d_lo = a - oracle_e4m3_value((uint8_t)lo);
+        double d_hi = oracle_e4m3_value((uint8_t)(lo + 1)) - a;
+        if (d_hi < d_lo || (d_hi == d_lo && ((lo + 1) & 1) == 0))
+            code = lo + 1;
+    }
+    return (uint8_t)(code | (signbit(y) ? 0x80 : 0));
+}
+
+/* Quantisation of one bf16 value for an FP8 pool with inverse scale inv. */
+uint8_t oracle_e4m3_quantize(uint16_t bits, float inv)
+{
+    uint32_t u = ((uint32_t)bits) << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    float y = x * inv;                          /* one fp32 rounding */
+    if (isnan(y))
+        return 0xFF;
+    if (y > 448.0f)
+        y = 448.0f;
+    if (y < -448.0f)
+        y = -448.0f;
+    return e4m3_nearest(y);
+}
+
+/* A cache element as a double: bf16 bits, or an FP8 code times its scale. */
+enum { KV_BF16 = 0, KV_FP8 = 1 };
+
+static double cache_value(const void *pool, size_t index, int dtype, double scale)
+{
+    if (dtype == KV_BF16)
+        return bf16_to_double(((const uint16_t *)pool)[index]);
+    return oracle_e4m3_value(((const uint8_t *)pool)[index]) * scale;
 }
 
 /* Address of key element (block p, kv head g, offset o, dim h). */
@@ -99,14 +166,42 @@ int oracle_append(const uint16_t *k, const uint16_t *v, const int64_t *slot_mapp
 }
 
 /*
+ * Append into FP8 pools: the same scatter, storing each value's quantised code
+ * (see the header comment).  k_inv / v_inv are the fp32 inverse scales.
+ */
+int oracle_append_fp8(const uint16_t *k, const uint16_t *v, const int64_t *slot_mapping,
+                      uint8_t *key_cache, uint8_t *value_cache, float k_inv, float v_inv,
+                      int T, int K, int H, int bs, int64_t num_blocks)
+{
+    for (int i = 0; i < T; i++) {
+        int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        if (s >= num_blocks * (int64_t)bs)
+            return -1;
+        int64_t p = s / bs;
+        int o = (int)(s % bs);
+        for (int g = 0; g < K; g++)
+            for (int h = 0; h < H; h++) {
+                size_t src = ((size_t)i * K + g) * H + h;
+                key_cache[key_index(p, g, o, h, K, bs, H)] = oracle_e4m3_quantize(k[src], k_inv);
+                value_cache[value_index(p, g, h, o, K, bs, H)] =
+                    oracle_e4m3_quantize(v[src], v_inv);
+            }
+    }
+    return 0;
+}
+
+/*
  * One output row (sequence b, query head n): the definition of
  * softmax(q K^T * scale) V over the sequence's ctx positions, gathering each
  * position t through the block table.  `scores` is caller scratch of length
  * ctx.  Writes H doubles to `row`.
  */
 static int decode_row(double *row, double *scores,
-                      const uint16_t *q, const uint16_t *key_cache,
-                      const uint16_t *value_cache, const int32_t *block_tables,
+                      const uint16_t *q, const void *key_cache,
+                      const void *value_cache, int dtype, double k_scale, double v_scale,
+                      const int32_t *block_tables,
                       int ctx, int b, int n, float scale,
                       int N, int K, int H, int bs, int max_blocks, int64_t num_blocks)
 {
@@ -130,7 +225,7 @@ static int decode_row(double *row, double *scores,
         double dot = 0.0;
         for (int h = 0; h < H; h++)
             dot += bf16_to_double(qrow[h]) *
-                   bf16_to_double(key_cache[key_index(p, g, o, h, K, bs, H)]);
+                   cache_value(key_cache, key_index(p, g, o, h, K, bs, H), dtype, k_scale);
         scores[t] = sc * dot;
         if (scores[t] > m)
             m = scores[t];
@@ -145,7 +240,7 @@ static int decode_row(double *row, double *scores,
         int o = t % bs;
         for (int h = 0; h < H; h++)
             row[h] += scores[t] *
-                      bf16_to_double(value_cache[value_index(p, g, h, o, K, bs, H)]);
+                      cache_value(value_cache, value_index(p, g, h, o, K, bs, H), dtype, v_scale);
     }
     for (int h = 0; h < H; h++)
         row[h] /= z;
@@ -168,11 +263,11 @@ static int check_shape(const int32_t *context_lens, int B, int N, int K, int bs,
  * `scratch` must hold max(context_lens) doubles per OpenMP thread; the
  * Python wrapper allocates it.
  */
-int oracle_decode(double *out, const uint16_t *q, const uint16_t *key_cache,
-                  const uint16_t *value_cache, const int32_t *block_tables,
-                  const int32_t *context_lens, float scale,
-                  int B, int N, int K, int H, int bs, int max_blocks,
-                  int64_t num_blocks, double *scratch, int scratch_stride)
+static int decode_all(double *out, const uint16_t *q, const void *key_cache,
+                      const void *value_cache, int dtype, double k_scale, double v_scale,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      int B, int N, int K, int H, int bs, int max_blocks,
+                      int64_t num_blocks, double *scratch, int scratch_stride)
 {
     if (check_shape(context_lens, B, N, K, bs, max_blocks))
         return -1;
@@ -186,8 +281,9 @@ int oracle_decode(double *out, const uint16_t *q, const uint16_t *key_cache,
             continue;
         }
         status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
-                             q, key_cache, value_cache, block_tables, context_lens[b],
-                             b, n, scale, N, K, H, bs, max_blocks, num_blocks) != 0;
+                             q, key_cache, value_cache, dtype, k_scale, v_scale, block_tables,
+                             context_lens[b], b, n, scale, N, K, H, bs, max_blocks,
+                             num_blocks) != 0;
     }
     return status ? -1 : 0;
 }
@@ -196,12 +292,12 @@ int oracle_decode(double *out, const uint16_t *q, const uint16_t *key_cache,
  * The same rows, but only the R (b, n) pairs listed: lets a test check
  * sampled outputs of a workload too large to recompute whole.
  */
-int oracle_decode_rows(double *out_rows, const int32_t *rows_b, const int32_t *rows_n, int R,
-                       const uint16_t *q, const uint16_t *key_cache,
-                       const uint16_t *value_cache, const int32_t *block_tables,
-                       const int32_t *context_lens, float scale,
-                       int B, int N, int K, int H, int bs, int max_blocks,
-                       int64_t num_blocks, double *scratch, int scratch_stride)
+static int decode_rows_all(double *out_rows, const int32_t *rows_b, const int32_t *rows_n,
+                           int R, const uint16_t *q, const void *key_cache,
+                           const void *value_cache, int dtype, double k_scale, double v_scale,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           float scale, int B, int N, int K, int H, int bs, int max_blocks,
+                           int64_t num_blocks, double *scratch, int scratch_stride)
 {
     if (check_shape(context_lens, B, N, K, bs, max_blocks))
         return -1;
@@ -215,10 +311,58 @@ int oracle_decode_rows(double *out_rows, const int32_t *rows_b, const int32_t *r
             continue;
         }
         status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
-                             q, key_cache, value_cache, block_tables, context_lens[b],
-                             b, n, scale, N, K, H, bs, max_blocks, num_blocks) != 0;
+                             q, key_cache, value_cache, dtype, k_scale, v_scale, block_tables,
+                             context_lens[b], b, n, scale, N, K, H, bs, max_blocks,
+                             num_blocks) != 0;
     }
     return status ? -1 : 0;
+}
+
+int oracle_decode(double *out, const uint16_t *q, const uint16_t *key_cache,
+                  const uint16_t *value_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, float scale,
+                  int B, int N, int K, int H, int bs, int max_blocks,
+                  int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    return decode_all(out, q, key_cache, value_cache, KV_BF16, 1.0, 1.0, block_tables,
+                      context_lens, scale, B, N, K, H, bs, max_blocks, num_blocks, scratch,
+                      scratch_stride);
+}
+
+/* FP8 pools: keys and values are their codes times k_scale / v_scale. */
+int oracle_decode_fp8(double *out, const uint16_t *q, const uint8_t *key_cache,
+                      const uint8_t *value_cache, float k_scale, float v_scale,
+                      const int32_t *block_tables, const int32_t *context_lens, float scale,
+                      int B, int N, int K, int H, int bs, int max_blocks,
+                      int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    return decode_all(out, q, key_cache, value_cache, KV_FP8, k_scale, v_scale, block_tables,
+                      context_lens, scale, B, N, K, H, bs, max_blocks, num_blocks, scratch,
+                      scratch_stride);
+}
+
+int oracle_decode_rows(double *out_rows, const int32_t *rows_b, const int32_t *rows_n, int R,
+                       const uint16_t *q, const uint16_t *key_cache,
+                       const uint16_t *value_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale,
+                       int B, int N, int K, int H, int bs, int max_blocks,
+                       int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    return decode_rows_all(out_rows, rows_b, rows_n, R, q, key_cache, value_cache, KV_BF16,
+                           1.0, 1.0, block_tables, context_lens, scale, B, N, K, H, bs,
+                           max_blocks, num_blocks, scratch, scratch_stride);
+}
+
+int oracle_decode_rows_fp8(double *out_rows, const int32_t *rows_b, const int32_t *rows_n,
+                           int R, const uint16_t *q, const uint8_t *key_cache,
+                           const uint8_t *value_cache, float k_scale, float v_scale,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           float scale, int B, int N, int K, int H, int bs, int max_blocks,
+                           int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    return decode_rows_all(out_rows, rows_b, rows_n, R, q, key_cache, value_cache, KV_FP8,
+                           k_scale, v_scale, block_tables, context_lens, scale, B, N, K, H,
+                           bs, max_blocks, num_blocks, scratch, scratch_stride);
 }
 
 /*

@@ -319,6 +319,99 @@ def check_append_then_decode_is_contiguous_update(lib):
         assert_close(got[b], ref[:, 0, :].numpy(), 1e-12, "append then decode")
 
 
+# ------------------------------------------------------------------- FP8 ----
+# OCP FP8 E4M3 pools.  torch's float8_e4m3fn dtype is the library routine the
+# code table and the rounding are checked against.
+
+def _torch_e4m3_values():
+    codes = torch.arange(256, dtype=torch.int16).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).float().double().numpy()
+
+
+def check_e4m3_code_table(lib):
+    ref = _torch_e4m3_values()
+    got = np.array([oracle.e4m3_value(c, lib=lib) for c in range(256)])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), f"E4M3 value of codes {np.nonzero(~same)[0][:5]} differs from torch"
+
+
+def _all_bf16_as_tokens():
+    """Every bf16 bit pattern, as [512, 1, 128] tokens for a vectorised append."""
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(512, 1, 128)
+
+
+def check_e4m3_rounding_vs_torch(lib):
+    k = _all_bf16_as_tokens()
+    with np.errstate(all="ignore"):     # the sweep includes inf and NaN patterns
+        _e4m3_rounding_sweep(k, lib)
+
+
+def _e4m3_rounding_sweep(k, lib):
+    x = bits_to_f64(k).astype(np.float32).reshape(-1)
+    for scale in (1.0, 2.0 ** -5, 0.75, 1.0 / 3.0):
+        kc = np.zeros((512, 1, 1, 128), np.uint8)
+        vc = np.zeros((512, 1, 128, 1), np.uint8)
+        slots = np.arange(512, dtype=np.int64)
+        # block size 1: token i lands in block i
+        oracle.append_fp8(k, k, slots, kc, vc, scale, scale, lib=lib)
+        got = kc.reshape(-1)
+        inv = np.float32(oracle.fp32_inverse(scale))
+        y = torch.from_numpy(x * inv).clamp(-448.0, 448.0)
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        nan = np.isnan(x)
+        bad = np.nonzero((got != ref) & ~nan)[0]
+        assert bad.size == 0, f"scale {scale}: code of {x[bad[:3]]} differs from torch"
+        assert np.all(got[nan] == 0xFF), "NaN must store 0xFF"
+        assert np.array_equal(vc.reshape(-1), got), "V pool quantised differently from K"
+
+
+def check_fp8_decode_is_bf16_decode_of_its_values(lib):
+    """With power-of-two scales every FP8 value times its scale is a bf16 value:
+    decoding the FP8 pools equals decoding bf16 pools holding those values."""
+    c = Case(171, B=3, N=8, K=2, H=16, bs=4, max_ctx=40)
+    rng = np.random.default_rng(9)
+    finite = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    kc8 = rng.choice(finite, size=c.kc.shape).astype(np.uint8)
+    vc8 = rng.choice(finite, size=c.vc.shape).astype(np.uint8)
+    ks, vs = 2.0 ** -4, 2.0 ** 3
+    table = _torch_e4m3_values()
+    kc16 = to_bf16_bits(table[kc8] * ks)
+    vc16 = to_bf16_bits(table[vc8] * vs)
+    assert np.array_equal(bits_to_f64(kc16), table[kc8] * ks)
+    got = oracle.decode_fp8(c.q, kc8, vc8, c.tables, c.ctx, c.scale, ks, vs, lib=lib)
+    ref = oracle.decode(c.q, kc16, vc16, c.tables, c.ctx, c.scale, lib=lib)
+    assert np.array_equal(got, ref), "FP8 decode differs from the bf16 decode of its values"
+    rb = np.array([2, 0, 1], np.int32)
+    rn = np.array([7, 3, 0], np.int32)
+    rows = oracle.decode_rows_fp8(rb, rn, c.q, kc8, vc8, c.tables, c.ctx, c.scale, ks, vs,
+                                  lib=lib)
+    assert np.array_equal(rows, got[rb, rn]), "FP8 row sampling differs from the full decode"
+
+
+def check_append_fp8_scatter(lib):
+    k, v, slots, _, _, _ = _append_case(181)
+    T, K, H = k.shape
+    nb, bs = 9, 4
+    sentinel = np.uint8(0x5A)
+    kc = np.full((nb, K, bs, H), sentinel, np.uint8)
+    vc = np.full((nb, K, H, bs), sentinel, np.uint8)
+    ks, vs = 2.0 ** -5, 0.1
+    oracle.append_fp8(k, v, slots, kc, vc, ks, vs, lib=lib)
+    for i, s_ in enumerate(slots):
+        if s_ < 0:
+            continue
+        p_, o_ = divmod(int(s_), bs)
+        want_k = [oracle.e4m3_quantize(b, oracle.fp32_inverse(ks), lib=lib) for b in k[i].reshape(-1)]
+        want_v = [oracle.e4m3_quantize(b, oracle.fp32_inverse(vs), lib=lib) for b in v[i].reshape(-1)]
+        assert np.array_equal(kc[p_, :, o_, :].reshape(-1), np.array(want_k, np.uint8))
+        assert np.array_equal(vc[p_, :, :, o_].reshape(-1), np.array(want_v, np.uint8))
+    written = {int(x) for x in slots if x >= 0}
+    for blk in range(nb):
+        for o_ in range(bs):
+            if blk * bs + o_ not in written:
+                assert np.all(kc[blk, :, o_, :] == sentinel) and np.all(vc[blk, :, :, o_] == sentinel)
+
+
 # ------------------------------------------------------------ accounting ----
 
 def check_printed_kv_sizes(lib):

@@ -32,6 +32,14 @@ MUTANTS = {
     "merge_unweighted_l": ("L += w * piece_l[j];", "L += piece_l[j];"),
     "merge_no_rescale": ("double w = exp(piece_m[j] - M);", "double w = 1.0;"),
     "kv_formula_no_two": ("return 2 * layers", "return layers"),
+    "e4m3_bias": ("mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    "e4m3_subnormal": ("mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    "e4m3_ties_odd": ("((lo + 1) & 1) == 0", "((lo + 1) & 1) == 1"),
+    "e4m3_nan_not_kept": ("if (isnan(y))\n        return 0xFF;", "if (0)\n        return 0xFF;"),
+    "e4m3_truncate": ("if (d_hi < d_lo ||", "if (0 &&"),
+    "fp8_scale_dropped": ("return oracle_e4m3_value(((const uint8_t *)pool)[index]) * scale;",
+                          "return oracle_e4m3_value(((const uint8_t *)pool)[index]);"),
+    "fp8_append_v_from_k": ("oracle_e4m3_quantize(v[src], v_inv);", "oracle_e4m3_quantize(k[src], v_inv);"),
 }
 
 
