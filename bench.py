@@ -9,8 +9,9 @@ decode and log-sum-exp merge kernels).  Inputs are generated on the CPU from a
 seed, copied to HBM, and stay resident while the K timed steps run.
 
 Prints one JSON line.  ``value`` is the KV-read bandwidth of the whole step:
-the bytes of K and V the method must read (sum of contexts x K x H x 2 bytes x
-2) divided by the measured step time.  ``roofline`` is for the attention call
+the bytes of K and V the method must read (sum of contexts x K x H x 2 pools x
+the element size: 2 bytes for bf16 pools, 1 for the FP8 pools of the ``_fp8``
+workloads) divided by the measured step time.  ``roofline`` is for the attention call
 (its HIP events bracket all of its kernels), against the
 MI355X's 8 TB/s HBM peak.  ``cpu_baseline`` times the CPU oracle on a bounded
 sample of the same workload on this host.
@@ -33,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b_b64_ctx8k"
 KERNEL_SOURCES = ["paged_kv_cache_100_amd/csrc/kernels/decode.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/decode_balanced.hpp",
+                  "paged_kv_cache_100_amd/csrc/kernels/kv_format.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/common.hpp",
                   "paged_kv_cache_100_amd/csrc/pagedkv.hip"]
 
@@ -48,12 +50,13 @@ def kernel_hash() -> str:
 def algorithmic_bytes(w, part: int) -> dict:
     """Bytes the method must move for one step (not what the kernels move)."""
     s = w.spec
+    elem = 1 if w.kv_dtype == "fp8" else 2
     ctx = [int(c) for c in w.context_lens.tolist()]
-    kv = sum(ctx) * s.K * s.H * 2 * 2                  # K and V, bf16
+    kv = sum(ctx) * s.K * s.H * 2 * elem               # K and V pools
     q = s.B * s.N * s.H * 2
     out = s.B * s.N * s.H * 4
     tables = sum(-(-c // s.bs) for c in ctx) * 4 + s.B * 4
-    append = 2 * (s.B * s.K * s.H * 2) * 2              # read k, v; write them into the pools
+    append = 2 * (s.B * s.K * s.H) * (2 + elem)        # read bf16 k, v; write them into the pools
     return {"kv": kv, "q": q, "out": out, "tables": tables, "attention": kv + q + out + tables,
             "append": append}
 
@@ -84,15 +87,27 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     def u16(t):
         return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    q, kc, vc = u16(w.q), u16(w.key_cache), u16(w.value_cache)
+    fp8 = w.kv_dtype == "fp8"
+    pool = (lambda t: t.contiguous().numpy()) if fp8 else u16
+    q, kc, vc = u16(w.q), pool(w.key_cache).copy(), pool(w.value_cache).copy()
     bt, cl = w.block_tables.numpy(), w.context_lens.numpy()
-    kc, vc = kc.copy(), vc.copy()
-    oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
+    if fp8:
+        oracle.append_fp8(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc,
+                          w.k_scale, w.v_scale)
+    else:
+        oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
+
+    def decode(n):
+        if fp8:
+            return oracle.decode_fp8(q[:n], kc, vc, bt[:n], cl[:n], w.scale, w.k_scale,
+                                     w.v_scale)
+        return oracle.decode(q[:n], kc, vc, bt[:n], cl[:n], w.scale)
+
     B = w.spec.B
     n = 1
     while True:                       # smallest prefix that takes >= budget/10
         t0 = time.perf_counter()
-        oracle.decode(q[:n], kc, vc, bt[:n], cl[:n], w.scale)
+        decode(n)
         dt = time.perf_counter() - t0
         if dt >= budget_s / 10 or n == B:
             break
@@ -100,11 +115,11 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     reps, spent = 1, dt
     while spent < budget_s and n == B:
         t0 = time.perf_counter()
-        oracle.decode(q, kc, vc, bt, cl, w.scale)
+        decode(B)
         spent += time.perf_counter() - t0
         reps += 1
     tokens = int(cl[:n].sum()) * reps
-    kv_bytes = tokens * w.spec.K * w.spec.H * 4
+    kv_bytes = tokens * w.spec.K * w.spec.H * 2 * (1 if fp8 else 2)
     what = (f"the full batch of {B} sequences, {reps} times" if n == B
             else f"the first {n} of {B} sequences")
     return {"value": n * reps / spent, "unit": "tokens/s per layer",
@@ -152,13 +167,24 @@ def main() -> int:
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((s.B, s.N, s.H), dtype=torch.float32, device=dev)
 
-    def append():
-        pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+    if w.kv_dtype == "fp8":
+        def append():
+            pkv.paged_kv_append_fp8(g.k_new, g.v_new, g.slot_mapping, g.key_cache,
+                                    g.value_cache, w.k_scale, w.v_scale)
 
-    def attend():
-        pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
-                                   g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
-                                   partition=part, workspace=workspace)
+        def attend():
+            pkv.paged_decode_attention_fp8(out, g.q, g.key_cache, g.value_cache,
+                                           g.block_tables, g.context_lens, w.scale, w.k_scale,
+                                           w.v_scale, s.K, s.bs, max_context_len=mcl,
+                                           partition=part, workspace=workspace)
+    else:
+        def append():
+            pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+
+        def attend():
+            pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                       g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
+                                       partition=part, workspace=workspace)
 
     # Achievable bandwidth: plain 16-byte streaming read of 1 GiB, and a 1 GiB
     # copy (its known read and write sizes also scale the HBM byte counters
@@ -238,9 +264,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) bf16 q/k/v, block tables from a seeded permutation",
-        "config": {"workload": args.workload, "B": s.B, "N": s.N, "K": s.K, "H": s.H,
+        "dtype": "fp8e4m3-kv/bf16" if w.kv_dtype == "fp8" else "bf16",
+        "data": ("synthetic: seeded N(0,1) bf16 q/k/v, block tables from a seeded permutation"
+                 + ("; K/V pools as E4M3 codes with per-pool scales" if w.kv_dtype == "fp8"
+                    else "")),
+        "config": {"workload": args.workload, "kv_dtype": w.kv_dtype,
+                   "B": s.B, "N": s.N, "K": s.K, "H": s.H,
                    "block_size": s.bs, "sum_context": int(w.context_lens.sum()),
                    "max_context": mcl, "partition": part, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

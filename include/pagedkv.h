@@ -168,6 +168,51 @@ int paged_decode_attention(float *out, const void *q,
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * FP8 KV pools.  The same two operations over pools that hold one-byte OCP
+ * FP8 E4M3 codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+ * no infinities; codes 0x7F / 0xFF are NaN) in the same layouts, with one
+ * scale per pool: a stored code c stands for e4m3(c) * k_scale in the key
+ * pool and e4m3(c) * v_scale in the value pool.  Quantising the cache to 8
+ * bits is the lever "Week 11. Inference", step 2, names for halving the
+ * cache, and the lesson's exercises ("Optimización de la inferencia")
+ * ask for the FP8 cache's capacity; the pages fix neither the 8-bit format
+ * nor the rounding, so the library takes E4M3 with round-to-nearest-even and
+ * a per-pool scale.
+ *
+ * paged_kv_append_fp8 -- as paged_kv_append, except that each bf16 value x
+ *   is stored as the code nearest to y = fp32(x * fp32(1 / scale)) (the pool's
+ *   scale), where y is first clamped to [-448, 448] (the largest finite
+ *   code); ties go to the code with an even last bit; NaN stores 0xFF; the
+ *   sign of zero is kept (-0 stores 0x80).
+ *   key_cache      [num_blocks][num_kv_heads][block_size][head_dim] uint8,
+ *   value_cache    [num_blocks][num_kv_heads][head_dim][block_size] uint8.
+ *   k_scale, v_scale   positive, finite, with finite fp32 inverses; else
+ *                  PKV_ERR_SHAPE.  Other checks as for paged_kv_append.
+ *   The codes are bit exact against that definition.
+ *
+ * paged_decode_attention_fp8 -- as paged_decode_attention over FP8 pools
+ *   (same arguments, plus k_scale and v_scale as above; the workspace is
+ *   sized by paged_decode_workspace_size with the same arguments).  Codes are
+ *   widened to bf16 exactly before the matrix-core products; k_scale is
+ *   folded into the softmax scale and v_scale into the output normalisation,
+ *   both in fp32.  q and out are as in paged_decode_attention.
+ */
+int paged_kv_append_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                        void *key_cache, void *value_cache, float k_scale, float v_scale,
+                        int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, void *stream);
+
+int paged_decode_attention_fp8(float *out, const void *q,
+                               const void *key_cache, const void *value_cache,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               float scale, float k_scale, float v_scale,
+                               int32_t num_kv_heads, int32_t block_size,
+                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int64_t num_blocks, int32_t partition_size,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * pagedkv_stream_read -- measurement helper, not part of the method: reads
  * `bytes` (a multiple of 16) from `src` with 16-byte loads and writes one
  * 16-byte value per workgroup into `sink` ([gridDim] x 16 bytes; the size is

@@ -9,11 +9,16 @@ computation runs in the library's HIP kernels.  The library must be built
     paged_kv_append(k, v, slot_mapping, key_cache, value_cache)
     paged_decode_attention(out, q, key_cache, value_cache, block_tables,
                            context_lens, scale, num_kv_heads, block_size)
+    paged_kv_append_fp8(k, v, slot_mapping, key_cache, value_cache, k_scale, v_scale)
+    paged_decode_attention_fp8(out, q, key_cache, value_cache, block_tables,
+                               context_lens, scale, k_scale, v_scale, num_kv_heads,
+                               block_size)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
-[num_blocks, K, 16, H] bf16; value_cache [num_blocks, K, H, 16] bf16;
-q [B, N, H] bf16; out [B, N, H] float32; block_tables [B, max_blocks] int32;
-context_lens [B] int32.
+[num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
+``_fp8`` calls one-byte OCP FP8 E4M3 codes as uint8 or float8_e4m3fn, one
+scale per pool); q [B, N, H] bf16; out [B, N, H] float32; block_tables
+[B, max_blocks] int32; context_lens [B] int32.
 """
 from __future__ import annotations
 
@@ -57,6 +62,11 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_attention.argtypes = [P, P, P, P, P, P, f32, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, P, sz, P]
     L.paged_decode_attention.restype = ctypes.c_int
+    L.paged_kv_append_fp8.argtypes = [P, P, P, P, P, f32, f32, i32, i32, i32, i32, i64, P]
+    L.paged_kv_append_fp8.restype = ctypes.c_int
+    L.paged_decode_attention_fp8.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32,
+                                             i32, i32, i32, i64, i32, P, sz, P]
+    L.paged_decode_attention_fp8.restype = ctypes.c_int
     L.pagedkv_stream_read_sink_bytes.argtypes = [sz]
     L.pagedkv_stream_read_sink_bytes.restype = sz
     L.pagedkv_stream_read.argtypes = [P, sz, P, P]
@@ -80,11 +90,15 @@ def _check(rc: int, what: str) -> None:
         raise PagedKVError(rc, what)
 
 
-def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _dev(t: torch.Tensor, name: str, dtype) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be {' or '.join(map(str, allowed))}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     if not t.is_contiguous():
@@ -96,14 +110,12 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def paged_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
-                    key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
-    """Write k[i], v[i] ([T, K, H] bf16) at slot slot_mapping[i] of the caches."""
+def _append_args(k, v, slot_mapping, key_cache, value_cache, cache_dtype):
     pk = _dev(k, "k", torch.bfloat16)
     pv = _dev(v, "v", torch.bfloat16)
     ps = _dev(slot_mapping, "slot_mapping", torch.int64)
-    pkc = _dev(key_cache, "key_cache", torch.bfloat16)
-    pvc = _dev(value_cache, "value_cache", torch.bfloat16)
+    pkc = _dev(key_cache, "key_cache", cache_dtype)
+    pvc = _dev(value_cache, "value_cache", cache_dtype)
     if k.dim() != 3 or v.shape != k.shape:
         raise ValueError("k and v must both be [T, K, H]")
     T, K, H = k.shape
@@ -114,8 +126,25 @@ def paged_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
         raise ValueError("cache shapes do not match k/v ([nb,K,bs,H] and [nb,K,H,bs])")
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [T]")
-    _check(lib().paged_kv_append(pk, pv, ps, pkc, pvc, T, K, H, bs, nb, _stream(k.device)),
-           "paged_kv_append")
+    return (pk, pv, ps, pkc, pvc), (T, K, H, bs, nb)
+
+
+def paged_kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    key_cache: torch.Tensor, value_cache: torch.Tensor) -> None:
+    """Write k[i], v[i] ([T, K, H] bf16) at slot slot_mapping[i] of the caches."""
+    ptrs, sizes = _append_args(k, v, slot_mapping, key_cache, value_cache, torch.bfloat16)
+    _check(lib().paged_kv_append(*ptrs, *sizes, _stream(k.device)), "paged_kv_append")
+
+
+def paged_kv_append_fp8(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                        key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale: float,
+                        v_scale: float) -> None:
+    """Quantise k[i], v[i] ([T, K, H] bf16) into FP8 E4M3 pools (uint8 or
+    float8_e4m3fn) at slot slot_mapping[i]; code c in a pool stands for
+    e4m3(c) * that pool's scale."""
+    ptrs, sizes = _append_args(k, v, slot_mapping, key_cache, value_cache, FP8_DTYPES)
+    _check(lib().paged_kv_append_fp8(*ptrs, float(k_scale), float(v_scale), *sizes,
+                                     _stream(k.device)), "paged_kv_append_fp8")
 
 
 def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
@@ -124,24 +153,12 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
                                                  max_context_len, partition))
 
 
-def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
-                           value_cache: torch.Tensor, block_tables: torch.Tensor,
-                           context_lens: torch.Tensor, scale: float, num_kv_heads: int,
-                           block_size: int, max_context_len: Optional[int] = None,
-                           partition: int = 0,
-                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out[b, n] = softmax(scale * q[b, n] . K_b^T) V_b over the paged cache.
-
-    ``max_context_len`` is a host-known bound of ``context_lens``; by default
-    the block-table capacity (max_blocks * block_size).  ``partition`` 0 uses
-    the token-balanced schedule, P > 0 fixed P-token partitions.
-    ``workspace`` (uint8, on the GPU) is allocated here when not given and the
-    call needs one.  Returns ``out``.
-    """
+def _decode_args(out, q, key_cache, value_cache, block_tables, context_lens, num_kv_heads,
+                 block_size, max_context_len, partition, workspace, cache_dtype):
     po = _dev(out, "out", torch.float32)
     pq = _dev(q, "q", torch.bfloat16)
-    pkc = _dev(key_cache, "key_cache", torch.bfloat16)
-    pvc = _dev(value_cache, "value_cache", torch.bfloat16)
+    pkc = _dev(key_cache, "key_cache", cache_dtype)
+    pvc = _dev(value_cache, "value_cache", cache_dtype)
     pbt = _dev(block_tables, "block_tables", torch.int32)
     pcl = _dev(context_lens, "context_lens", torch.int32)
     if q.dim() != 3 or out.shape != q.shape:
@@ -164,10 +181,46 @@ def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.
     if workspace is not None:
         pw = _dev(workspace, "workspace", torch.uint8)
         wbytes = workspace.numel()
-    _check(lib().paged_decode_attention(po, pq, pkc, pvc, pbt, pcl, float(scale), K, bs, B, N, H,
-                                        max_blocks, int(max_context_len), nb, int(partition),
-                                        pw, wbytes, _stream(q.device)),
-           "paged_decode_attention")
+    head = (po, pq, pkc, pvc, pbt, pcl)
+    tail = (K, bs, B, N, H, max_blocks, int(max_context_len), nb, int(partition), pw, wbytes,
+            _stream(q.device))
+    return head, tail
+
+
+def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                           value_cache: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                           block_size: int, max_context_len: Optional[int] = None,
+                           partition: int = 0,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[b, n] = softmax(scale * q[b, n] . K_b^T) V_b over the paged cache.
+
+    ``max_context_len`` is a host-known bound of ``context_lens``; by default
+    the block-table capacity (max_blocks * block_size).  ``partition`` 0 uses
+    the token-balanced schedule, P > 0 fixed P-token partitions.
+    ``workspace`` (uint8, on the GPU) is allocated here when not given and the
+    call needs one.  Returns ``out``.
+    """
+    head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
+                              num_kv_heads, block_size, max_context_len, partition, workspace,
+                              torch.bfloat16)
+    _check(lib().paged_decode_attention(*head, float(scale), *tail), "paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                               value_cache: torch.Tensor, block_tables: torch.Tensor,
+                               context_lens: torch.Tensor, scale: float, k_scale: float,
+                               v_scale: float, num_kv_heads: int, block_size: int,
+                               max_context_len: Optional[int] = None, partition: int = 0,
+                               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``paged_decode_attention`` over FP8 E4M3 pools (uint8 or float8_e4m3fn),
+    keys being codes times ``k_scale`` and values codes times ``v_scale``."""
+    head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
+                              num_kv_heads, block_size, max_context_len, partition, workspace,
+                              FP8_DTYPES)
+    _check(lib().paged_decode_attention_fp8(*head, float(scale), float(k_scale), float(v_scale),
+                                            *tail), "paged_decode_attention_fp8")
     return out
 
 

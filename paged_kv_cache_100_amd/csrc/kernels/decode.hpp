@@ -48,7 +48,7 @@
 // addressed (its table entry is not read).
 #pragma once
 
-#include "common.hpp"
+#include "kv_format.hpp"
 
 namespace pkv {
 
@@ -59,11 +59,12 @@ struct DecodeParams {
     float *part_o;                // [B][N][P][H]   (split only)
     float *part_ml;               // [B][N][P][2]   (split only)
     const uint16_t *q;            // [B][N][H] bf16
-    const uint16_t *key_cache;    // [num_blocks][K][16][H]
-    const uint16_t *value_cache;  // [num_blocks][K][H][16]
+    const void *key_cache;        // [num_blocks][K][16][H]  (Fmt::Elem)
+    const void *value_cache;      // [num_blocks][K][H][16]  (Fmt::Elem)
     const int32_t *block_tables;  // [B][max_blocks]
     const int32_t *context_lens;  // [B]
-    float scale_log2;             // scale * log2(e)
+    float scale_log2;             // scale * log2(e) (times k_scale for FP8 pools)
+    float out_scale;              // factor on every written o: 1, or v_scale for FP8 pools
     int32_t num_heads;            // N
     int32_t num_kv_heads;         // K
     int32_t group;                // G = N / K
@@ -74,45 +75,15 @@ struct DecodeParams {
     int64_t num_blocks;
 };
 
-// Per-lane operand registers of one 32-token chunk.
-template <int H>
-struct ChunkRegs {
-    u32x4 k[2][H / 32];   // score tile a, k-step s
-    u32x4 v[H / 16];      // value tile c
-};
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
 __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
 {
     return (id >= 0 && (int64_t)id < num_blocks) ? id : 0;
 }
 
-template <int H>
-__device__ __forceinline__ void load_chunk(ChunkRegs<H> &r, const uint16_t *k_lo,
-                                           const uint16_t *k_hi, const uint16_t *v_lo,
-                                           const uint16_t *v_hi, int col, int quad)
-{
-    // Keys: tile a, row m=col -> token 8*(col/4) + 4a + col%4 of the chunk,
-    // i.e. block col/8, row 8*((col/4)&1) + 4a + (col&3); k-values 32s + 8quad.
-    const uint16_t *kb = (col >> 3) ? k_hi : k_lo;
-    const int krow = 8 * ((col >> 2) & 1) + (col & 3);
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int s = 0; s < H / 32; ++s)
-            r.k[a][s] = load16_stream(kb + (krow + 4 * a) * H + 32 * s + 8 * quad);
-    // Values: tile c, lane (col, quad) -> dim 16c + col, tokens 8quad..8quad+7
-    // of the chunk, i.e. block quad/2, offsets 8*(quad&1)..+7 (contiguous).
-    const uint16_t *vb = (quad >> 1) ? v_hi : v_lo;
-#pragma unroll
-    for (int c = 0; c < H / 16; ++c)
-        r.v[c] = load16_stream(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
-}
-
 // `qf(s)` yields the lane's query operand for k-step s (from registers or LDS).
-template <int H, bool kTail, class QFrag>
-__device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, int rem, int quad,
+template <class Fmt, int H, bool kTail, class QFrag>
+__device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H> &r, QFrag &&qf,
+                                             int rem, int quad,
                                              float scale_log2, float &m, float &l,
                                              f32x4 (&acc)[H / 16])
 {
@@ -120,8 +91,8 @@ __device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, 
 #pragma unroll
     for (int s = 0; s < H / 32; ++s) {
         const bf16x8 q = qf(s);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[0][s]), q, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[1][s]), q, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 0, s), q, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 1, s), q, s1, 0, 0, 0);
     }
     // Lane (col, quad) now holds the scores of tokens 8quad + e, e = 0..7.
     float x[8];
@@ -166,16 +137,17 @@ __device__ __forceinline__ void attend_chunk(const ChunkRegs<H> &r, QFrag &&qf, 
     }
 #pragma unroll
     for (int c = 0; c < H / 16; ++c) {
-        const bf16x8 vv = as_bf16x8(kTail ? (r.v[c] & vmask) : r.v[c]);
+        const u32x4 vbits = Fmt::value(r, c);
+        const bf16x8 vv = as_bf16x8(kTail ? (vbits & vmask) : vbits);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, acc[c], 0, 0, 0);
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, acc[c], 0, 0, 0);
     }
 }
 
-// Depth of the register ring: chunks issued ahead of the one being computed
-// is kRing - 1 (16 KiB each).  One wave per SIMD owns up to 512 registers,
-// enough for four 64-register chunk buffers next to the accumulators.
-constexpr int kRingDepth = 4;
+// Register ring: a kernel keeps Fmt::kRing chunk buffers per wave, so
+// kRing - 1 chunks are in flight while one is computed.  One wave per SIMD
+// owns up to 512 registers: four 64-register bf16 chunks, or seven
+// 32-register FP8 chunks, fit next to the accumulators.
 
 // Runs chunks 0 .. total-1 (total >= 1) through a ring of kRing register
 // buffers: issue(buf, k) starts the loads of chunk k, attend(buf, k) consumes
@@ -212,7 +184,7 @@ __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&i
     }
 }
 
-template <int H, bool kSplit>
+template <class Fmt, int H, bool kSplit>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
@@ -258,7 +230,7 @@ void decode_kernel(DecodeParams p)
         const uint16_t *qrow = p.q + ((int64_t)b * p.num_heads + (live ? n : 0)) * H;
 #pragma unroll
         for (int s = 0; s < H / 32; ++s) {
-            u32x4 raw = load16(qrow + 32 * s + 8 * quad);
+            u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
             if (!live)
                 raw = u32x4{0u, 0u, 0u, 0u};
             qf[s] = as_bf16x8(raw);
@@ -267,17 +239,19 @@ void decode_kernel(DecodeParams p)
 
     const int64_t tile_elems = (int64_t)kBlockSize * H;              // one (block, head) tile
     const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
-    const uint16_t *kbase = p.key_cache + kvh * tile_elems;
-    const uint16_t *vbase = p.value_cache + kvh * tile_elems;
+    using Elem = typename Fmt::Elem;
+    using Regs = typename Fmt::template Regs<H>;
+    const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
+    const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
 
     // Issue the loads of chunk ci (tokens start + 32ci ...); its second block
     // is addressed only if the chunk reaches into it.
-    auto issue = [&](ChunkRegs<H> &r, int ci) {
+    auto issue = [&](Regs &r, int ci) {
         const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
         const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
                                                 : id0;
-        load_chunk<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
-                      vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
+                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
     };
 
     float m = -INFINITY, l = 0.f;
@@ -290,15 +264,15 @@ void decode_kernel(DecodeParams p)
     const int n_chunks = n_full + ((end - start) % kChunk != 0);
     const int tail_rem = end - start - n_full * kChunk;
     auto qfrag = [&](int s) { return qf[s]; };
-    auto attend = [&](const ChunkRegs<H> &r, int ci) {
+    auto attend = [&](const Regs &r, int ci) {
         if (ci < n_full)
-            attend_chunk<H, false>(r, qfrag, kChunk, quad, p.scale_log2, m, l, acc);
+            attend_chunk<Fmt, H, false>(r, qfrag, kChunk, quad, p.scale_log2, m, l, acc);
         else
-            attend_chunk<H, true>(r, qfrag, tail_rem, quad, p.scale_log2, m, l, acc);
+            attend_chunk<Fmt, H, true>(r, qfrag, tail_rem, quad, p.scale_log2, m, l, acc);
     };
 
-    ChunkRegs<H> ring[kRingDepth];
-    run_ring<kRingDepth>(n_chunks, ring, issue, attend);
+    Regs ring[Fmt::kRing];
+    run_ring<Fmt::kRing>(n_chunks, ring, issue, attend);
 
     // Each lane summed its own 8 tokens per chunk; add the four quads.
     l = sum_over_rows(l);
@@ -306,7 +280,7 @@ void decode_kernel(DecodeParams p)
         return;
     // acc[c] holds O^T[16c + 4quad + i][col], i = 0..3.
     if (!kSplit) {
-        const float inv = 1.0f / l;
+        const float inv = p.out_scale / l;
         float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
@@ -316,7 +290,7 @@ void decode_kernel(DecodeParams p)
         float *o = p.part_o + slot * H;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
-            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c];
+            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * p.out_scale;
         if (quad == 0) {
             p.part_ml[2 * slot] = m;
             p.part_ml[2 * slot + 1] = l;

@@ -32,7 +32,6 @@ namespace pkv {
 
 constexpr int kScheduleThreads = 1024;
 constexpr int kMaxBalancedWaves = 4096;
-constexpr int kBalancedRing = 3;
 
 struct BalancedParams {
     DecodeParams d;               // shapes, pointers, scale (part/num_parts unused)
@@ -194,16 +193,18 @@ struct Pos {
 
 // One ring slot: the chunk's key/value operands, plus the group's query
 // rows when the chunk opens a segment (or is the wave's first chunk).
-template <int H>
+template <class Fmt, int H>
 struct BalancedBuf {
-    ChunkRegs<H> kv;
+    typename Fmt::template Regs<H> kv;
     u32x4 q[H / 32];
 };
 
-template <int H>
+template <class Fmt, int H>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
+    using Elem = typename Fmt::Elem;
+    using Buf = BalancedBuf<Fmt, H>;
     const DecodeParams &d = p.d;
     const int wv = blockIdx.x;
     const int lane = threadIdx.x;
@@ -319,12 +320,12 @@ void decode_balanced_kernel(BalancedParams p)
         id1 = 2 * q.j + 1 < nblk ? clamp_block(scalar_load(row + 1), d.num_blocks) : id0;
     };
     load_ids(ip);
-    auto issue = [&](BalancedBuf<H> &r, int k) {
+    auto issue = [&](Buf &r, int k) {
         // ip is chunk k; (id0, id1) are its blocks
-        const uint16_t *kb = d.key_cache + ip.kvh * tile_elems;
-        const uint16_t *vb = d.value_cache + ip.kvh * tile_elems;
-        load_chunk<H>(r.kv, kb + id0 * block_elems, kb + id1 * block_elems,
-                      vb + id0 * block_elems, vb + id1 * block_elems, col, quad);
+        const Elem *kb = static_cast<const Elem *>(d.key_cache) + ip.kvh * tile_elems;
+        const Elem *vb = static_cast<const Elem *>(d.value_cache) + ip.kvh * tile_elems;
+        Fmt::template load<H>(r.kv, kb + id0 * block_elems, kb + id1 * block_elems,
+                              vb + id0 * block_elems, vb + id1 * block_elems, col, quad);
         if (k == 0 || ip.j == 0) {    // the chunk opens a segment: bring its queries
             // Columns past the group repeat its last query; their results are
             // never stored.
@@ -332,7 +333,7 @@ void decode_balanced_kernel(BalancedParams p)
             const uint16_t *qrow = d.q + ((int64_t)ip.b * d.num_heads + n) * H;
 #pragma unroll
             for (int s = 0; s < H / 32; ++s)
-                r.q[s] = load16(qrow + 32 * s + 8 * quad);
+                r.q[s] = load16(qrow + Fmt::dim_offset(s, quad));
         }
         if (k + 1 < total) {          // step to chunk k + 1 and fetch its block ids
             next_pos(ip);
@@ -351,7 +352,7 @@ void decode_balanced_kernel(BalancedParams p)
     bool piece_from_start = start.j == 0;   // this wave's piece began at the segment start
     auto qfrag = [&](int s) { return as_bf16x8(qcur[s]); };
 
-    auto attend = [&](const BalancedBuf<H> &r, int k) {
+    auto attend = [&](const Buf &r, int k) {
         if (k > 0)
             next_pos(ap);
         if (k == 0 || ap.j == 0) {
@@ -361,10 +362,10 @@ void decode_balanced_kernel(BalancedParams p)
         }
         const bool seg_end = ap.j + 1 == ap.nc;
         if (!seg_end || ap.ctx % kChunk == 0)
-            attend_chunk<H, false>(r.kv, qfrag, kChunk, quad, d.scale_log2, m, l, acc);
+            attend_chunk<Fmt, H, false>(r.kv, qfrag, kChunk, quad, d.scale_log2, m, l, acc);
         else
-            attend_chunk<H, true>(r.kv, qfrag, ap.ctx - kChunk * ap.j, quad, d.scale_log2, m, l,
-                                  acc);
+            attend_chunk<Fmt, H, true>(r.kv, qfrag, ap.ctx - kChunk * ap.j, quad, d.scale_log2,
+                                       m, l, acc);
         if (!seg_end && k + 1 < total)
             return;
         // The piece ends here (segment end, or the wave's last chunk).
@@ -372,7 +373,7 @@ void decode_balanced_kernel(BalancedParams p)
         const int n = ap.kvh * d.group + col;
         if (live) {
             if (piece_from_start && seg_end) {          // the whole segment: final output
-                const float inv = 1.0f / lt;
+                const float inv = d.out_scale / lt;
                 float *o = d.out + ((int64_t)ap.b * d.num_heads + n) * H;
 #pragma unroll
                 for (int c = 0; c < H / 16; ++c)
@@ -382,7 +383,7 @@ void decode_balanced_kernel(BalancedParams p)
                 float *o = p.piece_o + slot * H;
 #pragma unroll
                 for (int c = 0; c < H / 16; ++c)
-                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c];
+                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * d.out_scale;
                 if (quad == 0) {
                     p.piece_ml[2 * slot] = m;
                     p.piece_ml[2 * slot + 1] = lt;
@@ -397,8 +398,8 @@ void decode_balanced_kernel(BalancedParams p)
         piece_from_start = true;                    // the next piece opens a segment
     };
 
-    BalancedBuf<H> ring[kBalancedRing];
-    run_ring<kBalancedRing>(total, ring, issue, attend);
+    Buf ring[Fmt::kBalancedRing];
+    run_ring<Fmt::kBalancedRing>(total, ring, issue, attend);
 }
 
 // ------------------------------------------------------------------- merge --

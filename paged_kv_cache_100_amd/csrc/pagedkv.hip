@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 0;
+constexpr int kVersionMinor = 1;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
@@ -121,30 +121,10 @@ int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream
     return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-int pagedkv_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
-
-const char *pagedkv_status_string(int status)
-{
-    switch (status) {
-    case PKV_OK: return "ok";
-    case PKV_ERR_NULL: return "a required pointer is NULL";
-    case PKV_ERR_SHAPE: return "sizes inconsistent or out of range";
-    case PKV_ERR_UNSUPPORTED: return "head_dim, block_size or group size not supported";
-    case PKV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
-    case PKV_ERR_LAUNCH: return "kernel launch failed";
-    case PKV_ERR_DEVICE: return "no usable HIP device";
-    default: return "unknown status";
-    }
-}
-
-int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, void *key_cache,
-                    void *value_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t block_size, int64_t num_blocks, void *stream)
+// Checks shared by both appends (the grid size is checked too).
+int check_append(const void *k, const void *v, const int64_t *slot_mapping, void *key_cache,
+                 void *value_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t block_size, int64_t num_blocks)
 {
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
         return PKV_ERR_SHAPE;
@@ -157,45 +137,31 @@ int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, v
     if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache) ||
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
         return PKV_ERR_ALIGN;
-
-    pkv::AppendParams p;
-    p.k = static_cast<const uint16_t *>(k);
-    p.v = static_cast<const uint16_t *>(v);
-    p.slot_mapping = slot_mapping;
-    p.key_cache = static_cast<uint16_t *>(key_cache);
-    p.value_cache = static_cast<uint16_t *>(value_cache);
-    p.num_tokens = num_tokens;
-    p.num_kv_heads = num_kv_heads;
-    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
-
-    const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
-    const int64_t blocks = ceil_div(threads, 256);
-    if (blocks > INT32_MAX)
+    if (ceil_div((int64_t)num_tokens * num_kv_heads * (head_dim / 8), 256) > INT32_MAX)
         return PKV_ERR_SHAPE;
-    const void *kern = head_dim == 128 ? (const void *)pkv::append_kernel<128>
-                                       : (const void *)pkv::append_kernel<64>;
-    return launch(kern, dim3((unsigned)blocks), dim3(256), &p, stream);
+    return PKV_OK;
 }
 
-size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                   int32_t head_dim, int32_t max_context_len,
-                                   int32_t partition_size)
+dim3 append_grid(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim)
 {
-    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_context_len <= 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
-        return 0;
-    if (partition_size == 0)
-        return balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim).total;
-    return fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+    const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
+    return dim3((unsigned)ceil_div(threads, 256));
 }
 
-int paged_decode_attention(float *out, const void *q, const void *key_cache,
-                           const void *value_cache, const int32_t *block_tables,
-                           const int32_t *context_lens, float scale, int32_t num_kv_heads,
-                           int32_t block_size, int32_t num_seqs, int32_t num_heads,
-                           int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
-                           int64_t num_blocks, int32_t partition_size, void *workspace,
-                           size_t workspace_bytes, void *stream)
+// An FP8 pool scale: finite, positive, with a finite fp32 inverse.
+bool valid_pool_scale(float s)
+{
+    return isfinite(s) && s > 0.0f && isfinite(1.0f / s);
+}
+
+// Both decode entry points: bf16 pools (k_scale = v_scale = 1) or FP8 pools.
+template <class Fmt>
+int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
+                const int32_t *block_tables, const int32_t *context_lens, float scale,
+                float k_scale, float v_scale, int32_t num_kv_heads, int32_t block_size,
+                int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         max_context_len < 0 || num_blocks < 0)
@@ -214,7 +180,7 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
         (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_PARTITION ||
          partition_size % PKV_PARTITION_GRAIN != 0))
         return PKV_ERR_SHAPE;
-    if (!isfinite(scale))
+    if (!isfinite(scale) || !isfinite(scale * k_scale))
         return PKV_ERR_SHAPE;
     if (num_seqs == 0)
         return PKV_OK;
@@ -235,11 +201,12 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
     p.part_o = nullptr;
     p.part_ml = nullptr;
     p.q = static_cast<const uint16_t *>(q);
-    p.key_cache = static_cast<const uint16_t *>(key_cache);
-    p.value_cache = static_cast<const uint16_t *>(value_cache);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
     p.group = num_heads / num_kv_heads;
@@ -281,8 +248,8 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
             if (rc != PKV_OK)
                 return rc;
         }
-        const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<128>
-                                         : (const void *)pkv::decode_balanced_kernel<64>;
+        const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128>
+                                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64>;
         rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
         if (rc != PKV_OK)
             return rc;
@@ -312,11 +279,11 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
     const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
     const void *kern;
     if (head_dim == 128)
-        kern = split ? (const void *)pkv::decode_kernel<128, true>
-                     : (const void *)pkv::decode_kernel<128, false>;
+        kern = split ? (const void *)pkv::decode_kernel<Fmt, 128, true>
+                     : (const void *)pkv::decode_kernel<Fmt, 128, false>;
     else
-        kern = split ? (const void *)pkv::decode_kernel<64, true>
-                     : (const void *)pkv::decode_kernel<64, false>;
+        kern = split ? (const void *)pkv::decode_kernel<Fmt, 64, true>
+                     : (const void *)pkv::decode_kernel<Fmt, 64, false>;
     int rc = launch(kern, grid, dim3(pkv::kWave), &p, stream);
     if (rc != PKV_OK || !split)
         return rc;
@@ -334,6 +301,122 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
                                      : (const void *)pkv::merge_kernel<64>;
     return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads), &mp,
                   stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pagedkv_version(void) { return (kVersionMajor << 16) | kVersionMinor; }
+
+const char *pagedkv_status_string(int status)
+{
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "sizes inconsistent or out of range";
+    case PKV_ERR_UNSUPPORTED: return "head_dim, block_size or group size not supported";
+    case PKV_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+    }
+}
+
+int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, void *key_cache,
+                    void *value_cache, int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, void *stream)
+{
+    int rc = check_append(k, v, slot_mapping, key_cache, value_cache, num_tokens, num_kv_heads,
+                          head_dim, block_size, num_blocks);
+    if (rc != PKV_OK || num_tokens == 0)
+        return rc;
+    pkv::AppendParams p;
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.slot_mapping = slot_mapping;
+    p.key_cache = static_cast<uint16_t *>(key_cache);
+    p.value_cache = static_cast<uint16_t *>(value_cache);
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
+    const void *kern = head_dim == 128 ? (const void *)pkv::append_kernel<128>
+                                       : (const void *)pkv::append_kernel<64>;
+    return launch(kern, append_grid(num_tokens, num_kv_heads, head_dim), dim3(256), &p, stream);
+}
+
+int paged_kv_append_fp8(const void *k, const void *v, const int64_t *slot_mapping,
+                        void *key_cache, void *value_cache, float k_scale, float v_scale,
+                        int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, void *stream)
+{
+    int rc = check_append(k, v, slot_mapping, key_cache, value_cache, num_tokens, num_kv_heads,
+                          head_dim, block_size, num_blocks);
+    if (rc != PKV_OK)
+        return rc;
+    if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+        return PKV_ERR_SHAPE;
+    if (num_tokens == 0)
+        return PKV_OK;
+    pkv::AppendFp8Params p;
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.slot_mapping = slot_mapping;
+    p.key_cache = static_cast<uint8_t *>(key_cache);
+    p.value_cache = static_cast<uint8_t *>(value_cache);
+    p.k_inv = 1.0f / k_scale;
+    p.v_inv = 1.0f / v_scale;
+    p.num_tokens = num_tokens;
+    p.num_kv_heads = num_kv_heads;
+    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
+    const void *kern = head_dim == 128 ? (const void *)pkv::append_fp8_kernel<128>
+                                       : (const void *)pkv::append_fp8_kernel<64>;
+    return launch(kern, append_grid(num_tokens, num_kv_heads, head_dim), dim3(256), &p, stream);
+}
+
+size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len <= 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
+        return 0;
+    if (partition_size == 0)
+        return balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim).total;
+    return fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+}
+
+int paged_decode_attention(float *out, const void *q, const void *key_cache,
+                           const void *value_cache, const int32_t *block_tables,
+                           const int32_t *context_lens, float scale, int32_t num_kv_heads,
+                           int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                           int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int64_t num_blocks, int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    return decode_impl<pkv::KvBf16>(out, q, key_cache, value_cache, block_tables, context_lens,
+                                    scale, 1.0f, 1.0f, num_kv_heads, block_size, num_seqs,
+                                    num_heads, head_dim, max_blocks_per_seq, max_context_len,
+                                    num_blocks, partition_size, workspace, workspace_bytes,
+                                    stream);
+}
+
+int paged_decode_attention_fp8(float *out, const void *q, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, float scale, float k_scale,
+                               float v_scale, int32_t num_kv_heads, int32_t block_size,
+                               int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int64_t num_blocks, int32_t partition_size, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+        return PKV_ERR_SHAPE;
+    return decode_impl<pkv::KvFp8>(out, q, key_cache, value_cache, block_tables, context_lens,
+                                   scale, k_scale, v_scale, num_kv_heads, block_size, num_seqs,
+                                   num_heads, head_dim, max_blocks_per_seq, max_context_len,
+                                   num_blocks, partition_size, workspace, workspace_bytes, stream);
 }
 
 size_t pagedkv_stream_read_sink_bytes(size_t bytes)

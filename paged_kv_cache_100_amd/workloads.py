@@ -28,6 +28,14 @@ Poisoning (``poison=True``): cache slots that hold no valid token (block
 tails, and the new token's slot before the append) are bf16 NaN (0x7FC0), and
 block-table entries past a sequence's last block point at one extra pool
 block filled with NaN.  A kernel that reads any of them produces NaN.
+
+FP8 pools (``kv_dtype="fp8"``, the 8-bit cache of "Week 11. Inference",
+step 2): the same draws, stored as OCP FP8 E4M3 codes (uint8) with one scale
+per pool chosen so that 6 standard deviations map to the largest code, 448:
+k_scale = 6 * key_scale / 448, v_scale = 6 / 448 (fp32).  The cached codes
+are the drawn values divided by the pool scale, clamped to +-448 and cast
+with torch's float8_e4m3fn conversion; poison is the NaN code 0x7F.  The
+step's new rows stay bf16 (the append quantises them).
 """
 from __future__ import annotations
 
@@ -38,6 +46,9 @@ from typing import List, Optional
 import torch
 
 BF16_NAN_BITS = 0x7FC0
+E4M3_NAN_CODE = 0x7F
+E4M3_MAX = 448.0
+FP8_SIGMAS = 6.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +73,7 @@ class Spec:
     sharers: int = 0
     partition_size: int = 0               # 0: the library chooses
     seed: int = 0
+    kv_dtype: str = "bf16"                # "bf16" or "fp8" (E4M3 codes, one scale per pool)
 
 
 # The five workloads (seed = 1000 + index).
@@ -83,6 +95,9 @@ SPECS = {
     "llama3_70b_long_b4_ctx128k": Spec("llama3_70b_long_b4_ctx128k", B=4, N=64, K=8, H=128,
                                        bs=16, ctx=131072, partition_size=512, seed=1005),
 }
+# The same draws in FP8 pools.
+for _name in ("tiny", "llama3_8b_b64_ctx8k", "llama3_70b_ragged_b100"):
+    SPECS[_name + "_fp8"] = dataclasses.replace(SPECS[_name], name=_name + "_fp8", kv_dtype="fp8")
 
 
 @dataclasses.dataclass
@@ -92,14 +107,17 @@ class Workload:
     k_new: torch.Tensor          # [B, K, H] bf16
     v_new: torch.Tensor          # [B, K, H] bf16
     slot_mapping: torch.Tensor   # [B] int64
-    key_cache: torch.Tensor      # [nb, K, bs, H] bf16 (state before the append)
-    value_cache: torch.Tensor    # [nb, K, H, bs] bf16
+    key_cache: torch.Tensor      # [nb, K, bs, H] bf16 or uint8 codes (state before the append)
+    value_cache: torch.Tensor    # [nb, K, H, bs] bf16 or uint8 codes
     block_tables: torch.Tensor   # [B, max_blocks] int32
     context_lens: torch.Tensor   # [B] int32
     scale: float                 # fp32 value of 1/sqrt(H)
     sharer_ids: List[int]
     shared_blocks: List[int]
     poison_block: Optional[int]
+    kv_dtype: str = "bf16"
+    k_scale: float = 1.0         # FP8 pools: a key code c stands for e4m3(c) * k_scale
+    v_scale: float = 1.0
 
     @property
     def max_context_len(self) -> int:
@@ -120,6 +138,18 @@ class Workload:
 def fp32_scale(H: int) -> float:
     """1/sqrt(H) rounded to fp32, as a Python float."""
     return float(torch.tensor(1.0 / math.sqrt(H), dtype=torch.float32))
+
+
+def fp8_scales(spec: Spec):
+    """(k_scale, v_scale) of a workload's FP8 pools, fp32 values as floats."""
+    f32 = lambda x: float(torch.tensor(x, dtype=torch.float32))
+    return (f32(FP8_SIGMAS * spec.key_scale / E4M3_MAX), f32(FP8_SIGMAS / E4M3_MAX))
+
+
+def _e4m3_codes(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """Codes of x / scale (clamped to the finite range; NaN stays NaN) as uint8."""
+    y = (x.float() / scale).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
 def _randn_bf16(shape, gen, mult: float = 1.0) -> torch.Tensor:
@@ -234,11 +264,20 @@ def make(spec_or_name, poison: bool = True) -> Workload:
         prefix_k = _randn_bf16((spec.shared_prefix, K, H), gen, spec.key_scale)
         prefix_v = _randn_bf16((spec.shared_prefix, K, H), gen)
 
-    key_cache = torch.empty((lay.num_blocks, K, bs, H), dtype=torch.bfloat16)
-    value_cache = torch.empty((lay.num_blocks, K, H, bs), dtype=torch.bfloat16)
+    fp8 = spec.kv_dtype == "fp8"
+    if spec.kv_dtype not in ("bf16", "fp8"):
+        raise ValueError(f"unknown kv_dtype {spec.kv_dtype!r}")
+    k_scale, v_scale = fp8_scales(spec) if fp8 else (1.0, 1.0)
+    pool_dtype = torch.uint8 if fp8 else torch.bfloat16
+    key_cache = torch.empty((lay.num_blocks, K, bs, H), dtype=pool_dtype)
+    value_cache = torch.empty((lay.num_blocks, K, H, bs), dtype=pool_dtype)
     fill_bits = BF16_NAN_BITS if poison else 0
-    key_cache.view(torch.int16).fill_(fill_bits)
-    value_cache.view(torch.int16).fill_(fill_bits)
+    if fp8:
+        key_cache.fill_(E4M3_NAN_CODE if poison else 0)
+        value_cache.fill_(E4M3_NAN_CODE if poison else 0)
+    else:
+        key_cache.view(torch.int16).fill_(fill_bits)
+        value_cache.view(torch.int16).fill_(fill_bits)
 
     for b in range(B):
         nb_b = lay.blocks_per_seq[b]
@@ -253,6 +292,9 @@ def make(spec_or_name, poison: bool = True) -> Workload:
         valid = max(lay.context_lens[b] - 1, 0)
         lk[valid:].view(torch.int16).fill_(fill_bits)
         lv[valid:].view(torch.int16).fill_(fill_bits)
+        if fp8:
+            lk = _e4m3_codes(lk, k_scale)
+            lv = _e4m3_codes(lv, v_scale)
         ids = lay.block_tables[b, :nb_b].long()
         key_cache[ids] = lk.view(nb_b, bs, K, H).permute(0, 2, 1, 3)
         value_cache[ids] = lv.view(nb_b, bs, K, H).permute(0, 2, 3, 1)
@@ -262,13 +304,15 @@ def make(spec_or_name, poison: bool = True) -> Workload:
                     block_tables=lay.block_tables,
                     context_lens=torch.tensor(lay.context_lens, dtype=torch.int32),
                     scale=fp32_scale(H), sharer_ids=lay.sharer_ids,
-                    shared_blocks=lay.shared_blocks, poison_block=lay.poison_block)
+                    shared_blocks=lay.shared_blocks, poison_block=lay.poison_block,
+                    kv_dtype=spec.kv_dtype, k_scale=k_scale, v_scale=v_scale)
 
 
 def small(name: str, **overrides) -> Spec:
     """A reduced variant of a named workload the oracle finishes in seconds
     (same heads, head dim and block size; fewer sequences and tokens)."""
     base = SPECS[name]
+    key = name[:-len("_fp8")] if name.endswith("_fp8") else name
     defaults = {
         "llama3_8b_b64_ctx8k": dict(B=3, ctx=[700, 1040, 33]),
         "llama2_13b_b1_ctx1k": dict(B=1, ctx=[1024]),
@@ -279,6 +323,6 @@ def small(name: str, **overrides) -> Spec:
                                        sharers=4),
         "llama3_70b_long_b4_ctx128k": dict(B=2, ctx=[2600, 1537]),
         "tiny": dict(),
-    }[name]
+    }[key]
     defaults.update(overrides)
     return dataclasses.replace(base, name=base.name + "_small", **defaults)

@@ -22,8 +22,16 @@ def f64_to_bits(x) -> np.ndarray:
     return (u >> 16).astype(np.uint16)
 
 
+def pool_bits(t: torch.Tensor) -> np.ndarray:
+    """A KV pool as the oracle takes it: uint16 bf16 bits, or uint8 FP8 codes."""
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return t.detach().cpu().contiguous().view(torch.uint8).numpy().copy()
+    return bits(t)
+
+
 def oracle_inputs(w):
     """numpy views of a workload's decode inputs in the oracle's types."""
-    return dict(q=bits(w.q), key_cache=bits(w.key_cache), value_cache=bits(w.value_cache),
+    return dict(q=bits(w.q), key_cache=pool_bits(w.key_cache),
+                value_cache=pool_bits(w.value_cache),
                 block_tables=w.block_tables.numpy().astype(np.int32),
                 context_lens=w.context_lens.numpy().astype(np.int32))

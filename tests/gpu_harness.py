@@ -18,7 +18,7 @@ import torch
 import oracle
 import paged_kv_cache_100_amd as pkv
 
-from _util import bits, oracle_inputs
+from _util import bits, oracle_inputs, pool_bits
 
 ABS_TOL = 2e-3
 REL_TOL = 2e-3
@@ -29,27 +29,74 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+def gpu_append(g, w):
+    """The workload's append through the C ABI (bf16 or FP8 pools)."""
+    if w.kv_dtype == "fp8":
+        pkv.paged_kv_append_fp8(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache,
+                                w.k_scale, w.v_scale)
+    else:
+        pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+
+
+def gpu_decode(out, g, w, partition: int = 0, max_context_len=None, workspace=None):
+    """The workload's decode through the C ABI (bf16 or FP8 pools)."""
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    if w.kv_dtype == "fp8":
+        pkv.paged_decode_attention_fp8(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                       g.context_lens, w.scale, w.k_scale, w.v_scale, w.spec.K,
+                                       w.spec.bs, max_context_len=mcl, partition=partition,
+                                       workspace=workspace)
+    else:
+        pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                   g.context_lens, w.scale, w.spec.K, w.spec.bs,
+                                   max_context_len=mcl, partition=partition,
+                                   workspace=workspace)
+    return out
+
+
 def gpu_step(w, partition: int = 0, device: str = "cuda:0", max_context_len=None):
     """Append then decode on the GPU.  Returns (out float32 cpu, gpu workload)."""
     g = w.to(device)
-    pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
+    gpu_append(g, w)
     out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=device)
-    mcl = w.max_context_len if max_context_len is None else max_context_len
-    pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
-                               g.context_lens, w.scale, w.spec.K, w.spec.bs,
-                               max_context_len=mcl, partition=partition)
+    gpu_decode(out, g, w, partition=partition, max_context_len=max_context_len)
     torch.cuda.synchronize()
     return out.cpu(), g
+
+
+def oracle_append(w, inp):
+    """The oracle's append into the host pools of ``inp`` (in place)."""
+    if w.kv_dtype == "fp8":
+        oracle.append_fp8(bits(w.k_new), bits(w.v_new), w.slot_mapping.numpy(),
+                          inp["key_cache"], inp["value_cache"], w.k_scale, w.v_scale)
+    else:
+        oracle.append(bits(w.k_new), bits(w.v_new), w.slot_mapping.numpy(), inp["key_cache"],
+                      inp["value_cache"])
+
+
+def oracle_decode(w, inp):
+    if w.kv_dtype == "fp8":
+        return oracle.decode_fp8(inp["q"], inp["key_cache"], inp["value_cache"],
+                                 inp["block_tables"], inp["context_lens"], w.scale, w.k_scale,
+                                 w.v_scale)
+    return oracle.decode(inp["q"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
+                         inp["context_lens"], w.scale)
+
+
+def oracle_decode_rows(w, inp, rows_b, rows_n):
+    if w.kv_dtype == "fp8":
+        return oracle.decode_rows_fp8(rows_b, rows_n, inp["q"], inp["key_cache"],
+                                      inp["value_cache"], inp["block_tables"],
+                                      inp["context_lens"], w.scale, w.k_scale, w.v_scale)
+    return oracle.decode_rows(rows_b, rows_n, inp["q"], inp["key_cache"], inp["value_cache"],
+                              inp["block_tables"], inp["context_lens"], w.scale)
 
 
 def oracle_step(w):
     """Oracle append on host copies of the pools, then the oracle decode."""
     inp = oracle_inputs(w)
-    oracle.append(bits(w.k_new), bits(w.v_new), w.slot_mapping.numpy(), inp["key_cache"],
-                  inp["value_cache"])
-    ref = oracle.decode(inp["q"], inp["key_cache"], inp["value_cache"], inp["block_tables"],
-                        inp["context_lens"], w.scale)
-    return ref, inp
+    oracle_append(w, inp)
+    return oracle_decode(w, inp), inp
 
 
 def errors(got, ref):
@@ -76,8 +123,8 @@ def assert_parity(got, ref, what: str):
 
 
 def assert_append_exact(g, inp, what: str):
-    kc = bits(g.key_cache)
-    vc = bits(g.value_cache)
+    kc = pool_bits(g.key_cache)
+    vc = pool_bits(g.value_cache)
     assert np.array_equal(kc, inp["key_cache"]), f"{what}: key cache differs after append"
     assert np.array_equal(vc, inp["value_cache"]), f"{what}: value cache differs after append"
 

@@ -32,6 +32,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
+            "paged_kv_append_fp8", "paged_decode_attention_fp8",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
             "pagedkv_stream_copy"} <= set(names)
@@ -43,7 +44,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.0"
+    assert pkv.version() == "1.1"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -89,6 +90,42 @@ def test_decode_checks(L):
     assert decode(L, ws=0, part=32) == WS                 # split needs a workspace
     assert decode(L, wsb=16, part=32) == WS
     assert decode(L, ws=MIS, part=32) == ALIGN
+
+
+def append_fp8(L, k=A, v=A, slots=A, kc=A, vc=A, ks=0.01, vs=0.02, T=4, K=2, H=64, bs=16,
+               nb=8):
+    return L.paged_kv_append_fp8(k, v, slots, kc, vc, ks, vs, T, K, H, bs, nb, None)
+
+
+def test_append_fp8_checks(L):
+    assert append_fp8(L, T=0, k=0, v=0) == OK
+    assert append_fp8(L, k=0) == NULL
+    assert append_fp8(L, T=-1) == SHAPE
+    assert append_fp8(L, H=96) == UNSUP
+    assert append_fp8(L, vc=MIS) == ALIGN
+    for bad in (0.0, -0.5, float("inf"), float("nan"), 1e-45):   # 1e-45: inverse overflows
+        assert append_fp8(L, ks=bad) == SHAPE
+        assert append_fp8(L, vs=bad) == SHAPE
+        assert append_fp8(L, ks=bad, T=0, k=0, v=0) == SHAPE
+
+
+def decode_fp8(L, out=A, q=A, kc=A, vc=A, bt=A, cl=A, scale=0.125, ks=0.01, vs=0.02, K=2, bs=16,
+               B=4, N=8, H=64, maxblk=16, maxctx=256, nb=128, part=0, ws=A, wsb=1 << 30):
+    return L.paged_decode_attention_fp8(out, q, kc, vc, bt, cl, scale, ks, vs, K, bs, B, N, H,
+                                        maxblk, maxctx, nb, part, ws, wsb, None)
+
+
+def test_decode_fp8_checks(L):
+    assert decode_fp8(L, B=0) == OK
+    assert decode_fp8(L, kc=0) == NULL
+    assert decode_fp8(L, N=64, K=2) == UNSUP
+    assert decode_fp8(L, part=48) == SHAPE
+    assert decode_fp8(L, kc=MIS) == ALIGN
+    assert decode_fp8(L, ws=0, part=32) == WS
+    assert decode_fp8(L, scale=3e38, ks=10.0) == SHAPE     # scale * k_scale overflows
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
+        assert decode_fp8(L, ks=bad) == SHAPE
+        assert decode_fp8(L, vs=bad) == SHAPE
 
 
 def test_workspace_sizes(L):

@@ -10,16 +10,16 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 from paged_kv_cache_100_amd import workloads as W
 
 import gpu_harness as H
-from _util import bits
+from _util import oracle_inputs, pool_bits
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["llama3_8b_b64_ctx8k", "llama2_13b_b1_ctx1k", "llama2_13b_b64_ctx1k",
-        "llama2_13b_b256_ctx1k", "llama3_70b_ragged_b100", "llama3_70b_long_b4_ctx128k"]
+        "llama2_13b_b256_ctx1k", "llama3_70b_ragged_b100", "llama3_70b_long_b4_ctx128k",
+        "llama3_8b_b64_ctx8k_fp8", "llama3_70b_ragged_b100_fp8"]
 
 
 def sample_rows(w, n_random=8, seed=0):
@@ -46,14 +46,15 @@ def test_full_size(name):
         out, g = H.gpu_step(w, partition=w.spec.partition_size)
     assert torch.isfinite(out).all(), "non-finite output"
     with H.Timer("oracle append + compare pools"):
-        kc, vc = bits(w.key_cache), bits(w.value_cache)
-        oracle.append(bits(w.k_new), bits(w.v_new), w.slot_mapping.numpy(), kc, vc)
-        assert np.array_equal(bits(g.key_cache), kc), "key cache differs after append"
-        assert np.array_equal(bits(g.value_cache), vc), "value cache differs after append"
+        inp = oracle_inputs(w)
+        H.oracle_append(w, inp)
+        assert np.array_equal(pool_bits(g.key_cache), inp["key_cache"]), \
+            "key cache differs after append"
+        assert np.array_equal(pool_bits(g.value_cache), inp["value_cache"]), \
+            "value cache differs after append"
         del g
         torch.cuda.empty_cache()
     rb, rn = sample_rows(w)
     with H.Timer(f"oracle on {len(rb)} sampled rows"):
-        ref = oracle.decode_rows(rb, rn, bits(w.q), kc, vc, w.block_tables.numpy(),
-                                 w.context_lens.numpy(), w.scale)
+        ref = H.oracle_decode_rows(w, inp, rb, rn)
     H.assert_parity(out.numpy()[rb, rn], ref, f"{name} sampled rows")
