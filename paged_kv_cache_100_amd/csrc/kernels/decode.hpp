@@ -146,7 +146,7 @@ __device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H
 
 // Register ring: a kernel keeps Fmt::kRing chunk buffers per wave, so
 // kRing - 1 chunks are in flight while one is computed.  One wave per SIMD
-// owns up to 512 registers: four 64-register bf16 chunks, or seven
+// owns up to 512 registers: four 64-register bf16 chunks, or five
 // 32-register FP8 chunks, fit next to the accumulators.
 
 // Runs chunks 0 .. total-1 (total >= 1) through a ring of kRing register

@@ -111,10 +111,10 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1)
 
 struct KvFp8 {
     using Elem = uint8_t;
-    // An FP8 chunk is 32 registers per lane: twice the chunks in flight for
-    // the same bytes in flight as bf16.
-    static constexpr int kRing = 7;
-    static constexpr int kBalancedRing = 5;
+    // An FP8 chunk is 32 registers per lane.  Rings of 5 and 4 (16 and 12
+    // KiB in flight per wave) measured as fast as deeper ones (up to 8 and 5).
+    static constexpr int kRing = 5;
+    static constexpr int kBalancedRing = 4;
 
     template <int H>
     struct Regs {
