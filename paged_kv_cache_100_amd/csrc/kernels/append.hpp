@@ -28,30 +28,41 @@ struct AppendParams {
     int64_t num_slots;             // num_blocks * 16
 };
 
+// Makes the two row loads complete before the slot test: left alone, the
+// compiler moves them behind it and the thread waits for two memory round
+// trips (slot, then rows) instead of one.
+__device__ __forceinline__ void keep_loaded(const u32x4 &a, const u32x4 &b)
+{
+    asm volatile("" : : "v"(a), "v"(b));
+}
+
 template <int H>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
 {
     constexpr int kChunks = H / 8;   // 16-byte pieces per row
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * kChunks;
+    // The host guarantees T * K * H / 8 < 2^31: 32-bit index arithmetic.
+    const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t total = (uint32_t)p.num_tokens * p.num_kv_heads * kChunks;
     if (gid >= total)
         return;
     const int c = (int)(gid % kChunks);
-    const int64_t row = gid / kChunks;             // token * K + head
-    const int g = (int)(row % p.num_kv_heads);
-    const int64_t i = row / p.num_kv_heads;
+    const uint32_t row = gid / kChunks;            // token * K + head
+    const int g = (int)(row % (uint32_t)p.num_kv_heads);
+    const uint32_t i = row / (uint32_t)p.num_kv_heads;
 
+    // The rows' loads do not depend on the slot: issue all three together.
+    const int64_t src = (int64_t)row * H + 8 * c;
+    const u32x4 kk = load16(p.k + src);
+    const u32x4 vv = load16(p.v + src);
     const int64_t slot = p.slot_mapping[i];
+    keep_loaded(kk, vv);
     if (slot < 0 || slot >= p.num_slots)
         return;                                    // padding or outside the pool
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
     const int64_t tile = blk * p.num_kv_heads + g; // (block, head) tile index
 
-    const int64_t src = row * H + 8 * c;
-    store16(p.key_cache + (tile * kBlockSize + off) * H + 8 * c, load16(p.k + src));
-
-    const u32x4 vv = load16(p.v + src);
+    store16(p.key_cache + (tile * kBlockSize + off) * H + 8 * c, kk);
     uint16_t *dst = p.value_cache + (tile * H + 8 * c) * kBlockSize + off;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -112,27 +123,30 @@ template <int H>
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params p)
 {
     constexpr int kChunks = H / 8;   // 8-value pieces per row
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)p.num_tokens * p.num_kv_heads * kChunks;
+    const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t total = (uint32_t)p.num_tokens * p.num_kv_heads * kChunks;
     if (gid >= total)
         return;
     const int c = (int)(gid % kChunks);
-    const int64_t row = gid / kChunks;
-    const int g = (int)(row % p.num_kv_heads);
-    const int64_t i = row / p.num_kv_heads;
+    const uint32_t row = gid / kChunks;
+    const int g = (int)(row % (uint32_t)p.num_kv_heads);
+    const uint32_t i = row / (uint32_t)p.num_kv_heads;
 
+    const int64_t src = (int64_t)row * H + 8 * c;
+    const u32x4 kk = load16(p.k + src);
+    const u32x4 vv = load16(p.v + src);
     const int64_t slot = p.slot_mapping[i];
+    keep_loaded(kk, vv);
     if (slot < 0 || slot >= p.num_slots)
         return;
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
     const int64_t tile = blk * p.num_kv_heads + g;
 
-    const int64_t src = row * H + 8 * c;
-    const u32x2 kq = quantize8(load16(p.k + src), p.k_inv);
+    const u32x2 kq = quantize8(kk, p.k_inv);
     *reinterpret_cast<u32x2 *>(p.key_cache + (tile * kBlockSize + off) * H + 8 * c) = kq;
 
-    const u32x2 vq = quantize8(load16(p.v + src), p.v_inv);
+    const u32x2 vq = quantize8(vv, p.v_inv);
     uint8_t *dst = p.value_cache + (tile * H + 8 * c) * kBlockSize + off;
 #pragma unroll
     for (int e = 0; e < 8; ++e)

@@ -418,7 +418,8 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     constexpr int kLanesPerHead = kWave / Gp;
     constexpr int kVals = H / kLanesPerHead;      // values per lane (multiple of 4)
     constexpr int kTiles = kInlineScheduleSeqs / kWave;
-    constexpr int kFast = 4;                      // pieces combined in one round trip
+    // Pieces per memory round trip: up to 8, within about 128 registers of rows.
+    constexpr int kBatch = kVals / 4 >= 8 ? 4 : 8;
     const DecodeParams &d = p.d;
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
@@ -474,53 +475,50 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     // piece (w, seg): rows (w + seg) * G + g' for the group's heads g'
     auto row_of = [&](int w) { return ((int64_t)min(w, w_last) + seg) * d.group + gg; };
 
+    // Pieces are combined kBatch at a time: every load of a batch in one
+    // memory round trip, then the batch joins the running log-sum-exp state
+    // (maximum `big`, denominator `den`, numerator `num`), rescaled when the
+    // maximum grows.  Most segments span at most kBatch waves: one round trip.
     float big = -INFINITY, den = 0.f;
     f32x4 num[kVals / 4];
 #pragma unroll
     for (int v = 0; v < kVals / 4; ++v)
         num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (count <= kFast) {
-        // Common case (a segment over at most four waves): every load in one
-        // round trip, then the log-sum-exp combination in registers.
-        float mv[kFast], lv[kFast];
-        f32x4 ov[kFast][kVals / 4];
+    for (int i0 = 0; i0 < count; i0 += kBatch) {
+        float mv[kBatch], lv[kBatch];
+        f32x4 ov[kBatch][kVals / 4];
 #pragma unroll
-        for (int u = 0; u < kFast; ++u) {
-            const int64_t r = row_of(w_first + u);
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t r = row_of(w_first + i0 + u);
             mv[u] = p.piece_ml[2 * r];
             lv[u] = p.piece_ml[2 * r + 1];
 #pragma unroll
             for (int v = 0; v < kVals / 4; ++v)
                 ov[u][v] = *reinterpret_cast<const f32x4 *>(p.piece_o + r * H + h0 + 4 * v);
         }
-        bool use[kFast];
+        bool use[kBatch];
+        float nb = big;
 #pragma unroll
-        for (int u = 0; u < kFast; ++u) {
-            use[u] = u < count && !empty(w_first + u);
-            big = use[u] ? fmaxf(big, mv[u]) : big;
+        for (int u = 0; u < kBatch; ++u) {
+            use[u] = i0 + u < count && !empty(w_first + i0 + u);
+            nb = use[u] ? fmaxf(nb, mv[u]) : nb;
         }
+        // The first batch holds the segment's first piece, so nb is finite from
+        // then on; a later batch of empty waves leaves it unchanged (sc = 1).
+        const float sc = big == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(big - nb);
+        den *= sc;
 #pragma unroll
-        for (int u = 0; u < kFast; ++u) {
-            const float wt = use[u] ? __builtin_amdgcn_exp2f(mv[u] - big) : 0.f;
+        for (int v = 0; v < kVals / 4; ++v)
+            num[v] *= sc;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const float wt = use[u] ? __builtin_amdgcn_exp2f(mv[u] - nb) : 0.f;
             den += use[u] ? wt * lv[u] : 0.f;
 #pragma unroll
             for (int v = 0; v < kVals / 4; ++v)
                 num[v] += use[u] ? wt * ov[u][v] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    } else {
-        for (int i = 0; i < count; ++i)
-            if (!empty(w_first + i))
-                big = fmaxf(big, p.piece_ml[2 * row_of(w_first + i)]);
-        for (int i = 0; i < count; ++i) {
-            if (empty(w_first + i))
-                continue;
-            const int64_t r = row_of(w_first + i);
-            const float wt = __builtin_amdgcn_exp2f(p.piece_ml[2 * r] - big);
-            den += wt * p.piece_ml[2 * r + 1];
-#pragma unroll
-            for (int v = 0; v < kVals / 4; ++v)
-                num[v] += wt * *reinterpret_cast<const f32x4 *>(p.piece_o + r * H + h0 + 4 * v);
-        }
+        big = nb;
     }
     if (live) {
         const float inv = 1.0f / den;

@@ -137,8 +137,8 @@ int check_append(const void *k, const void *v, const int64_t *slot_mapping, void
     if (!aligned16(k) || !aligned16(v) || !aligned16(key_cache) || !aligned16(value_cache) ||
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
         return PKV_ERR_ALIGN;
-    if (ceil_div((int64_t)num_tokens * num_kv_heads * (head_dim / 8), 256) > INT32_MAX)
-        return PKV_ERR_SHAPE;
+    if ((int64_t)num_tokens * num_kv_heads * (head_dim / 8) + 256 > INT32_MAX)
+        return PKV_ERR_SHAPE;                      // the kernels index threads in 32 bits
     return PKV_OK;
 }
 
