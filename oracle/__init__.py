@@ -74,6 +74,12 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_decode_rows_fp8.argtypes = [P, P, P, i32, P, P, P, f32, f32, P, P, f32,
                                            i32, i32, i32, i32, i32, i32, i64, P, i32]
     lib.oracle_decode_rows_fp8.restype = i32
+    lib.oracle_decode_multi.argtypes = [P, P, P, P, i32, f32, f32, P, P, f32,
+                                        i32, i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_multi.restype = i32
+    lib.oracle_decode_multi_rows.argtypes = [P, P, P, P, i32, P, P, P, i32, f32, f32, P, P, f32,
+                                             i32, i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_multi_rows.restype = i32
     return lib
 
 
@@ -282,6 +288,61 @@ def decode_rows_fp8(rows_b, rows_n, q, key_cache, value_cache, block_tables, con
         _ptr(out), _ptr(rb), _ptr(rn), R, _ptr(q), _ptr(kc), _ptr(vc),
         float(np.float32(k_scale)), float(np.float32(v_scale)), _ptr(bt), _ptr(cl),
         float(np.float32(scale)), B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (row, block id, shape or context)")
+    return out
+
+
+# ------------------------------------------------------- multi-query ----
+# Q query tokens per sequence (speculative verification): q, out [B, Q, N, H];
+# query i sees positions 0 .. ctx - Q + i (bottom-right causal mask).
+
+_KV_DTYPES = {np.dtype(np.uint16): 0, np.dtype(np.uint8): 1}
+
+
+def _multi_args(q, key_cache, value_cache, block_tables, context_lens):
+    q = _as(q, np.uint16)
+    if q.ndim != 4:
+        raise ValueError("q must be [B, Q, N, H]")
+    B, Q, N, H = q.shape
+    kc = np.ascontiguousarray(key_cache)
+    if kc.dtype not in _KV_DTYPES:
+        raise TypeError("pools must be uint16 (bf16 bits) or uint8 (E4M3 codes)")
+    _, kc, vc, bt, cl, (_, _, _, nb, K, bs) = _decode_args(
+        q.reshape(B, Q * N, H), kc, value_cache, block_tables, context_lens, kc.dtype.type)
+    return q, kc, vc, bt, cl, (B, Q, N, H, nb, K, bs), _KV_DTYPES[kc.dtype]
+
+
+def decode_multi(q, key_cache, value_cache, block_tables, context_lens, scale,
+                 k_scale: float = 1.0, v_scale: float = 1.0, lib=None) -> np.ndarray:
+    """Q query tokens per sequence over bf16 or FP8 pools, float64 [B, Q, N, H]."""
+    q, kc, vc, bt, cl, (B, Q, N, H, nb, K, bs), dt = _multi_args(
+        q, key_cache, value_cache, block_tables, context_lens)
+    out = np.zeros((B, Q, N, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_multi(
+        _ptr(out), _ptr(q), _ptr(kc), _ptr(vc), dt, float(np.float32(k_scale)),
+        float(np.float32(v_scale)), _ptr(bt), _ptr(cl), float(np.float32(scale)),
+        B, Q, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (block id, shape or context)")
+    return out
+
+
+def decode_multi_rows(rows_b, rows_i, rows_n, q, key_cache, value_cache, block_tables,
+                      context_lens, scale, k_scale: float = 1.0, v_scale: float = 1.0,
+                      lib=None) -> np.ndarray:
+    """Rows (rows_b[r], rows_i[r], rows_n[r]) of ``decode_multi`` only, float64 [R, H]."""
+    q, kc, vc, bt, cl, (B, Q, N, H, nb, K, bs), dt = _multi_args(
+        q, key_cache, value_cache, block_tables, context_lens)
+    rb, ri, rn = _as(rows_b, np.int32), _as(rows_i, np.int32), _as(rows_n, np.int32)
+    R = rb.shape[0]
+    out = np.zeros((R, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_multi_rows(
+        _ptr(out), _ptr(rb), _ptr(ri), _ptr(rn), R, _ptr(q), _ptr(kc), _ptr(vc), dt,
+        float(np.float32(k_scale)), float(np.float32(v_scale)), _ptr(bt), _ptr(cl),
+        float(np.float32(scale)), B, Q, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
     if rc:
         raise ValueError("invalid decode arguments (row, block id, shape or context)")
     return out

@@ -76,3 +76,33 @@ def paged_append(k, v, slot_mapping, key_cache, value_cache):
             for h in range(len(k[i][g])):
                 key_cache[p][g][o][h] = k[i][g][h]
                 value_cache[p][g][h][o] = v[i][g][h]
+
+
+def paged_decode_multi(q, key_cache, value_cache, block_tables, context_lens, scale):
+    """Several query tokens per sequence: q[b][r][n][h] for the seq_len_q = Q
+    tokens that end the sequence's seq_len_k = context_lens[b] cached ones.
+
+    The lesson's Build-It step 2 drops score (r, j) when the key index j
+    exceeds the query index r by at least seq_len_k - seq_len_q + 1 (its
+    upper-triangle mask with that diagonal offset).  Returns out[b][r][n][h].
+    """
+    out = []
+    for b in range(len(q)):
+        seq_len_q, seq_len_k = len(q[b]), context_lens[b]
+        rows_b = []
+        for r in range(seq_len_q):
+            keep = [j for j in range(seq_len_k) if j - r < seq_len_k - seq_len_q + 1]
+            N = len(q[b][r])
+            K = len(key_cache[0]) if key_cache else 1
+            bs = len(key_cache[0][0]) if key_cache else 1
+            group = N // K
+            rows_r = []
+            for n in range(N):
+                g = n // group
+                keys = [list(key_cache[block_tables[b][j // bs]][g][j % bs]) for j in keep]
+                values = [[value_cache[block_tables[b][j // bs]][g][h][j % bs]
+                           for h in range(len(q[b][r][n]))] for j in keep]
+                rows_r.append(attend_one(q[b][r][n], keys, values, scale))
+            rows_b.append(rows_r)
+        out.append(rows_b)
+    return out

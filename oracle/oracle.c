@@ -193,22 +193,19 @@ int oracle_append_fp8(const uint16_t *k, const uint16_t *v, const int64_t *slot_
 }
 
 /*
- * One output row (sequence b, query head n): the definition of
- * softmax(q K^T * scale) V over the sequence's ctx positions, gathering each
- * position t through the block table.  `scores` is caller scratch of length
- * ctx.  Writes H doubles to `row`.
+ * One output row (query row qrow of query head n): the definition of
+ * softmax(q K^T * scale) V over the first ctx positions of the sequence
+ * whose block-table row is `table`, gathering each position t through it.
+ * `scores` is caller scratch of length ctx.  Writes H doubles to `row`.
  */
 static int decode_row(double *row, double *scores,
-                      const uint16_t *q, const void *key_cache,
+                      const uint16_t *qrow, const void *key_cache,
                       const void *value_cache, int dtype, double k_scale, double v_scale,
-                      const int32_t *block_tables,
-                      int ctx, int b, int n, float scale,
-                      int N, int K, int H, int bs, int max_blocks, int64_t num_blocks)
+                      const int32_t *table, int ctx, int n, float scale,
+                      int N, int K, int H, int bs, int64_t num_blocks)
 {
     int G = N / K;
     int g = n / G;
-    const uint16_t *qrow = q + ((size_t)b * N + n) * H;
-    const int32_t *table = block_tables + (size_t)b * max_blocks;
     double sc = (double)scale;
 
     for (int h = 0; h < H; h++)
@@ -281,9 +278,9 @@ static int decode_all(double *out, const uint16_t *q, const void *key_cache,
             continue;
         }
         status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
-                             q, key_cache, value_cache, dtype, k_scale, v_scale, block_tables,
-                             context_lens[b], b, n, scale, N, K, H, bs, max_blocks,
-                             num_blocks) != 0;
+                             q + ((size_t)b * N + n) * H, key_cache, value_cache, dtype,
+                             k_scale, v_scale, block_tables + (size_t)b * max_blocks,
+                             context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
     }
     return status ? -1 : 0;
 }
@@ -311,9 +308,9 @@ static int decode_rows_all(double *out_rows, const int32_t *rows_b, const int32_
             continue;
         }
         status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
-                             q, key_cache, value_cache, dtype, k_scale, v_scale, block_tables,
-                             context_lens[b], b, n, scale, N, K, H, bs, max_blocks,
-                             num_blocks) != 0;
+                             q + ((size_t)b * N + n) * H, key_cache, value_cache, dtype,
+                             k_scale, v_scale, block_tables + (size_t)b * max_blocks,
+                             context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
     }
     return status ? -1 : 0;
 }
@@ -363,6 +360,84 @@ int oracle_decode_rows_fp8(double *out_rows, const int32_t *rows_b, const int32_
     return decode_rows_all(out_rows, rows_b, rows_n, R, q, key_cache, value_cache, KV_FP8,
                            k_scale, v_scale, block_tables, context_lens, scale, B, N, K, H,
                            bs, max_blocks, num_blocks, scratch, scratch_stride);
+}
+
+/*
+ * Several query tokens per sequence: the Q tokens of a speculative-decoding
+ * verification pass (the lesson's speculative-decoding section: the target
+ * model checks all draft tokens in one forward pass), appended to the cache
+ * before attention like a single decode token.  The lesson's Build-It step 2
+ * masks, for seq_len_q > 1, every score whose key index exceeds the query
+ * index by seq_len_k - seq_len_q or more (an upper triangle anchored at the
+ * bottom-right corner), so query i of Q -- the token at position
+ * ctx - Q + i -- sees positions 0 .. ctx - Q + i, as if the tokens had been
+ * decoded one after another.  A query that sees no position (ctx < Q - i)
+ * gets zeros, like an empty sequence.
+ * q and out are [B][Q][N][H]; kv_dtype is KV_BF16 (pools of bf16 bits) or
+ * KV_FP8 (E4M3 codes with scales k_scale, v_scale).
+ */
+static int visible_positions(int ctx, int Q, int i)
+{
+    int v = ctx - Q + i + 1;
+    return v < 0 ? 0 : v;
+}
+
+int oracle_decode_multi(double *out, const uint16_t *q, const void *key_cache,
+                        const void *value_cache, int kv_dtype, float k_scale, float v_scale,
+                        const int32_t *block_tables, const int32_t *context_lens, float scale,
+                        int B, int Q, int N, int K, int H, int bs, int max_blocks,
+                        int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    if (Q < 1 || (kv_dtype != KV_BF16 && kv_dtype != KV_FP8) ||
+        check_shape(context_lens, B, N, K, bs, max_blocks))
+        return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int r = 0; r < B * Q * N; r++) {
+        int b = r / (Q * N), i = (r / N) % Q, n = r % N;
+        int tid = thread_id();
+        if (context_lens[b] > scratch_stride) {
+            status |= 1;
+            continue;
+        }
+        status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
+                             q + (size_t)r * H, key_cache, value_cache, kv_dtype, k_scale,
+                             v_scale, block_tables + (size_t)b * max_blocks,
+                             visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
+                             num_blocks) != 0;
+    }
+    return status ? -1 : 0;
+}
+
+/* Rows (rows_b[r], rows_i[r], rows_n[r]) of oracle_decode_multi only. */
+int oracle_decode_multi_rows(double *out_rows, const int32_t *rows_b, const int32_t *rows_i,
+                             const int32_t *rows_n, int R, const uint16_t *q,
+                             const void *key_cache, const void *value_cache, int kv_dtype,
+                             float k_scale, float v_scale, const int32_t *block_tables,
+                             const int32_t *context_lens, float scale, int B, int Q, int N,
+                             int K, int H, int bs, int max_blocks, int64_t num_blocks,
+                             double *scratch, int scratch_stride)
+{
+    if (Q < 1 || (kv_dtype != KV_BF16 && kv_dtype != KV_FP8) ||
+        check_shape(context_lens, B, N, K, bs, max_blocks))
+        return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int r = 0; r < R; r++) {
+        int b = rows_b[r], i = rows_i[r], n = rows_n[r];
+        int tid = thread_id();
+        if (b < 0 || b >= B || i < 0 || i >= Q || n < 0 || n >= N ||
+            context_lens[b] > scratch_stride) {
+            status |= 1;
+            continue;
+        }
+        status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
+                             q + (((size_t)b * Q + i) * N + n) * H, key_cache, value_cache,
+                             kv_dtype, k_scale, v_scale, block_tables + (size_t)b * max_blocks,
+                             visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
+                             num_blocks) != 0;
+    }
+    return status ? -1 : 0;
 }
 
 /*

@@ -429,4 +429,88 @@ def check_printed_kv_sizes(lib):
         assert mha == r["factor"] * gqa
 
 
+# ----------------------------------------------------------- multi-query ----
+# Q query tokens per sequence, q and out [B, Q, N, H].
+
+def _multi_case(seed, Q, **kw):
+    c = Case(seed, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    c.Q = Q
+    c.qm = to_bf16_bits(rng.standard_normal((c.B, Q, c.N, c.H)))
+    return c
+
+
+def check_multi_brute_force(lib):
+    for seed, (Q, N, K, bs, H) in enumerate([(3, 4, 2, 4, 8), (5, 6, 1, 4, 4),
+                                              (2, 4, 4, 16, 8)]):
+        c = _multi_case(300 + seed, Q, N=N, K=K, bs=bs, H=H, max_ctx=30)
+        c.ctx = np.maximum(c.ctx, Q).astype(np.int32)      # the Q tokens are in the cache
+        got = oracle.decode_multi(c.qm, c.kc, c.vc, c.tables, c.ctx, c.scale, lib=lib)
+        ref = np.array(brute.paged_decode_multi(
+            bits_to_f64(c.qm).tolist(), bits_to_f64(c.kc).tolist(), bits_to_f64(c.vc).tolist(),
+            c.tables.tolist(), c.ctx.tolist(), c.scale))
+        assert_close(got, ref, 1e-12, f"multi-query brute force (Q={Q}, N={N}, K={K})")
+
+
+def check_multi_torch_bottom_right_mask(lib):
+    """torch float64 SDPA on the gathered cache with the lesson's mask: key j
+    is hidden from query r when j - r >= Sk - Sq + 1 (np.triu with that
+    diagonal offset)."""
+    Q = 4
+    c = _multi_case(311, Q, B=3, N=8, K=2, H=16, bs=4, ctx=[4, 17, 33])
+    got = oracle.decode_multi(c.qm, c.kc, c.vc, c.tables, c.ctx, c.scale, lib=lib)
+    qf = bits_to_f64(c.qm)
+    G = c.N // c.K
+    for b, (kb, vb) in enumerate(c.contiguous()):
+        Sk = int(c.ctx[b])
+        hidden = np.triu(np.ones((Q, Sk), bool), k=Sk - Q + 1)
+        qt = torch.from_numpy(qf[b].transpose(1, 0, 2).copy())            # [N, Q, H]
+        kt = torch.from_numpy(np.repeat(kb.transpose(1, 0, 2), G, axis=0).copy())  # [N, Sk, H]
+        vt = torch.from_numpy(np.repeat(vb.transpose(1, 0, 2), G, axis=0).copy())
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, attn_mask=torch.from_numpy(~hidden), scale=c.scale)
+        assert_close(got[b], ref.numpy().transpose(1, 0, 2), 1e-12,
+                     f"multi-query vs torch SDPA with the bottom-right mask (seq {b})")
+
+
+def check_multi_q1_is_decode(lib):
+    c = Case(321, B=4, N=8, K=2, H=8, bs=4, max_ctx=50)
+    got = oracle.decode_multi(c.q.reshape(c.B, 1, c.N, c.H), c.kc, c.vc, c.tables, c.ctx,
+                              c.scale, lib=lib)
+    assert np.array_equal(got[:, 0], c.decode(lib)), "Q = 1 differs from single-token decode"
+
+
+def check_multi_is_sequential_decoding(lib):
+    """Verification of Q appended tokens equals decoding them one after
+    another: the i-th token's step sees the cache up to and including itself."""
+    Q = 5
+    c = _multi_case(331, Q, B=3, N=4, K=2, H=8, bs=4, ctx=[5, 23, 40])
+    got = oracle.decode_multi(c.qm, c.kc, c.vc, c.tables, c.ctx, c.scale, lib=lib)
+    for i in range(Q):
+        step = oracle.decode(np.ascontiguousarray(c.qm[:, i]), c.kc, c.vc, c.tables,
+                             (c.ctx - (Q - 1 - i)).astype(np.int32), c.scale, lib=lib)
+        assert np.array_equal(got[:, i], step), f"query {i} differs from its sequential step"
+
+
+def check_multi_rows_and_fp8(lib):
+    Q = 3
+    c = _multi_case(341, Q, B=3, N=6, K=3, H=8, bs=4, ctx=[3, 20, 31])
+    full = oracle.decode_multi(c.qm, c.kc, c.vc, c.tables, c.ctx, c.scale, lib=lib)
+    rb = np.array([2, 0, 1, 2], np.int32)
+    ri = np.array([0, 2, 1, 2], np.int32)
+    rn = np.array([5, 0, 3, 1], np.int32)
+    rows = oracle.decode_multi_rows(rb, ri, rn, c.qm, c.kc, c.vc, c.tables, c.ctx, c.scale,
+                                    lib=lib)
+    assert np.array_equal(rows, full[rb, ri, rn]), "sampled rows differ from the full result"
+    rng = np.random.default_rng(342)
+    finite = np.array([i for i in range(256) if (i & 0x7F) != 0x7F], np.uint8)
+    kc8 = rng.choice(finite, size=c.kc.shape).astype(np.uint8)
+    vc8 = rng.choice(finite, size=c.vc.shape).astype(np.uint8)
+    got = oracle.decode_multi(c.qm[:, :1], kc8, vc8, c.tables, c.ctx, c.scale, 0.5, 0.25,
+                              lib=lib)
+    ref = oracle.decode_fp8(np.ascontiguousarray(c.qm[:, 0]), kc8, vc8, c.tables, c.ctx,
+                            c.scale, 0.5, 0.25, lib=lib)
+    assert np.array_equal(got[:, 0], ref), "FP8 multi-query with Q = 1 differs from FP8 decode"
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -40,6 +40,12 @@ MUTANTS = {
     "fp8_scale_dropped": ("return oracle_e4m3_value(((const uint8_t *)pool)[index]) * scale;",
                           "return oracle_e4m3_value(((const uint8_t *)pool)[index]);"),
     "fp8_append_v_from_k": ("oracle_e4m3_quantize(v[src], v_inv);", "oracle_e4m3_quantize(k[src], v_inv);"),
+    "multi_top_left_mask": ("int v = ctx - Q + i + 1;", "int v = i + 1;"),
+    "multi_mask_off_by_one": ("int v = ctx - Q + i + 1;", "int v = ctx - Q + i;"),
+    "multi_query_layout": ("int b = r / (Q * N), i = (r / N) % Q, n = r % N;",
+                           "int b = r / (Q * N), i = r % Q, n = (r / Q) % N;"),
+    "multi_rows_query_layout": ("q + (((size_t)b * Q + i) * N + n) * H",
+                                "q + (((size_t)b * N + n) * Q + i) * H"),
 }
 
 
