@@ -34,6 +34,7 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "llama3_8b_b64_ctx8k"
 KERNEL_SOURCES = ["paged_kv_cache_100_amd/csrc/kernels/decode.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/decode_balanced.hpp",
+                  "paged_kv_cache_100_amd/csrc/kernels/decode_multi.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/kv_format.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/common.hpp",
                   "paged_kv_cache_100_amd/csrc/pagedkv.hip"]
@@ -53,10 +54,11 @@ def algorithmic_bytes(w, part: int) -> dict:
     elem = 1 if w.kv_dtype == "fp8" else 2
     ctx = [int(c) for c in w.context_lens.tolist()]
     kv = sum(ctx) * s.K * s.H * 2 * elem               # K and V pools
-    q = s.B * s.N * s.H * 2
-    out = s.B * s.N * s.H * 4
+    Q = s.queries
+    q = s.B * Q * s.N * s.H * 2
+    out = s.B * Q * s.N * s.H * 4
     tables = sum(-(-c // s.bs) for c in ctx) * 4 + s.B * 4
-    append = 2 * (s.B * s.K * s.H) * (2 + elem)        # read bf16 k, v; write them into the pools
+    append = 2 * (s.B * Q * s.K * s.H) * (2 + elem)    # read bf16 k, v; write them into the pools
     return {"kv": kv, "q": q, "out": out, "tables": tables, "attention": kv + q + out + tables,
             "append": append}
 
@@ -98,6 +100,9 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
 
     def decode(n):
+        if w.spec.queries > 1:
+            return oracle.decode_multi(q[:n], kc, vc, bt[:n], cl[:n], w.scale, w.k_scale,
+                                       w.v_scale)
         if fp8:
             return oracle.decode_fp8(q[:n], kc, vc, bt[:n], cl[:n], w.scale, w.k_scale,
                                      w.v_scale)
@@ -122,7 +127,7 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     kv_bytes = tokens * w.spec.K * w.spec.H * 2 * (1 if fp8 else 2)
     what = (f"the full batch of {B} sequences, {reps} times" if n == B
             else f"the first {n} of {B} sequences")
-    return {"value": n * reps / spent, "unit": "tokens/s per layer",
+    return {"value": n * w.spec.queries * reps / spent, "unit": "tokens/s per layer",
             "cores": oracle.num_threads(), "kind": "oracle", "kv_GBps": kv_bytes / spent / 1e9,
             "sample": f"{what} ({tokens} cached tokens attended), fp64 C oracle with OpenMP, "
                       f"{spent:.1f} s"}
@@ -167,12 +172,24 @@ def main() -> int:
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((s.B, s.N, s.H), dtype=torch.float32, device=dev)
 
+    multi = s.queries > 1
+    if multi:
+        out = torch.empty((s.B, s.queries, s.N, s.H), dtype=torch.float32, device=dev)
+        ws_bytes = pkv.mq_workspace_size(s.B, s.queries, s.N, s.H, mcl, part)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    if multi:
+        def attend():
+            pkv.paged_decode_attention_mq(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                          g.context_lens, w.scale, s.K, s.bs, part,
+                                          k_scale=w.k_scale, v_scale=w.v_scale,
+                                          max_context_len=mcl, workspace=workspace)
     if w.kv_dtype == "fp8":
         def append():
             pkv.paged_kv_append_fp8(g.k_new, g.v_new, g.slot_mapping, g.key_cache,
                                     g.value_cache, w.k_scale, w.v_scale)
 
-        def attend():
+        def attend_one():
             pkv.paged_decode_attention_fp8(out, g.q, g.key_cache, g.value_cache,
                                            g.block_tables, g.context_lens, w.scale, w.k_scale,
                                            w.v_scale, s.K, s.bs, max_context_len=mcl,
@@ -181,10 +198,13 @@ def main() -> int:
         def append():
             pkv.paged_kv_append(g.k_new, g.v_new, g.slot_mapping, g.key_cache, g.value_cache)
 
-        def attend():
+        def attend_one():
             pkv.paged_decode_attention(out, g.q, g.key_cache, g.value_cache, g.block_tables,
                                        g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
                                        partition=part, workspace=workspace)
+
+    if not multi:
+        attend = attend_one
 
     # Achievable bandwidth: plain 16-byte streaming read of 1 GiB, and a 1 GiB
     # copy (its known read and write sizes also scale the HBM byte counters
@@ -268,13 +288,13 @@ def main() -> int:
         "data": ("synthetic: seeded N(0,1) bf16 q/k/v, block tables from a seeded permutation"
                  + ("; K/V pools as E4M3 codes with per-pool scales" if w.kv_dtype == "fp8"
                     else "")),
-        "config": {"workload": args.workload, "kv_dtype": w.kv_dtype,
+        "config": {"workload": args.workload, "kv_dtype": w.kv_dtype, "queries": s.queries,
                    "B": s.B, "N": s.N, "K": s.K, "H": s.H,
                    "block_size": s.bs, "sum_context": int(w.context_lens.sum()),
                    "max_context": mcl, "partition": part, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "tokens_per_s_per_layer": round(s.B / (ms_per_step * 1e-3), 1),
-        "attention_tokens_per_s_per_layer": round(s.B / (attn_avg * 1e-3), 1),
+        "tokens_per_s_per_layer": round(s.B * s.queries / (ms_per_step * 1e-3), 1),
+        "attention_tokens_per_s_per_layer": round(s.B * s.queries / (attn_avg * 1e-3), 1),
         "attention_ms": round(attn_avg, 5),
         "append_call_ms": round(append_avg, 5),
         "step_ms_events": round(steps_event_ms / K, 5),

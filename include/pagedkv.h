@@ -78,6 +78,11 @@ typedef enum pkv_status {
 #define PKV_MAX_GROUP 16           /* largest N / K (query heads per KV head)     */
 #define PKV_PARTITION_GRAIN 32     /* partition sizes are multiples of this       */
 #define PKV_MAX_PARTITION 1024
+#define PKV_MAX_QUERY_ROWS 64      /* num_queries * (N / K) for the multi-query call */
+
+/* KV pool element types of paged_decode_attention_mq. */
+#define PKV_KV_BF16 0              /* bf16 bit patterns                           */
+#define PKV_KV_FP8_E4M3 1          /* OCP FP8 E4M3 codes, one scale per pool      */
 
 /*
  * paged_kv_append -- write one decode step's keys and values into the cache.
@@ -211,6 +216,50 @@ int paged_decode_attention_fp8(float *out, const void *q,
                                int32_t max_blocks_per_seq, int32_t max_context_len,
                                int64_t num_blocks, int32_t partition_size,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * paged_decode_attention_mq -- attention for num_queries (Q) query tokens per
+ * sequence: the Q tokens a speculative-decoding verification pass checks at
+ * once (the lesson's speculative-decoding section: the target model processes
+ * all draft tokens in one forward pass), appended to the cache beforehand
+ * with paged_kv_append / paged_kv_append_fp8 (Q slots per sequence) and
+ * counted in context_lens.
+ *
+ * Query token i (0 <= i < Q) of sequence b stands at position ctx_b - Q + i
+ * and attends positions 0 .. ctx_b - Q + i: the causal mask of the lesson's
+ * Build-It step 2 for seq_len_q > 1, an upper triangle anchored at the
+ * bottom-right corner ("Week 11. Inference" warns against the top-left
+ * alignment).  The result equals Q single-token decode steps.  A query that
+ * sees no position (ctx_b < Q - i) gets zeros.
+ *
+ *   out            [num_seqs][Q][num_heads][head_dim] float32 (written).
+ *   q              [num_seqs][Q][num_heads][head_dim] bf16.
+ *   kv_dtype       PKV_KV_BF16 (k_scale, v_scale ignored) or PKV_KV_FP8_E4M3
+ *                  (pools of E4M3 codes; scales as for the _fp8 calls).
+ *   num_queries    Q >= 1 with Q * (N / K) <= PKV_MAX_QUERY_ROWS.
+ *   partition_size fixed partitions only: a multiple of 32 in [32, 1024].
+ *   workspace      at least paged_decode_mq_workspace_size(num_seqs,
+ *                  num_queries, num_heads, head_dim, max_context_len,
+ *                  partition_size) bytes (0 when one partition covers
+ *                  max_context_len), 16-byte aligned.
+ * Other arguments, checks and clamping as for paged_decode_attention.  The
+ * Q * G (query token, head) pairs of a KV head's group share each load of
+ * its keys and values.
+ */
+size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t partition_size);
+
+int paged_decode_attention_mq(float *out, const void *q,
+                              const void *key_cache, const void *value_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              float scale, int32_t kv_dtype, float k_scale, float v_scale,
+                              int32_t num_kv_heads, int32_t block_size,
+                              int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                              int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, int64_t num_blocks,
+                              int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream);
 
 /*
  * pagedkv_stream_read -- measurement helper, not part of the method: reads

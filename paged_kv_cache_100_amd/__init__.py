@@ -13,6 +13,8 @@ computation runs in the library's HIP kernels.  The library must be built
     paged_decode_attention_fp8(out, q, key_cache, value_cache, block_tables,
                                context_lens, scale, k_scale, v_scale, num_kv_heads,
                                block_size)
+    paged_decode_attention_mq(out, q, key_cache, value_cache, block_tables,
+                              context_lens, scale, num_kv_heads, block_size, partition)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
 [num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
@@ -67,6 +69,11 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_attention_fp8.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32,
                                              i32, i32, i32, i64, i32, P, sz, P]
     L.paged_decode_attention_fp8.restype = ctypes.c_int
+    L.paged_decode_mq_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.paged_decode_mq_workspace_size.restype = sz
+    L.paged_decode_attention_mq.argtypes = [P, P, P, P, P, P, f32, i32, f32, f32, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, i64, i32, P, sz, P]
+    L.paged_decode_attention_mq.restype = ctypes.c_int
     L.pagedkv_stream_read_sink_bytes.argtypes = [sz]
     L.pagedkv_stream_read_sink_bytes.restype = sz
     L.pagedkv_stream_read.argtypes = [P, sz, P, P]
@@ -221,6 +228,60 @@ def paged_decode_attention_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: to
                               FP8_DTYPES)
     _check(lib().paged_decode_attention_fp8(*head, float(scale), float(k_scale), float(v_scale),
                                             *tail), "paged_decode_attention_fp8")
+    return out
+
+
+KV_BF16, KV_FP8_E4M3 = 0, 1
+
+
+def mq_workspace_size(num_seqs: int, num_queries: int, num_heads: int, head_dim: int,
+                      max_context_len: int, partition: int) -> int:
+    return int(lib().paged_decode_mq_workspace_size(num_seqs, num_queries, num_heads, head_dim,
+                                                    max_context_len, partition))
+
+
+def paged_decode_attention_mq(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                              value_cache: torch.Tensor, block_tables: torch.Tensor,
+                              context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                              block_size: int, partition: int, k_scale: float = 1.0,
+                              v_scale: float = 1.0, max_context_len: Optional[int] = None,
+                              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Q query tokens per sequence (q, out [B, Q, N, H]): token i of sequence b
+    attends positions 0 .. ctx_b - Q + i.  bf16 pools, or FP8 E4M3 pools
+    (uint8 / float8_e4m3fn) with ``k_scale``, ``v_scale``.  ``partition`` is
+    the fixed split size (a multiple of 32 in [32, 1024])."""
+    po = _dev(out, "out", torch.float32)
+    pq = _dev(q, "q", torch.bfloat16)
+    fp8 = key_cache.dtype in FP8_DTYPES
+    pool = FP8_DTYPES if fp8 else torch.bfloat16
+    pkc = _dev(key_cache, "key_cache", pool)
+    pvc = _dev(value_cache, "value_cache", pool)
+    pbt = _dev(block_tables, "block_tables", torch.int32)
+    pcl = _dev(context_lens, "context_lens", torch.int32)
+    if q.dim() != 4 or out.shape != q.shape:
+        raise ValueError("q and out must both be [B, Q, N, H]")
+    B, Q, N, H = q.shape
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be [num_blocks, K, block_size, H]")
+    nb, K, bs, H2 = key_cache.shape
+    if K != num_kv_heads or bs != block_size or H2 != H or value_cache.shape != (nb, K, H, bs):
+        raise ValueError("cache shapes disagree with num_kv_heads / block_size / head_dim")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    need = mq_workspace_size(B, Q, N, H, max_context_len, partition) if B else 0
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw, wbytes = 0, 0
+    if workspace is not None:
+        pw = _dev(workspace, "workspace", torch.uint8)
+        wbytes = workspace.numel()
+    _check(lib().paged_decode_attention_mq(
+        po, pq, pkc, pvc, pbt, pcl, float(scale), KV_FP8_E4M3 if fp8 else KV_BF16,
+        float(k_scale), float(v_scale), K, bs, B, Q, N, H, max_blocks, int(max_context_len),
+        nb, int(partition), pw, wbytes, _stream(q.device)), "paged_decode_attention_mq")
     return out
 
 

@@ -72,6 +72,9 @@ struct DecodeParams {
     int32_t max_ctx;
     int32_t part;                 // tokens per partition (multiple of 32)
     int32_t num_parts;            // P
+    int32_t num_queries;          // Q query tokens per sequence (1 for plain decode)
+    int32_t col_groups;           // multi-query: waves per (partition, KV head, sequence)
+    int32_t num_seqs;             // B (multi-query grid decoding)
     int64_t num_blocks;
 };
 
@@ -299,10 +302,11 @@ void decode_kernel(DecodeParams p)
 }
 
 struct MergeParams {
-    float *out;                   // [B][N][H]
-    const float *part_o;          // [B][N][P][H]
-    const float *part_ml;         // [B][N][P][2]
+    float *out;                   // [B][Q][N][H]
+    const float *part_o;          // [B][Q][N][P][H]
+    const float *part_ml;         // [B][Q][N][P][2]
     const int32_t *context_lens;  // [B]
+    int32_t num_queries;          // Q (1 for plain decode)
     int32_t num_heads;
     int32_t max_ctx;
     int32_t part;
@@ -332,11 +336,12 @@ __device__ __forceinline__ float block_reduce(float v, float *scratch)
     return v;
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head), one
-// workgroup each: the partition maxima and weighted sums are reduced across
-// the threads, then kMergeThreads / H groups of H threads each accumulate a
-// strided subset of the partitions' o vectors, combined through LDS.
-// Partition maxima are in log2 units.
+// Log-sum-exp merge of the partitions of one (sequence, query token, query
+// head) row, one workgroup each: the partition maxima and weighted sums are
+// reduced across the threads, then kMergeThreads / H groups of H threads each
+// accumulate a strided subset of the partitions' o vectors, combined through
+// LDS.  Partition maxima are in log2 units; a row that saw no position in any
+// partition (maximum -inf, sums 0) gets zeros.
 template <int H>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
 {
@@ -345,11 +350,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
     __shared__ float part_sum[kGroups][H];
 
     const int n = blockIdx.x;
-    const int b = blockIdx.y;
+    const int bq = blockIdx.y;                     // b * Q + query token
+    const int b = bq / p.num_queries;
     const int tid = threadIdx.x;
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
     const int parts = (ctx + p.part - 1) / p.part;
-    const int64_t row = (int64_t)b * p.num_heads + n;
+    const int64_t row = (int64_t)bq * p.num_heads + n;
     const float *ml = p.part_ml + row * p.num_parts * 2;
     const float *po = p.part_o + row * p.num_parts * H;
 
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
 #pragma unroll
         for (int g2 = 0; g2 < kGroups; ++g2)
             total += part_sum[g2][h];
-        p.out[row * H + h] = parts ? total / den : 0.f;
+        p.out[row * H + h] = (parts && den > 0.f) ? total / den : 0.f;
     }
 }
 

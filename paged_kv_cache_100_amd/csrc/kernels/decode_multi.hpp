@@ -1,0 +1,280 @@
+// Decode attention for several query tokens per sequence: the Q tokens of a
+// speculative-decoding verification pass (the lesson's speculative-decoding
+// section: the target model checks all draft tokens in one forward pass),
+// already appended to the cache like a single decode token.
+//
+// What is computed: query token i (0 <= i < Q) of sequence b sits at position
+// ctx - Q + i and, under the lesson's Build-It step 2 mask for seq_len_q > 1
+// (an upper triangle anchored at the bottom-right corner of the score
+// matrix), attends positions 0 .. ctx - Q + i -- what decoding the tokens one
+// after another would have computed.  A query that sees no position gets
+// zeros.  q and out are [B][Q][N][H].
+//
+// Work decomposition: as in decode.hpp, a wave per (partition, KV head,
+// sequence), but the columns of the matrix-core tiles are now the Q * G
+// (query token, query head) pairs of the KV head's group: column c = 16t + col
+// of tile t is query token c / G, head c % G.  A wave carries up to two tiles
+// (32 columns; its key and value registers serve both, and the accumulators
+// of a third tile would not fit next to the load ring).  With more than 32
+// columns the pairs are split into column groups of two tiles, one wave each;
+// the waves of one (partition, KV head, sequence) are placed on the same XCD
+// at consecutive dispatch slots (workgroups go to the eight XCDs round-robin),
+// so the second wave's reads of the same blocks are served by that XCD's L2.
+// Each tile column keeps its own running maximum and sum.
+//
+// Masking: a chunk entirely below the first query's limit (ctx - Q + 1)
+// needs none; the last one or two chunks of a sequence mask each score
+// against its own column's limit, zero value elements at or past ctx, and
+// keep an all-masked column's state finite (reference maximum 0 while the
+// column has seen no position).
+#pragma once
+
+#include "decode.hpp"
+
+namespace pkv {
+
+constexpr int kMaxQueryTiles = 4;   // Q * G <= 64
+constexpr int kTilesPerWave = 2;
+constexpr int kXcds = 8;            // MI355X: workgroups are dealt to 8 XCDs in turn
+
+// Chunk buffers per wave: a second tile's accumulators take ring space.
+template <class Fmt, int kTiles>
+constexpr int multi_ring_depth()
+{
+    return kTiles == 1 ? Fmt::kRing : (sizeof(typename Fmt::Elem) == 1 ? Fmt::kRing - 1 : 2);
+}
+
+// One 32-token chunk for kTiles column tiles.  tok0 is the position of this
+// lane's first token (chunk start + 8 * quad); column t of this lane sees
+// positions below lim[t]; vrem = ctx - chunk start (value elements at or
+// past it are zeroed).  qf(t, s) yields the lane's query operand.
+template <class Fmt, int H, int kTiles, bool kMasked, class QFrag>
+__device__ __forceinline__ void attend_chunk_multi(const typename Fmt::template Regs<H> &r,
+                                                   QFrag &&qf, int tok0,
+                                                   const int (&lim)[kTiles], int vrem, int quad,
+                                                   float scale_log2, float (&m)[kTiles],
+                                                   float (&l)[kTiles],
+                                                   f32x4 (&acc)[kTiles][H / 16])
+{
+    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
+    if (kMasked) {
+        const int valid = min(max(vrem - 8 * quad, 0), 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            vmask[w] = (2 * w < valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+    }
+    // One tile at a time (scores, softmax, P.V), so only one tile's P is live.
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s) {
+            const bf16x8 q = qf(t, s);
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 0, s), q, s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 1, s), q, s1, 0, 0, 0);
+        }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = s0[i] * scale_log2;
+            x[4 + i] = s1[i] * scale_log2;
+        }
+        if (kMasked) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (tok0 + e >= lim[t])
+                    x[e] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = max_over_rows(mx);
+        const float m_new = fmaxf(m[t], mx);
+        // A column that has seen no position yet keeps m = -inf; exponentials
+        // are then taken against 0 (all of them are 0).
+        const float m_ref = (kMasked && m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m[t] - m_ref);
+        bf16x8 p_hi, p_lo;
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(x[e] - m_ref);
+            psum += p;
+            const __bf16 hi = (__bf16)p;
+            p_hi[e] = hi;
+            p_lo[e] = (__bf16)(p - (float)hi);
+        }
+        l[t] = l[t] * alpha + psum;
+        m[t] = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                acc[t][c] *= alpha;
+        }
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c) {
+            const u32x4 vbits = Fmt::value(r, c);
+            const bf16x8 vv = as_bf16x8(kMasked ? (vbits & vmask) : vbits);
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, acc[t][c], 0, 0, 0);
+            acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, acc[t][c], 0, 0, 0);
+        }
+    }
+}
+
+// Grid: one dimension of kXcds * col_groups * ceil(items / kXcds) waves.
+// Workgroup id L -> XCD L % 8, slot j = L / 8 on it; column group j % CG of
+// item (j / CG) * 8 + L % 8; item = (b * K + kvh) * parts + partition.
+template <class Fmt, int H, int kTiles, bool kSplit>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_multi_kernel(DecodeParams p)
+{
+    const int L = blockIdx.x;
+    const int xcd = L % kXcds;
+    const int j = L / kXcds;
+    const int cg = j % p.col_groups;
+    const int64_t item = (int64_t)(j / p.col_groups) * kXcds + xcd;
+    if (item >= (int64_t)p.num_parts * p.num_kv_heads * p.num_seqs)
+        return;
+    const int part_idx = (int)(item % p.num_parts);
+    const int kvh = (int)((item / p.num_parts) % p.num_kv_heads);
+    const int b = (int)(item / ((int64_t)p.num_parts * p.num_kv_heads));
+    const int lane = threadIdx.x;
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+    const int Q = p.num_queries;
+    const int G = p.group;
+
+    const int start = part_idx * p.part;
+    const int first_block = start / kBlockSize;
+    const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks + first_block;
+    const int table_avail = min(p.part / kBlockSize, p.max_blocks - first_block);
+    int my_id = 0;
+    if (lane < table_avail)
+        my_id = table[lane];
+
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+
+    // Column t of this lane: query token i, head g; its output row in
+    // [B][Q][N] and the positions it sees.
+    bool live[kTiles];
+    int lim[kTiles];
+    int64_t orow[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const int c = 16 * (kTilesPerWave * cg + t) + col;
+        live[t] = c < Q * G;
+        const int i = live[t] ? c / G : 0;
+        const int g = live[t] ? c - (c / G) * G : 0;
+        orow[t] = ((int64_t)b * Q + i) * p.num_heads + kvh * G + g;
+        lim[t] = live[t] ? ctx - Q + i + 1 : ctx;
+    }
+
+    if (start >= ctx) {
+        if (!kSplit && part_idx == 0) {   // empty sequence: zeros
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) {
+                if (!live[t])
+                    continue;
+                float *o = p.out + orow[t] * H;
+#pragma unroll
+                for (int c = 0; c < H / 16; ++c)
+                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        return;
+    }
+    const int end = min(start + p.part, ctx);
+    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
+    my_id = clamp_block(my_id, p.num_blocks);
+
+    // The query fragments live in this wave's LDS (each lane reads back only
+    // what it wrote): registers go to the accumulators and the chunk ring.
+    __shared__ u32x4 q_lds[kTiles * (H / 32) * kWave];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const uint16_t *qrow = p.q + orow[t] * H;
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s) {
+            u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
+            if (!live[t])
+                raw = u32x4{0u, 0u, 0u, 0u};
+            q_lds[(t * (H / 32) + s) * kWave + lane] = raw;
+        }
+    }
+
+    const int64_t tile_elems = (int64_t)kBlockSize * H;
+    const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
+    using Elem = typename Fmt::Elem;
+    using Regs = typename Fmt::template Regs<H>;
+    const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
+    const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
+
+    auto issue = [&](Regs &r, int ci) {
+        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
+        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
+                                                : id0;
+        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
+                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+    };
+
+    float m[kTiles], l[kTiles];
+    f32x4 acc[kTiles][H / 16];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        m[t] = -INFINITY;
+        l[t] = 0.f;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // Chunks wholly below the first query's limit need no mask.
+    const int n_chunks = (end - start + kChunk - 1) / kChunk;
+    const int lim_min = ctx - Q + 1;
+    const int n_plain = lim_min > start ? min((lim_min - start) / kChunk, n_chunks) : 0;
+    auto attend = [&](const Regs &r, int ci) {
+        // An index the compiler cannot see through, so that the LDS reads stay
+        // inside the loop instead of being hoisted back into registers.
+        int opaque = lane;
+        asm volatile("" : "+v"(opaque));
+        auto qfrag = [&](int t, int s) {
+            return as_bf16x8(q_lds[(t * (H / 32) + s) * kWave + opaque]);
+        };
+        const int c0 = start + kChunk * ci;
+        if (ci < n_plain)
+            attend_chunk_multi<Fmt, H, kTiles, false>(r, qfrag, c0 + 8 * quad, lim, ctx - c0,
+                                                      quad, p.scale_log2, m, l, acc);
+        else
+            attend_chunk_multi<Fmt, H, kTiles, true>(r, qfrag, c0 + 8 * quad, lim, ctx - c0,
+                                                     quad, p.scale_log2, m, l, acc);
+    };
+
+    constexpr int kRing = multi_ring_depth<Fmt, kTiles>();
+    Regs ring[kRing];
+    run_ring<kRing>(n_chunks, ring, issue, attend);
+
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const float lt = sum_over_rows(l[t]);
+        if (!live[t])
+            continue;
+        if (!kSplit) {
+            const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
+            float *o = p.out + orow[t] * H;
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * inv;
+        } else {
+            const int64_t slot = orow[t] * p.num_parts + part_idx;
+            float *o = p.part_o + slot * H;
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * p.out_scale;
+            if (quad == 0) {
+                p.part_ml[2 * slot] = m[t];
+                p.part_ml[2 * slot + 1] = lt;
+            }
+        }
+    }
+}
+
+}  // namespace pkv

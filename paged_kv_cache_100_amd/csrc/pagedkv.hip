@@ -10,12 +10,13 @@
 #include "kernels/append.hpp"
 #include "kernels/decode.hpp"
 #include "kernels/decode_balanced.hpp"
+#include "kernels/decode_multi.hpp"
 #include "kernels/stream_read.hpp"
 
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 1;
+constexpr int kVersionMinor = 2;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
@@ -214,6 +215,9 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.max_ctx = max_context_len;
     p.part = partition_size;
     p.num_parts = 1;
+    p.num_queries = 1;
+    p.col_groups = 1;
+    p.num_seqs = num_seqs;
     p.num_blocks = num_blocks;
 
     if (partition_size == 0) {
@@ -293,6 +297,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     mp.part_o = p.part_o;
     mp.part_ml = p.part_ml;
     mp.context_lens = context_lens;
+    mp.num_queries = 1;
     mp.num_heads = num_heads;
     mp.max_ctx = max_context_len;
     mp.part = part;
@@ -301,6 +306,67 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
                                      : (const void *)pkv::merge_kernel<64>;
     return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads), &mp,
                   stream);
+}
+
+// Multi-query decode: kernel for a head dim, tiles per wave (1 or 2) and split.
+template <class Fmt, int H>
+const void *multi_kernel(int tiles, bool split)
+{
+    if (tiles == 1)
+        return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 1, true>
+                     : (const void *)pkv::decode_multi_kernel<Fmt, H, 1, false>;
+    return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 2, true>
+                 : (const void *)pkv::decode_multi_kernel<Fmt, H, 2, false>;
+}
+
+template <class Fmt>
+int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_queries,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t max_context_len,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int32_t part = p.part;
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
+    const bool split = parts > 1;
+    if (split) {
+        const size_t need = fixed_workspace_bytes(num_seqs * num_queries, num_heads, head_dim,
+                                                  max_context_len, part);
+        if (!workspace || workspace_bytes < need)
+            return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace))
+            return PKV_ERR_ALIGN;
+        const int64_t rows = (int64_t)num_seqs * num_queries * num_heads * parts;
+        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+        p.part_o = static_cast<float *>(workspace);
+        p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    p.num_parts = (int32_t)parts;
+    const int tiles = (int)ceil_div((int64_t)num_queries * (num_heads / num_kv_heads), 16);
+    p.col_groups = (int32_t)ceil_div(tiles, pkv::kTilesPerWave);
+    p.num_seqs = num_seqs;
+    const int per_wave = tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
+    const void *kern = head_dim == 128 ? multi_kernel<Fmt, 128>(per_wave, split)
+                                       : multi_kernel<Fmt, 64>(per_wave, split);
+    const int64_t items = parts * num_kv_heads * num_seqs;
+    const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * p.col_groups;
+    if (waves > INT32_MAX)
+        return PKV_ERR_SHAPE;
+    int rc = launch(kern, dim3((unsigned)waves), dim3(pkv::kWave), &p, stream);
+    if (rc != PKV_OK || !split)
+        return rc;
+    pkv::MergeParams mp;
+    mp.out = p.out;
+    mp.part_o = p.part_o;
+    mp.part_ml = p.part_ml;
+    mp.context_lens = p.context_lens;
+    mp.num_queries = num_queries;
+    mp.num_heads = num_heads;
+    mp.max_ctx = max_context_len;
+    mp.part = part;
+    mp.num_parts = (int32_t)parts;
+    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
+                                     : (const void *)pkv::merge_kernel<64>;
+    return launch(mk, dim3((unsigned)num_heads, (unsigned)(num_seqs * num_queries)),
+                  dim3(pkv::kMergeThreads), &mp, stream);
 }
 
 }  // namespace
@@ -417,6 +483,100 @@ int paged_decode_attention_fp8(float *out, const void *q, const void *key_cache,
                                    scale, k_scale, v_scale, num_kv_heads, block_size, num_seqs,
                                    num_heads, head_dim, max_blocks_per_seq, max_context_len,
                                    num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t partition_size)
+{
+    if (num_seqs <= 0 || num_queries <= 0 || num_heads <= 0 || head_dim <= 0 ||
+        max_context_len <= 0 || partition_size <= 0)
+        return 0;
+    return fixed_workspace_bytes((int32_t)((int64_t)num_seqs * num_queries > INT32_MAX
+                                               ? INT32_MAX
+                                               : (int64_t)num_seqs * num_queries),
+                                 num_heads, head_dim, max_context_len, partition_size);
+}
+
+int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
+                              const void *value_cache, const int32_t *block_tables,
+                              const int32_t *context_lens, float scale, int32_t kv_dtype,
+                              float k_scale, float v_scale, int32_t num_kv_heads,
+                              int32_t block_size, int32_t num_seqs, int32_t num_queries,
+                              int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, int64_t num_blocks,
+                              int32_t partition_size, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    if (num_seqs < 0 || num_queries <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks < 0)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
+        return PKV_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_heads % num_kv_heads != 0)
+        return PKV_ERR_SHAPE;
+    if ((int64_t)num_queries * (num_heads / num_kv_heads) > PKV_MAX_QUERY_ROWS)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return PKV_ERR_SHAPE;
+    if ((int64_t)num_seqs * num_queries > 65535 || num_kv_heads > 65535)
+        return PKV_ERR_SHAPE;
+    if (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_PARTITION ||
+        partition_size % PKV_PARTITION_GRAIN != 0)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype == PKV_KV_BF16) {
+        k_scale = 1.0f;
+        v_scale = 1.0f;
+    } else if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale)) {
+        return PKV_ERR_SHAPE;
+    }
+    if (!isfinite(scale) || !isfinite(scale * k_scale))
+        return PKV_ERR_SHAPE;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!out || !q || !block_tables || !context_lens)
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && (!key_cache || !value_cache))
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && num_blocks == 0)
+        return PKV_ERR_SHAPE;
+    if (!aligned16(out) || !aligned16(q) || (key_cache && !aligned16(key_cache)) ||
+        (value_cache && !aligned16(value_cache)) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return PKV_ERR_ALIGN;
+
+    pkv::DecodeParams p;
+    p.out = out;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
+    p.q = static_cast<const uint16_t *>(q);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.out_scale = v_scale;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.max_ctx = max_context_len;
+    p.part = partition_size;
+    p.num_parts = 1;
+    p.num_queries = num_queries;
+    p.col_groups = 1;
+    p.num_seqs = num_seqs;
+    p.num_blocks = num_blocks;
+    if (kv_dtype == PKV_KV_FP8_E4M3)
+        return decode_mq_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_queries, num_heads,
+                                            num_kv_heads, max_context_len, workspace,
+                                            workspace_bytes, stream);
+    return decode_mq_launch<pkv::KvBf16>(p, head_dim, num_seqs, num_queries, num_heads,
+                                         num_kv_heads, max_context_len, workspace,
+                                         workspace_bytes, stream);
 }
 
 size_t pagedkv_stream_read_sink_bytes(size_t bytes)

@@ -19,10 +19,13 @@ dim):
     example of "Week 11. Inference", step 2), and at 128K context.
 Pages of 16 tokens follow the PagedAttention section of the same lesson.
 
-Layouts: key_cache [num_blocks][K][bs][H], value_cache [num_blocks][K][H][bs],
-both bf16; block_tables [B][max_blocks] int32; context_lens [B] int32 (the new
-token included); slot_mapping [B] int64 = block * bs + offset of position
-context_len - 1.
+Layouts: key_cache [num_blocks][K][bs][H], value_cache [num_blocks][K][H][bs]
+(bf16, or uint8 E4M3 codes for FP8 pools); block_tables [B][max_blocks] int32;
+context_lens [B] int32 (the step's new tokens included); slot_mapping = block *
+bs + offset of each new token's position.  A step appends one token per
+sequence (position context_len - 1), or Q tokens for the speculative-verify
+workloads (positions context_len - Q .. context_len - 1, whose queries are then
+attended together: q [B][Q][N][H], k_new / v_new [B * Q][K][H]).
 
 Poisoning (``poison=True``): cache slots that hold no valid token (block
 tails, and the new token's slot before the append) are bf16 NaN (0x7FC0), and
@@ -74,9 +77,10 @@ class Spec:
     partition_size: int = 0               # 0: the library chooses
     seed: int = 0
     kv_dtype: str = "bf16"                # "bf16" or "fp8" (E4M3 codes, one scale per pool)
+    queries: int = 1                      # Q query tokens per sequence (speculative verify)
 
 
-# The five workloads (seed = 1000 + index).
+# The workloads (seed = 1000 + index).
 SPECS = {
     "tiny": Spec("tiny", B=4, N=8, K=2, H=64, bs=16, ctx="uniform", ctx_lo=1,
                  ctx_hi=256, max_blocks=16, pool_blocks=128, seed=1001),
@@ -94,6 +98,13 @@ SPECS = {
                                    shared_prefix=1000, sharers=20, seed=1004),
     "llama3_70b_long_b4_ctx128k": Spec("llama3_70b_long_b4_ctx128k", B=4, N=64, K=8, H=128,
                                        bs=16, ctx=131072, partition_size=512, seed=1005),
+    # Speculative verification: gamma draft tokens plus one, all queried at once.
+    "llama3_8b_b64_ctx8k_spec4": Spec("llama3_8b_b64_ctx8k_spec4", B=64, N=32, K=8, H=128,
+                                      bs=16, ctx=8192, queries=4, partition_size=1024,
+                                      seed=1006),
+    "llama3_70b_b64_ctx4k_spec6": Spec("llama3_70b_b64_ctx4k_spec6", B=64, N=64, K=8, H=128,
+                                       bs=16, ctx=4096, queries=6, partition_size=512,
+                                       seed=1007),
 }
 # The same draws in FP8 pools.
 for _name in ("tiny", "llama3_8b_b64_ctx8k", "llama3_70b_ragged_b100"):
@@ -103,10 +114,10 @@ for _name in ("tiny", "llama3_8b_b64_ctx8k", "llama3_70b_ragged_b100"):
 @dataclasses.dataclass
 class Workload:
     spec: Spec
-    q: torch.Tensor              # [B, N, H] bf16
-    k_new: torch.Tensor          # [B, K, H] bf16
-    v_new: torch.Tensor          # [B, K, H] bf16
-    slot_mapping: torch.Tensor   # [B] int64
+    q: torch.Tensor              # [B, N, H] bf16 ([B, Q, N, H] with Q > 1 queries)
+    k_new: torch.Tensor          # [B * Q, K, H] bf16
+    v_new: torch.Tensor          # [B * Q, K, H] bf16
+    slot_mapping: torch.Tensor   # [B * Q] int64
     key_cache: torch.Tensor      # [nb, K, bs, H] bf16 or uint8 codes (state before the append)
     value_cache: torch.Tensor    # [nb, K, H, bs] bf16 or uint8 codes
     block_tables: torch.Tensor   # [B, max_blocks] int32
@@ -233,10 +244,14 @@ def _layout(spec: Spec, gen: torch.Generator, poison: bool) -> Layout:
         if sharer_ids and b == sharer_ids[0]:
             shared_ids = tables[b, :n_shared].tolist()
 
-    slots = torch.empty(B, dtype=torch.int64)
+    # The step's new tokens: positions ctx - Q .. ctx - 1 of each sequence
+    # (token-major within a sequence); a position below 0 gets slot -1.
+    Q = spec.queries
+    slots = torch.empty(B * Q, dtype=torch.int64)
     for b in range(B):
-        last = ctx[b] - 1
-        slots[b] = int(tables[b, last // bs]) * bs + last % bs if ctx[b] > 0 else -1
+        for i in range(Q):
+            pos = ctx[b] - Q + i
+            slots[b * Q + i] = int(tables[b, pos // bs]) * bs + pos % bs if pos >= 0 else -1
     return Layout(spec=spec, context_lens=ctx, blocks_per_seq=nblk, block_tables=tables,
                   slot_mapping=slots, num_blocks=pool + (1 if need_poison else 0),
                   sharer_ids=sharer_ids, shared_blocks=shared_ids, poison_block=poison_block)
@@ -256,9 +271,10 @@ def make(spec_or_name, poison: bool = True) -> Workload:
     lay = _layout(spec, gen, poison)
     B, N, K, H, bs = spec.B, spec.N, spec.K, spec.H, spec.bs
 
-    q = _randn_bf16((B, N, H), gen)
-    k_new = _randn_bf16((B, K, H), gen, spec.key_scale)
-    v_new = _randn_bf16((B, K, H), gen)
+    Q = spec.queries
+    q = _randn_bf16((B, N, H) if Q == 1 else (B, Q, N, H), gen)
+    k_new = _randn_bf16((B * Q, K, H), gen, spec.key_scale)
+    v_new = _randn_bf16((B * Q, K, H), gen)
     prefix_k = prefix_v = None
     if lay.sharer_ids:
         prefix_k = _randn_bf16((spec.shared_prefix, K, H), gen, spec.key_scale)
@@ -289,7 +305,7 @@ def make(spec_or_name, poison: bool = True) -> Workload:
             lv[:spec.shared_prefix] = prefix_v
         # Only positions [0, ctx-1) are in the cache before this step's append;
         # the new token's slot and the block tail hold the fill pattern.
-        valid = max(lay.context_lens[b] - 1, 0)
+        valid = max(lay.context_lens[b] - Q, 0)
         lk[valid:].view(torch.int16).fill_(fill_bits)
         lv[valid:].view(torch.int16).fill_(fill_bits)
         if fp8:
@@ -322,6 +338,8 @@ def small(name: str, **overrides) -> Spec:
                                        ctx_hi=1500, max_blocks=96, shared_prefix=200,
                                        sharers=4),
         "llama3_70b_long_b4_ctx128k": dict(B=2, ctx=[2600, 1537]),
+        "llama3_8b_b64_ctx8k_spec4": dict(B=3, ctx=[700, 1040, 5]),
+        "llama3_70b_b64_ctx4k_spec6": dict(B=3, ctx=[600, 1039, 6]),
         "tiny": dict(),
     }[key]
     defaults.update(overrides)

@@ -139,3 +139,32 @@ class Timer:
 
     def __exit__(self, *a):
         log(f"  {self.what}: {time.time() - self.t:.1f}s")
+
+
+# ----------------------------------------------------------- multi-query ----
+
+def gpu_decode_mq(out, g, w, partition: int, max_context_len=None):
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    pkv.paged_decode_attention_mq(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                  g.context_lens, w.scale, w.spec.K, w.spec.bs, partition,
+                                  k_scale=w.k_scale, v_scale=w.v_scale, max_context_len=mcl)
+    return out
+
+
+def gpu_step_mq(w, partition: int, device: str = "cuda:0"):
+    """Append the B * Q new tokens, then the multi-query decode, on the GPU."""
+    g = w.to(device)
+    gpu_append(g, w)
+    out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=device)
+    gpu_decode_mq(out, g, w, partition)
+    torch.cuda.synchronize()
+    return out.cpu(), g
+
+
+def oracle_step_mq(w):
+    inp = oracle_inputs(w)
+    oracle_append(w, inp)
+    ref = oracle.decode_multi(inp["q"], inp["key_cache"], inp["value_cache"],
+                              inp["block_tables"], inp["context_lens"], w.scale, w.k_scale,
+                              w.v_scale)
+    return ref, inp

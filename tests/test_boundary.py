@@ -33,6 +33,7 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
             "paged_kv_append_fp8", "paged_decode_attention_fp8",
+            "paged_decode_attention_mq", "paged_decode_mq_workspace_size",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
             "pagedkv_stream_copy"} <= set(names)
@@ -44,7 +45,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.1"
+    assert pkv.version() == "1.2"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -126,6 +127,35 @@ def test_decode_fp8_checks(L):
     for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-45):
         assert decode_fp8(L, ks=bad) == SHAPE
         assert decode_fp8(L, vs=bad) == SHAPE
+
+
+def decode_mq(L, out=A, q=A, kc=A, vc=A, bt=A, cl=A, scale=0.125, dt=0, ks=1.0, vs=1.0, K=2,
+              bs=16, B=4, Q=3, N=8, H=64, maxblk=16, maxctx=256, nb=128, part=64, ws=A,
+              wsb=1 << 30):
+    return L.paged_decode_attention_mq(out, q, kc, vc, bt, cl, scale, dt, ks, vs, K, bs, B, Q,
+                                       N, H, maxblk, maxctx, nb, part, ws, wsb, None)
+
+
+def test_decode_mq_checks(L):
+    assert decode_mq(L, B=0) == OK
+    assert decode_mq(L, out=0) == NULL
+    assert decode_mq(L, Q=0) == SHAPE
+    assert decode_mq(L, dt=2) == UNSUP                     # unknown pool type
+    assert decode_mq(L, Q=17, N=8, K=2) == UNSUP           # 17 * 4 rows > 64
+    assert decode_mq(L, Q=16, N=8, K=2) != UNSUP           # 64 rows: allowed
+    assert decode_mq(L, part=0) == SHAPE                   # fixed partitions only
+    assert decode_mq(L, part=48) == SHAPE
+    assert decode_mq(L, H=96) == UNSUP
+    assert decode_mq(L, maxctx=257) == SHAPE
+    assert decode_mq(L, B=40000, Q=2) == SHAPE             # B * Q rows of the merge grid
+    assert decode_mq(L, dt=1, ks=0.0) == SHAPE             # FP8 pools need valid scales
+    assert decode_mq(L, dt=0, ks=0.0) != SHAPE             # ... bf16 pools ignore them
+    assert decode_mq(L, ws=0) == WS
+    assert decode_mq(L, q=MIS) == ALIGN
+    # one partition covers the context: no workspace needed
+    assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 256) == 0
+    rows = 4 * 3 * 8 * 4
+    assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 64) == rows * 64 * 4 + rows * 8
 
 
 def test_workspace_sizes(L):

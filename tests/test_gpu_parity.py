@@ -28,7 +28,8 @@ def run_case(spec, partition=0, what=None):
     return w, out, ref
 
 
-@pytest.mark.parametrize("name", sorted(W.SPECS))
+# Single-query workloads; the speculative-verify ones are in test_gpu_multi.py.
+@pytest.mark.parametrize("name", sorted(n for n, sp in W.SPECS.items() if sp.queries == 1))
 def test_workload_small_variant(name):
     spec = W.small(name)
     run_case(spec, partition=spec.partition_size)

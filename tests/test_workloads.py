@@ -72,14 +72,21 @@ def test_deterministic_and_layout_matches_make():
 def test_small_variants(name):
     w = W.make(W.small(name))
     s = w.spec
-    assert w.q.shape == (s.B, s.N, s.H) and w.q.dtype == torch.bfloat16
+    Q = s.queries
+    qshape = (s.B, s.N, s.H) if Q == 1 else (s.B, Q, s.N, s.H)
+    assert w.q.shape == qshape and w.q.dtype == torch.bfloat16
+    assert w.k_new.shape == (s.B * Q, s.K, s.H) == w.v_new.shape
     assert w.key_cache.shape == (w.num_blocks, s.K, s.bs, s.H)
     assert w.value_cache.shape == (w.num_blocks, s.K, s.H, s.bs)
     ctx = w.context_lens.tolist()
     for b in range(s.B):
-        last = ctx[b] - 1
-        slot = int(w.slot_mapping[b])
-        assert slot // s.bs == int(w.block_tables[b, last // s.bs]) and slot % s.bs == last % s.bs
+        for i in range(Q):                # the new tokens: positions ctx - Q .. ctx - 1
+            pos = ctx[b] - Q + i
+            slot = int(w.slot_mapping[b * Q + i])
+            if pos < 0:
+                assert slot == -1
+                continue
+            assert slot // s.bs == int(w.block_tables[b, pos // s.bs]) and slot % s.bs == pos % s.bs
 
 
 def test_poison_marks_every_unused_slot():
