@@ -103,7 +103,7 @@ SPECS = {
                                       bs=16, ctx=8192, queries=4, partition_size=1024,
                                       seed=1006),
     "llama3_70b_b64_ctx4k_spec6": Spec("llama3_70b_b64_ctx4k_spec6", B=64, N=64, K=8, H=128,
-                                       bs=16, ctx=4096, queries=6, partition_size=512,
+                                       bs=16, ctx=4096, queries=6, partition_size=1024,
                                        seed=1007),
 }
 # The same draws in FP8 pools.
