@@ -80,6 +80,8 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_decode_multi_rows.argtypes = [P, P, P, P, i32, P, P, P, i32, f32, f32, P, P, f32,
                                              i32, i32, i32, i32, i32, i32, i32, i64, P, i32]
     lib.oracle_decode_multi_rows.restype = i32
+    lib.oracle_copy_blocks.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64]
+    lib.oracle_copy_blocks.restype = i32
     return lib
 
 
@@ -346,3 +348,26 @@ def decode_multi_rows(rows_b, rows_i, rows_n, q, key_cache, value_cache, block_t
     if rc:
         raise ValueError("invalid decode arguments (row, block id, shape or context)")
     return out
+
+
+# ------------------------------------------------------- block copy ----
+
+def copy_blocks(key_cache, value_cache, src, dst, lib=None) -> None:
+    """Copy whole physical blocks src[i] -> dst[i] (all heads, both pools), in
+    place and in pair order; bf16 (uint16) or E4M3 (uint8) pools."""
+    if not (key_cache.flags.c_contiguous and value_cache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous (written in place)")
+    if key_cache.dtype != value_cache.dtype or key_cache.dtype not in (np.uint16, np.uint8):
+        raise TypeError("pools must both be uint16 (bf16 bits) or uint8 (E4M3 codes)")
+    nb, K, bs, H = key_cache.shape
+    if value_cache.shape != (nb, K, H, bs):
+        raise ValueError("shape mismatch")
+    src = _as(src, np.int32)
+    dst = _as(dst, np.int32)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst differ in length")
+    rc = (lib or _load()).oracle_copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(src), _ptr(dst), src.shape[0], K, H, bs,
+        key_cache.dtype.itemsize, nb)
+    if rc:
+        raise ValueError("block id outside the pool")

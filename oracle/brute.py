@@ -106,3 +106,14 @@ def paged_decode_multi(q, key_cache, value_cache, block_tables, context_lens, sc
             rows_b.append(rows_r)
         out.append(rows_b)
     return out
+
+
+def copy_blocks(key_cache, value_cache, src, dst):
+    """Copy-on-write split: block dst[i] becomes a copy of block src[i] (every
+    head, offset and dim of both pools); pairs in order, negative ids skipped.
+    Caches are nested lists, modified in place."""
+    for a, b in zip(src, dst):
+        if a < 0 or b < 0:
+            continue
+        key_cache[b] = [[list(row) for row in head] for head in key_cache[a]]
+        value_cache[b] = [[list(row) for row in head] for head in value_cache[a]]

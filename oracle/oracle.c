@@ -166,6 +166,39 @@ int oracle_append(const uint16_t *k, const uint16_t *v, const int64_t *slot_mapp
 }
 
 /*
+ * Copy-on-write block split ("CS336 Lecture 10: Inference", part 6: blocks
+ * shared by several sequences are copied when one of them must write into
+ * its own version): for each pair i, every element of physical block
+ * src[i] -- all KV heads, all offsets, all dims, in both pools -- is copied
+ * bit for bit to block dst[i].  The pools hold elem_bytes bytes per element
+ * (2 for bf16, 1 for E4M3 codes); they are handled as raw bytes.  Pairs are
+ * applied in order; a negative src or dst skips the pair.
+ */
+int oracle_copy_blocks(uint8_t *key_cache, uint8_t *value_cache, const int32_t *src,
+                       const int32_t *dst, int n, int K, int H, int bs, int elem_bytes,
+                       int64_t num_blocks)
+{
+    for (int i = 0; i < n; i++) {
+        if (src[i] < 0 || dst[i] < 0)
+            continue;
+        if (src[i] >= num_blocks || dst[i] >= num_blocks)
+            return -1;
+        for (int g = 0; g < K; g++)
+            for (int o = 0; o < bs; o++)
+                for (int h = 0; h < H; h++)
+                    for (int e = 0; e < elem_bytes; e++) {
+                        size_t ks = key_index(src[i], g, o, h, K, bs, H) * elem_bytes + e;
+                        size_t kd = key_index(dst[i], g, o, h, K, bs, H) * elem_bytes + e;
+                        size_t vs = value_index(src[i], g, h, o, K, bs, H) * elem_bytes + e;
+                        size_t vd = value_index(dst[i], g, h, o, K, bs, H) * elem_bytes + e;
+                        key_cache[kd] = key_cache[ks];
+                        value_cache[vd] = value_cache[vs];
+                    }
+    }
+    return 0;
+}
+
+/*
  * Append into FP8 pools: the same scatter, storing each value's quantised code
  * (see the header comment).  k_inv / v_inv are the fp32 inverse scales.
  */

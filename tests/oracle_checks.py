@@ -513,4 +513,56 @@ def check_multi_rows_and_fp8(lib):
     assert np.array_equal(got[:, 0], ref), "FP8 multi-query with Q = 1 differs from FP8 decode"
 
 
+# ------------------------------------------------------------ block copy ----
+
+def check_copy_blocks_brute_force(lib):
+    rng = np.random.default_rng(401)
+    nb, K, bs, H = 7, 2, 4, 3
+    for dtype in (np.uint16, np.uint8):
+        kc = rng.integers(0, np.iinfo(dtype).max, (nb, K, bs, H)).astype(dtype)
+        vc = rng.integers(0, np.iinfo(dtype).max, (nb, K, H, bs)).astype(dtype)
+        src = np.array([1, 4, -1, 2, 5], np.int32)
+        dst = np.array([3, 0, 6, 1, 5], np.int32)     # 1 is copied out before it is overwritten
+        kl, vl = kc.tolist(), vc.tolist()
+        brute.copy_blocks(kl, vl, src.tolist(), dst.tolist())
+        oracle.copy_blocks(kc, vc, src, dst, lib=lib)
+        assert np.array_equal(kc, np.array(kl, dtype)), f"key pool copy ({dtype.__name__})"
+        assert np.array_equal(vc, np.array(vl, dtype)), f"value pool copy ({dtype.__name__})"
+
+
+def check_copy_on_write_divergence(lib):
+    """Two sequences share a partly filled block; before the second writes its
+    next token there, the block is copied and its table re-pointed.  Then the
+    first sequence's result is unchanged, and the second's equals what private
+    blocks holding the same values give."""
+    c = Case(411, B=2, N=4, K=2, H=8, bs=4, ctx=[6, 6])
+    kc, vc = c.kc.copy(), c.vc.copy()
+    shared = c.tables[0, :2].copy()
+    tables = c.tables.copy()
+    tables[1, :2] = shared                       # both point at the same two blocks
+    ctx = np.array([6, 6], np.int32)
+    before0 = oracle.decode(c.q, kc, vc, tables, ctx, c.scale, lib=lib)[0]
+    fresh = int(c.num_blocks - 1)                # a spare block no table uses
+    oracle.copy_blocks(kc, vc, np.array([shared[1]], np.int32), np.array([fresh], np.int32),
+                       lib=lib)
+    tables[1, 1] = fresh
+    rng = np.random.default_rng(412)
+    k_new = to_bf16_bits(rng.standard_normal((1, c.K, c.H)))
+    v_new = to_bf16_bits(rng.standard_normal((1, c.K, c.H)))
+    oracle.append(k_new, v_new, np.array([fresh * c.bs + 2], np.int64), kc, vc, lib=lib)
+    ctx2 = np.array([6, 7], np.int32)
+    after = oracle.decode(c.q, kc, vc, tables, ctx2, c.scale, lib=lib)
+    assert np.array_equal(after[0], before0), "the other sharer's result changed"
+    # reference: private copies of both blocks for sequence 1, new token written there
+    kp, vp = c.kc.copy(), c.vc.copy()
+    priv = np.array([c.num_blocks - 2, c.num_blocks - 1], np.int32)
+    kp[priv] = kp[shared]
+    vp[priv] = vp[shared]
+    oracle.append(k_new, v_new, np.array([priv[1] * c.bs + 2], np.int64), kp, vp, lib=lib)
+    t2 = tables.copy()
+    t2[1, :2] = priv
+    ref = oracle.decode(c.q, kp, vp, t2, ctx2, c.scale, lib=lib)
+    assert np.array_equal(after[1], ref[1]), "diverged sharer differs from private copies"
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

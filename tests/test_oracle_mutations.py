@@ -46,6 +46,10 @@ MUTANTS = {
                            "int b = r / (Q * N), i = r % Q, n = (r / Q) % N;"),
     "multi_rows_query_layout": ("q + (((size_t)b * Q + i) * N + n) * H",
                                 "q + (((size_t)b * N + n) * Q + i) * H"),
+    "copy_value_from_key": ("value_cache[vd] = value_cache[vs];", "value_cache[vd] = key_cache[ks];"),
+    "copy_one_head": ("for (int g = 0; g < K; g++)\n            for (int o = 0; o < bs; o++)",
+                      "for (int g = 0; g < 1; g++)\n            for (int o = 0; o < bs; o++)"),
+    "copy_low_bytes_only": ("for (int e = 0; e < elem_bytes; e++) {", "for (int e = 0; e < 1; e++) {"),
 }
 
 
