@@ -79,6 +79,7 @@ typedef enum pkv_status {
 #define PKV_PARTITION_GRAIN 32     /* partition sizes are multiples of this       */
 #define PKV_MAX_PARTITION 1024
 #define PKV_MAX_QUERY_ROWS 64      /* num_queries * (N / K) for the multi-query call */
+#define PKV_MAX_PREFIX_ROWS 1024   /* max_members * (N / K) for the prefix-aware call */
 
 /* KV pool element types of paged_decode_attention_mq. */
 #define PKV_KV_BF16 0              /* bf16 bit patterns                           */
@@ -260,6 +261,62 @@ int paged_decode_attention_mq(float *out, const void *q,
                               int32_t max_context_len, int64_t num_blocks,
                               int32_t partition_size, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/*
+ * Shared prompt prefixes.  Sequences that share a prefix point their block
+ * tables at the same physical blocks; a block is copied before one of its
+ * sharers writes into it ("CS336 Lecture 10: Inference", part 6: shared
+ * prefix blocks, copy on write; the lesson's prefix-caching section).
+ *
+ * paged_kv_copy_blocks -- for each pair i, physical block dst_blocks[i]
+ *   becomes a bit-exact copy of block src_blocks[i]: every KV head, offset
+ *   and head dim, in both pools.  kv_dtype (PKV_KV_BF16 or PKV_KV_FP8_E4M3)
+ *   fixes the element size.  A pair with an id outside [0, num_blocks) or
+ *   with src == dst is skipped.  Pairs run concurrently: no block may be the
+ *   destination of one pair and the source or destination of another (the
+ *   result is then unspecified).  src_blocks, dst_blocks: [num_pairs] int32
+ *   device arrays, num_pairs <= 65535.  Checks as for paged_kv_append.
+ *
+ * paged_decode_attention_prefix -- paged_decode_attention with fixed
+ *   partitions (partition_size P: a multiple of 32 in [32, 1024]) that reads
+ *   each shared prefix once per partition for all of its sharers instead of
+ *   once per sharer.  The result is plain attention over each sequence's
+ *   context, exactly (bit for bit) what paged_decode_attention gives with the
+ *   same partition size; only the reading changes.
+ *   seq_group      [num_seqs] int32: the prefix group of each sequence, -1 for
+ *                  none.
+ *   group_members  [num_groups][max_members] int32: the sequences of each
+ *                  group, -1 padded; the first is the group's lead.
+ *   prefix_tokens  [num_groups] int32: positions 0 .. prefix_tokens - 1 of
+ *                  every member map to the same physical blocks as the lead's.
+ *   max_prefix_tokens  host-known bound of prefix_tokens.
+ *   For a member b of group g, partitions p with (p + 1) * P <=
+ *   min(prefix_tokens[g], ctx_b, ctx_lead) are read once for the group; the
+ *   rest of its context is read on its own.  max_members * (N / K) <=
+ *   PKV_MAX_PREFIX_ROWS.  A member whose table disagrees with the lead's over
+ *   that span gets attention over the lead's blocks there.  Workspace as
+ *   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+ *   max_context_len, partition_size); kv_dtype, k_scale, v_scale as for
+ *   paged_decode_attention_mq; other arguments as for paged_decode_attention.
+ */
+int paged_kv_copy_blocks(void *key_cache, void *value_cache,
+                         const int32_t *src_blocks, const int32_t *dst_blocks,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, int32_t kv_dtype,
+                         void *stream);
+
+int paged_decode_attention_prefix(float *out, const void *q,
+                                  const void *key_cache, const void *value_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, int32_t kv_dtype, float k_scale, float v_scale,
+                                  int32_t num_kv_heads, int32_t block_size,
+                                  int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int64_t num_blocks, int32_t partition_size,
+                                  const int32_t *seq_group, const int32_t *group_members,
+                                  const int32_t *prefix_tokens, int32_t num_groups,
+                                  int32_t max_members, int32_t max_prefix_tokens,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * pagedkv_stream_read -- measurement helper, not part of the method: reads

@@ -15,6 +15,10 @@ computation runs in the library's HIP kernels.  The library must be built
                                block_size)
     paged_decode_attention_mq(out, q, key_cache, value_cache, block_tables,
                               context_lens, scale, num_kv_heads, block_size, partition)
+    paged_decode_attention_prefix(out, q, key_cache, value_cache, block_tables,
+                                  context_lens, scale, num_kv_heads, block_size, partition,
+                                  seq_group, group_members, prefix_tokens)
+    paged_kv_copy_blocks(key_cache, value_cache, src_blocks, dst_blocks)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
 [num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
@@ -74,6 +78,12 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_attention_mq.argtypes = [P, P, P, P, P, P, f32, i32, f32, f32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, i64, i32, P, sz, P]
     L.paged_decode_attention_mq.restype = ctypes.c_int
+    L.paged_decode_attention_prefix.argtypes = [P, P, P, P, P, P, f32, i32, f32, f32, i32, i32,
+                                                i32, i32, i32, i32, i32, i64, i32, P, P, P, i32,
+                                                i32, i32, P, sz, P]
+    L.paged_decode_attention_prefix.restype = ctypes.c_int
+    L.paged_kv_copy_blocks.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i32, P]
+    L.paged_kv_copy_blocks.restype = ctypes.c_int
     L.pagedkv_stream_read_sink_bytes.argtypes = [sz]
     L.pagedkv_stream_read_sink_bytes.restype = sz
     L.pagedkv_stream_read.argtypes = [P, sz, P, P]
@@ -283,6 +293,64 @@ def paged_decode_attention_mq(out: torch.Tensor, q: torch.Tensor, key_cache: tor
         float(k_scale), float(v_scale), K, bs, B, Q, N, H, max_blocks, int(max_context_len),
         nb, int(partition), pw, wbytes, _stream(q.device)), "paged_decode_attention_mq")
     return out
+
+
+def paged_decode_attention_prefix(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                                  block_size: int, partition: int, seq_group: torch.Tensor,
+                                  group_members: torch.Tensor, prefix_tokens: torch.Tensor,
+                                  max_prefix_tokens: Optional[int] = None,
+                                  k_scale: float = 1.0, v_scale: float = 1.0,
+                                  max_context_len: Optional[int] = None,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``paged_decode_attention`` with fixed ``partition``-token splits that
+    reads each shared prefix once for all its sharers.  seq_group [B] int32
+    (-1 = none), group_members [num_groups, max_members] int32 (-1 padded, lead
+    first), prefix_tokens [num_groups] int32; ``max_prefix_tokens`` is a host
+    bound of prefix_tokens (default: the block-table capacity)."""
+    head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
+                              num_kv_heads, block_size, max_context_len, partition, workspace,
+                              FP8_DTYPES if key_cache.dtype in FP8_DTYPES else torch.bfloat16)
+    fp8 = key_cache.dtype in FP8_DTYPES
+    psg = _dev(seq_group, "seq_group", torch.int32)
+    if group_members.dim() != 2 or prefix_tokens.shape != (group_members.shape[0],):
+        raise ValueError("group_members must be [num_groups, max_members] and prefix_tokens "
+                         "[num_groups]")
+    pgm = _dev(group_members, "group_members", torch.int32)
+    ppt = _dev(prefix_tokens, "prefix_tokens", torch.int32)
+    if seq_group.shape != (q.shape[0],):
+        raise ValueError("seq_group must be [B]")
+    num_groups, max_members = group_members.shape
+    if max_prefix_tokens is None:
+        max_prefix_tokens = block_tables.shape[1] * block_size
+    K, bs, B, N, H, max_blocks, mcl, nb, part, pw, wbytes, stream = tail
+    _check(lib().paged_decode_attention_prefix(
+        *head, float(scale), KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale), float(v_scale),
+        K, bs, B, N, H, max_blocks, mcl, nb, part, psg, pgm, ppt, num_groups, max_members,
+        int(max_prefix_tokens), pw, wbytes, stream), "paged_decode_attention_prefix")
+    return out
+
+
+def paged_kv_copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                         src_blocks: torch.Tensor, dst_blocks: torch.Tensor) -> None:
+    """Copy-on-write split: block dst_blocks[i] becomes a bit copy of block
+    src_blocks[i] (every head of both pools; bf16 or FP8 pools).  No block may
+    appear in two pairs."""
+    fp8 = key_cache.dtype in FP8_DTYPES
+    pool = FP8_DTYPES if fp8 else torch.bfloat16
+    pkc = _dev(key_cache, "key_cache", pool)
+    pvc = _dev(value_cache, "value_cache", pool)
+    ps = _dev(src_blocks, "src_blocks", torch.int32)
+    pd = _dev(dst_blocks, "dst_blocks", torch.int32)
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must both be [num_pairs]")
+    nb, K, bs, H = key_cache.shape
+    if value_cache.shape != (nb, K, H, bs):
+        raise ValueError("cache shapes disagree ([nb,K,bs,H] and [nb,K,H,bs])")
+    _check(lib().paged_kv_copy_blocks(pkc, pvc, ps, pd, src_blocks.shape[0], K, H, bs, nb,
+                                      KV_FP8_E4M3 if fp8 else KV_BF16,
+                                      _stream(key_cache.device)), "paged_kv_copy_blocks")
 
 
 def stream_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -73,10 +73,35 @@ struct DecodeParams {
     int32_t part;                 // tokens per partition (multiple of 32)
     int32_t num_parts;            // P
     int32_t num_queries;          // Q query tokens per sequence (1 for plain decode)
-    int32_t col_groups;           // multi-query: waves per (partition, KV head, sequence)
-    int32_t num_seqs;             // B (multi-query grid decoding)
+    int32_t col_groups;           // multi-query / prefix: waves per work item
+    int32_t num_seqs;             // B
     int64_t num_blocks;
+    // Prefix-aware decode only (else null / 0): sharers of a prompt prefix.
+    const int32_t *seq_group;     // [B]: prefix group of each sequence, -1 = none
+    const int32_t *group_members; // [num_groups][max_members], -1 = unused
+    const int32_t *prefix_tokens; // [num_groups]: shared positions 0 .. prefix_tokens - 1
+    int32_t num_groups;
+    int32_t max_members;
 };
+
+// Prefix-aware decode: the leading fixed partitions of sequence b that its
+// prefix group computes once for all sharers (0 when b shares nothing).
+// Partition p qualifies when (p + 1) * part <= min(prefix_tokens[g], ctx_b,
+// ctx_lead), lead being the group's first sharer, whose block table holds
+// the shared block ids.
+__device__ __forceinline__ int prefix_shared_parts(const DecodeParams &d, int b)
+{
+    const int g = d.seq_group[b];
+    if (g < 0 || g >= d.num_groups)
+        return 0;
+    const int lead = d.group_members[(int64_t)g * d.max_members];
+    if (lead < 0 || lead >= d.num_seqs)
+        return 0;
+    const int ctx_b = min(max(d.context_lens[b], 0), d.max_ctx);
+    const int ctx_lead = min(max(d.context_lens[lead], 0), d.max_ctx);
+    const int span = min(min(d.prefix_tokens[g], ctx_b), ctx_lead);
+    return max(span, 0) / d.part;
+}
 
 __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
 {
@@ -187,13 +212,17 @@ __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&i
     }
 }
 
-template <class Fmt, int H, bool kSplit>
+// kPrefix: prefix-aware decode; partitions the sequence's prefix group
+// computes are skipped (their split-K slots are written by that group).
+template <class Fmt, int H, bool kSplit, bool kPrefix = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
     const int part_idx = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
+    if (kPrefix && part_idx < prefix_shared_parts(p, b))
+        return;
     const int lane = threadIdx.x;
     const int col = lane & 15;    // query head within the group (tile column)
     const int quad = lane >> 4;   // 0..3

@@ -1,0 +1,191 @@
+// Shared-prefix-aware decode and the copy-on-write block copy.
+//
+// Sequences that share a prompt prefix point their block tables at the same
+// physical blocks ("CS336 Lecture 10: Inference", part 6: shared prefix
+// blocks, copied on write).  Plain decode reads those blocks once per sharer.
+// Here a prefix group -- its sharers listed by the caller -- is processed
+// once per fixed partition of the shared region: the columns of the
+// matrix-core tiles are the (sharer, query head) pairs of a KV head's group,
+// so every load of a shared key or value serves all the sharers a wave
+// carries (two tiles, 32 pairs, per wave; more sharers take more waves,
+// placed on one XCD at consecutive slots so their repeated reads meet in
+// its L2).  Each sharer gets the partition's partial (m, l, o) in its own
+// split-K slot, exactly as the per-sequence kernel would have written it; the
+// per-sequence kernel skips those partitions, and the log-sum-exp merge is
+// unchanged.  The result is plain attention: paging and sharing only change
+// where the blocks are read from.
+//
+// Partition p of sequence b comes from the group kernel when b belongs to a
+// group g and (p + 1) * P <= min(prefix_tokens[g], ctx_b, ctx_lead), where
+// lead is the group's first sharer, whose block table supplies the shared
+// block ids; both kernels compute this bound the same way.
+#pragma once
+
+#include "decode_multi.hpp"
+
+namespace pkv {
+
+struct PrefixParams {
+    DecodeParams d;                // split-K partials in d.part_o / d.part_ml, d.part = P,
+                                   // groups in d.seq_group / d.group_members / d.prefix_tokens
+    int32_t prefix_parts;          // grid bound: max over groups of prefix_tokens / P
+};
+
+// Grid (one dimension, XCD-aware as in decode_multi_kernel): items =
+// (group * K + kvh) * prefix_parts + partition, col_groups waves each.
+template <class Fmt, int H, int kTiles>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_prefix_kernel(PrefixParams p)
+{
+    const DecodeParams &d = p.d;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcds;
+    const int j = L / kXcds;
+    const int cg = j % d.col_groups;
+    const int64_t item = (int64_t)(j / d.col_groups) * kXcds + xcd;
+    if (item >= (int64_t)d.num_groups * d.num_kv_heads * p.prefix_parts)
+        return;
+    const int part_idx = (int)(item % p.prefix_parts);
+    const int kvh = (int)((item / p.prefix_parts) % d.num_kv_heads);
+    const int grp = (int)(item / ((int64_t)p.prefix_parts * d.num_kv_heads));
+    const int lane = threadIdx.x;
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+    const int G = d.group;
+    const int32_t *members = d.group_members + (int64_t)grp * d.max_members;
+
+    const int lead = members[0];
+    if (lead < 0 || lead >= d.num_seqs)
+        return;
+    const int start = part_idx * d.part;
+    const int end = start + d.part;
+    // The shared span as the lead sees it; sharers shorter than this
+    // partition's end get nothing here (their own kernel covers it).
+    if (end > min(d.prefix_tokens[grp], min(max(d.context_lens[lead], 0), d.max_ctx)))
+        return;
+
+    const int first_block = start / kBlockSize;
+    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + first_block;
+    int my_id = 0;
+    if (lane < d.part / kBlockSize)
+        my_id = clamp_block(table[lane], d.num_blocks);
+    const int n_blocks = d.part / kBlockSize;
+
+    // Column t of this lane: sharer m, head g.
+    bool live[kTiles];
+    int64_t qrow[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const int c = 16 * (kTiles * cg + t) + col;
+        const int m = c / G;
+        const int mb = m < d.max_members ? members[m] : -1;
+        live[t] = mb >= 0 && mb < d.num_seqs && d.seq_group[mb] == grp &&
+                  prefix_shared_parts(d, mb) > part_idx;
+        qrow[t] = (int64_t)(live[t] ? mb : lead) * d.num_heads + kvh * G + (c - m * G);
+    }
+
+    __shared__ u32x4 q_lds[kTiles * (H / 32) * kWave];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const uint16_t *qr = d.q + qrow[t] * H;
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s) {
+            u32x4 raw = load16(qr + Fmt::dim_offset(s, quad));
+            if (!live[t])
+                raw = u32x4{0u, 0u, 0u, 0u};
+            q_lds[(t * (H / 32) + s) * kWave + lane] = raw;
+        }
+    }
+
+    const int64_t tile_elems = (int64_t)kBlockSize * H;
+    const int64_t block_elems = (int64_t)d.num_kv_heads * tile_elems;
+    using Elem = typename Fmt::Elem;
+    using Regs = typename Fmt::template Regs<H>;
+    const Elem *kbase = static_cast<const Elem *>(d.key_cache) + kvh * tile_elems;
+    const Elem *vbase = static_cast<const Elem *>(d.value_cache) + kvh * tile_elems;
+    auto issue = [&](Regs &r, int ci) {
+        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
+        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
+                                                : id0;
+        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
+                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+    };
+
+    float m[kTiles], l[kTiles];
+    int lim[kTiles];
+    f32x4 acc[kTiles][H / 16];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        m[t] = -INFINITY;
+        l[t] = 0.f;
+        lim[t] = end;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Every position of the partition is valid for every live sharer.
+    auto attend = [&](const Regs &r, int ci) {
+        int opaque = lane;
+        asm volatile("" : "+v"(opaque));
+        auto qfrag = [&](int t, int s) {
+            return as_bf16x8(q_lds[(t * (H / 32) + s) * kWave + opaque]);
+        };
+        attend_chunk_multi<Fmt, H, kTiles, false>(r, qfrag, start + kChunk * ci + 8 * quad, lim,
+                                                  end - start - kChunk * ci, quad, d.scale_log2,
+                                                  m, l, acc);
+    };
+    // No masked chunks here: a two-tile wave keeps a deeper ring than in
+    // decode_multi_kernel.
+    constexpr int kRing = kTiles == 1 ? Fmt::kRing : Fmt::kRing - 1;
+    Regs ring[kRing];
+    run_ring<kRing>(d.part / kChunk, ring, issue, attend);
+
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        const float lt = sum_over_rows(l[t]);
+        if (!live[t])
+            continue;
+        const int64_t slot = qrow[t] * d.num_parts + part_idx;
+        float *o = d.part_o + slot * H;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * d.out_scale;
+        if (quad == 0) {
+            d.part_ml[2 * slot] = m[t];
+            d.part_ml[2 * slot + 1] = lt;
+        }
+    }
+}
+
+// ----------------------------------------------------- copy-on-write copy --
+
+struct CopyBlocksParams {
+    uint8_t *key_cache;
+    uint8_t *value_cache;
+    const int32_t *src;
+    const int32_t *dst;
+    int64_t block_bytes;   // K * block_size * H * element size, a multiple of 16
+    int64_t num_blocks;
+};
+
+constexpr int kCopyThreads = 256;
+
+// blockIdx.y = pair, blockIdx.x = slice of the block: 16-byte loads and
+// stores of both pools.  Pairs with an id outside [0, num_blocks) are skipped.
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksParams p)
+{
+    const int s = p.src[blockIdx.y];
+    const int t = p.dst[blockIdx.y];
+    if (s < 0 || t < 0 || s >= p.num_blocks || t >= p.num_blocks || s == t)
+        return;
+    const int64_t stride = (int64_t)gridDim.x * kCopyThreads * 16;
+    for (int64_t off = ((int64_t)blockIdx.x * kCopyThreads + threadIdx.x) * 16;
+         off < p.block_bytes; off += stride) {
+        const u32x4 k = load16(p.key_cache + s * p.block_bytes + off);
+        const u32x4 v = load16(p.value_cache + s * p.block_bytes + off);
+        store16(p.key_cache + t * p.block_bytes + off, k);
+        store16(p.value_cache + t * p.block_bytes + off, v);
+    }
+}
+
+}  // namespace pkv

@@ -11,12 +11,13 @@
 #include "kernels/decode.hpp"
 #include "kernels/decode_balanced.hpp"
 #include "kernels/decode_multi.hpp"
+#include "kernels/decode_prefix.hpp"
 #include "kernels/stream_read.hpp"
 
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 2;
+constexpr int kVersionMinor = 3;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
@@ -219,6 +220,11 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.col_groups = 1;
     p.num_seqs = num_seqs;
     p.num_blocks = num_blocks;
+    p.seq_group = nullptr;
+    p.group_members = nullptr;
+    p.prefix_tokens = nullptr;
+    p.num_groups = 0;
+    p.max_members = 0;
 
     if (partition_size == 0) {
         // Token-balanced: schedule, persistent decode, merge of split segments.
@@ -367,6 +373,82 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
                                      : (const void *)pkv::merge_kernel<64>;
     return launch(mk, dim3((unsigned)num_heads, (unsigned)(num_seqs * num_queries)),
                   dim3(pkv::kMergeThreads), &mp, stream);
+}
+
+// Prefix-aware decode: group kernel (shared partitions), per-sequence kernel
+// (the rest), merge.  With a single partition no partition can lie wholly
+// inside a shared prefix (which ends before the context does), so that case
+// is the plain kernel.
+template <class Fmt>
+int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t max_context_len, int32_t max_prefix_tokens,
+                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int32_t part = p.part;
+    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
+    const bool split = parts > 1;
+    const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
+    if (!split) {
+        p.num_parts = 1;
+        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, false>
+                                           : (const void *)pkv::decode_kernel<Fmt, 64, false>;
+        return launch(kern, grid, dim3(pkv::kWave), &p, stream);
+    }
+    const size_t need = fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, part);
+    if (!workspace || workspace_bytes < need)
+        return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return PKV_ERR_ALIGN;
+    const int64_t rows = (int64_t)num_seqs * num_heads * parts;
+    const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
+    p.part_o = static_cast<float *>(workspace);
+    p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    p.num_parts = (int32_t)parts;
+
+    const int64_t prefix_parts =
+        (int64_t)(max_prefix_tokens < max_context_len ? max_prefix_tokens : max_context_len) / part;
+    int rc = PKV_OK;
+    if (prefix_parts > 0 && p.num_groups > 0) {
+        const int tiles = (int)ceil_div((int64_t)p.max_members * (num_heads / num_kv_heads), 16);
+        const int per_wave = tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
+        pkv::PrefixParams pp;
+        pp.d = p;
+        pp.d.col_groups = (int32_t)ceil_div(tiles, per_wave);
+        pp.prefix_parts = (int32_t)prefix_parts;
+        const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
+        const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * pp.d.col_groups;
+        if (waves > INT32_MAX)
+            return PKV_ERR_SHAPE;
+        const void *gk;
+        if (head_dim == 128)
+            gk = per_wave == 1 ? (const void *)pkv::decode_prefix_kernel<Fmt, 128, 1>
+                               : (const void *)pkv::decode_prefix_kernel<Fmt, 128, 2>;
+        else
+            gk = per_wave == 1 ? (const void *)pkv::decode_prefix_kernel<Fmt, 64, 1>
+                               : (const void *)pkv::decode_prefix_kernel<Fmt, 64, 2>;
+        rc = launch(gk, dim3((unsigned)waves), dim3(pkv::kWave), &pp, stream);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, true, true>
+                                       : (const void *)pkv::decode_kernel<Fmt, 64, true, true>;
+    rc = launch(kern, grid, dim3(pkv::kWave), &p, stream);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::MergeParams mp;
+    mp.out = p.out;
+    mp.part_o = p.part_o;
+    mp.part_ml = p.part_ml;
+    mp.context_lens = p.context_lens;
+    mp.num_queries = 1;
+    mp.num_heads = num_heads;
+    mp.max_ctx = max_context_len;
+    mp.part = part;
+    mp.num_parts = (int32_t)parts;
+    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
+                                     : (const void *)pkv::merge_kernel<64>;
+    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads),
+                  &mp, stream);
 }
 
 }  // namespace
@@ -570,6 +652,11 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.col_groups = 1;
     p.num_seqs = num_seqs;
     p.num_blocks = num_blocks;
+    p.seq_group = nullptr;
+    p.group_members = nullptr;
+    p.prefix_tokens = nullptr;
+    p.num_groups = 0;
+    p.max_members = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_mq_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_queries, num_heads,
                                             num_kv_heads, max_context_len, workspace,
@@ -577,6 +664,138 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     return decode_mq_launch<pkv::KvBf16>(p, head_dim, num_seqs, num_queries, num_heads,
                                          num_kv_heads, max_context_len, workspace,
                                          workspace_bytes, stream);
+}
+
+int paged_decode_attention_prefix(float *out, const void *q, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, float scale, int32_t kv_dtype,
+                                  float k_scale, float v_scale, int32_t num_kv_heads,
+                                  int32_t block_size, int32_t num_seqs, int32_t num_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int32_t max_context_len, int64_t num_blocks,
+                                  int32_t partition_size, const int32_t *seq_group,
+                                  const int32_t *group_members, const int32_t *prefix_tokens,
+                                  int32_t num_groups, int32_t max_members,
+                                  int32_t max_prefix_tokens, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        max_context_len < 0 || num_blocks < 0 || num_groups < 0 || max_members < 0 ||
+        max_prefix_tokens < 0)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
+        return PKV_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_heads % num_kv_heads != 0)
+        return PKV_ERR_SHAPE;
+    if (num_heads / num_kv_heads > PKV_MAX_GROUP)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_members * (num_heads / num_kv_heads) > PKV_MAX_PREFIX_ROWS)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return PKV_ERR_SHAPE;
+    if (num_seqs > 65535 || num_kv_heads > 65535)
+        return PKV_ERR_SHAPE;
+    if (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_PARTITION ||
+        partition_size % PKV_PARTITION_GRAIN != 0)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype == PKV_KV_BF16) {
+        k_scale = 1.0f;
+        v_scale = 1.0f;
+    } else if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale)) {
+        return PKV_ERR_SHAPE;
+    }
+    if (!isfinite(scale) || !isfinite(scale * k_scale))
+        return PKV_ERR_SHAPE;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!out || !q || !block_tables || !context_lens || !seq_group)
+        return PKV_ERR_NULL;
+    if (num_groups > 0 && (!group_members || !prefix_tokens || max_members == 0))
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && (!key_cache || !value_cache))
+        return PKV_ERR_NULL;
+    if (max_context_len > 0 && num_blocks == 0)
+        return PKV_ERR_SHAPE;
+    if (!aligned16(out) || !aligned16(q) || (key_cache && !aligned16(key_cache)) ||
+        (value_cache && !aligned16(value_cache)) ||
+        (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+        (reinterpret_cast<uintptr_t>(context_lens) & 3u) ||
+        (reinterpret_cast<uintptr_t>(seq_group) & 3u) ||
+        (reinterpret_cast<uintptr_t>(group_members) & 3u) ||
+        (reinterpret_cast<uintptr_t>(prefix_tokens) & 3u))
+        return PKV_ERR_ALIGN;
+
+    pkv::DecodeParams p;
+    p.out = out;
+    p.part_o = nullptr;
+    p.part_ml = nullptr;
+    p.q = static_cast<const uint16_t *>(q);
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    p.out_scale = v_scale;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.max_blocks = max_blocks_per_seq;
+    p.max_ctx = max_context_len;
+    p.part = partition_size;
+    p.num_parts = 1;
+    p.num_queries = 1;
+    p.col_groups = 1;
+    p.num_seqs = num_seqs;
+    p.num_blocks = num_blocks;
+    p.seq_group = seq_group;
+    p.group_members = group_members;
+    p.prefix_tokens = prefix_tokens;
+    p.num_groups = num_groups;
+    p.max_members = max_members;
+    if (kv_dtype == PKV_KV_FP8_E4M3)
+        return decode_prefix_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_heads, num_kv_heads,
+                                                max_context_len, max_prefix_tokens, workspace,
+                                                workspace_bytes, stream);
+    return decode_prefix_launch<pkv::KvBf16>(p, head_dim, num_seqs, num_heads, num_kv_heads,
+                                             max_context_len, max_prefix_tokens, workspace,
+                                             workspace_bytes, stream);
+}
+
+int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *src_blocks,
+                         const int32_t *dst_blocks, int32_t num_pairs, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t kv_dtype, void *stream)
+{
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
+        return PKV_ERR_UNSUPPORTED;
+    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+        return PKV_ERR_UNSUPPORTED;
+    if (num_pairs == 0)
+        return PKV_OK;
+    if (num_pairs > 65535)
+        return PKV_ERR_SHAPE;
+    if (!key_cache || !value_cache || !src_blocks || !dst_blocks)
+        return PKV_ERR_NULL;
+    if (!aligned16(key_cache) || !aligned16(value_cache) ||
+        (reinterpret_cast<uintptr_t>(src_blocks) & 3u) ||
+        (reinterpret_cast<uintptr_t>(dst_blocks) & 3u))
+        return PKV_ERR_ALIGN;
+    pkv::CopyBlocksParams p;
+    p.key_cache = static_cast<uint8_t *>(key_cache);
+    p.value_cache = static_cast<uint8_t *>(value_cache);
+    p.src = src_blocks;
+    p.dst = dst_blocks;
+    p.block_bytes = (int64_t)num_kv_heads * PKV_BLOCK_SIZE * head_dim *
+                    (kv_dtype == PKV_KV_BF16 ? 2 : 1);
+    p.num_blocks = num_blocks;
+    const int64_t slices = ceil_div(p.block_bytes, (int64_t)pkv::kCopyThreads * 16);
+    const unsigned gx = (unsigned)(slices < 64 ? slices : 64);
+    return launch((const void *)pkv::copy_blocks_kernel, dim3(gx, (unsigned)num_pairs),
+                  dim3(pkv::kCopyThreads), &p, stream);
 }
 
 size_t pagedkv_stream_read_sink_bytes(size_t bytes)

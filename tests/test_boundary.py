@@ -34,6 +34,7 @@ def test_every_declared_symbol_is_exported(L):
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
             "paged_kv_append_fp8", "paged_decode_attention_fp8",
             "paged_decode_attention_mq", "paged_decode_mq_workspace_size",
+            "paged_decode_attention_prefix", "paged_kv_copy_blocks",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
             "pagedkv_stream_copy"} <= set(names)
@@ -45,7 +46,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.2"
+    assert pkv.version() == "1.3"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -156,6 +157,40 @@ def test_decode_mq_checks(L):
     assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 256) == 0
     rows = 4 * 3 * 8 * 4
     assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 64) == rows * 64 * 4 + rows * 8
+
+
+def decode_prefix(L, out=A, q=A, kc=A, vc=A, bt=A, cl=A, scale=0.125, dt=0, ks=1.0, vs=1.0,
+                  K=2, bs=16, B=4, N=8, H=64, maxblk=16, maxctx=256, nb=128, part=64, sg=A,
+                  gm=A, pt=A, ng=1, mm=3, mpt=100, ws=A, wsb=1 << 30):
+    return L.paged_decode_attention_prefix(out, q, kc, vc, bt, cl, scale, dt, ks, vs, K, bs, B,
+                                           N, H, maxblk, maxctx, nb, part, sg, gm, pt, ng, mm,
+                                           mpt, ws, wsb, None)
+
+
+def test_decode_prefix_checks(L):
+    assert decode_prefix(L, B=0) == OK
+    assert decode_prefix(L, sg=0) == NULL
+    assert decode_prefix(L, gm=0) == NULL
+    assert decode_prefix(L, gm=0, ng=0) != NULL            # no groups: members not needed
+    assert decode_prefix(L, part=0) == SHAPE               # fixed partitions only
+    assert decode_prefix(L, mm=300, N=8, K=2) == UNSUP     # 300 * 4 pairs > 1024
+    assert decode_prefix(L, ng=-1) == SHAPE
+    assert decode_prefix(L, pt=A + 2) == ALIGN
+    assert decode_prefix(L, ws=0) == WS
+
+
+def copy_blocks(L, kc=A, vc=A, src=A, dst=A, n=3, K=2, H=64, bs=16, nb=8, dt=0):
+    return L.paged_kv_copy_blocks(kc, vc, src, dst, n, K, H, bs, nb, dt, None)
+
+
+def test_copy_blocks_checks(L):
+    assert copy_blocks(L, n=0, src=0, dst=0) == OK
+    assert copy_blocks(L, src=0) == NULL
+    assert copy_blocks(L, n=-1) == SHAPE
+    assert copy_blocks(L, n=70000) == SHAPE
+    assert copy_blocks(L, H=96) == UNSUP
+    assert copy_blocks(L, dt=3) == UNSUP
+    assert copy_blocks(L, kc=MIS) == ALIGN
 
 
 def test_workspace_sizes(L):

@@ -1,0 +1,181 @@
+"""GPU: shared-prefix-aware decode and the copy-on-write block copy.
+
+``paged_decode_attention_prefix`` reads each shared prefix once per partition
+for all of its sharers.  What it computes is plain attention, so it is
+checked against the oracle's decode (``oracle.decode``) and, bit for bit,
+against ``paged_decode_attention`` with the same partition size: one group
+(the reduced ragged workload and its 20-sharer full size), several groups
+built by re-pointing block tables, more sharers than one wave carries,
+members shorter than the shared span, and FP8 pools.
+
+``paged_kv_copy_blocks`` is bit-exact against ``oracle.copy_blocks`` for
+bf16 and FP8 pools, and a copy-on-write divergence (copy a shared block,
+re-point one sharer, append into the copy) leaves the other sharers' results
+unchanged and matches the oracle.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_100_amd as pkv
+from paged_kv_cache_100_amd import workloads as W
+
+import gpu_harness as H
+from _util import bits, oracle_inputs, pool_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def groups_from(B, groups):
+    """groups: list of (members, prefix_tokens) -> device arrays."""
+    seq_group = torch.full((B,), -1, dtype=torch.int32)
+    width = max(len(m) for m, _ in groups)
+    members = torch.full((len(groups), width), -1, dtype=torch.int32)
+    tokens = torch.zeros(len(groups), dtype=torch.int32)
+    for g, (mem, t) in enumerate(groups):
+        members[g, :len(mem)] = torch.tensor(mem, dtype=torch.int32)
+        tokens[g] = t
+        for b in mem:
+            seq_group[b] = g
+    return seq_group.to(DEV), members.to(DEV), tokens.to(DEV)
+
+
+def run_prefix(w, groups, partition, what):
+    """Append, then prefix-aware and plain decode on copies of the same pools;
+    compare with the oracle and with each other."""
+    H.log(f"case {what}: B={w.spec.B} N={w.spec.N} K={w.spec.K} {w.kv_dtype} part {partition} "
+          f"groups={[(len(m), t) for m, t in groups]}")
+    ref, inp = H.oracle_step(w)
+    g = w.to(DEV)
+    H.gpu_append(g, w)
+    sg, gm, pt = groups_from(w.spec.B, groups)
+    out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    pkv.paged_decode_attention_prefix(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                      g.context_lens, w.scale, w.spec.K, w.spec.bs, partition,
+                                      sg, gm, pt, max_prefix_tokens=int(pt.max()),
+                                      k_scale=w.k_scale, v_scale=w.v_scale,
+                                      max_context_len=w.max_context_len)
+    plain = torch.full_like(out, float("nan"))
+    H.gpu_decode(plain, g, w, partition=partition)
+    torch.cuda.synchronize()
+    H.assert_append_exact(g, inp, what)
+    H.assert_parity(out.cpu().numpy(), ref, what)
+    assert torch.equal(out, plain), f"{what}: differs from plain decode with the same partitions"
+
+
+def workload_groups(w):
+    return [(w.sharer_ids, len(w.shared_blocks) * w.spec.bs)]
+
+
+@pytest.mark.parametrize("partition", [32, 64, 128])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_ragged_small(kv, partition):
+    spec = dataclasses.replace(W.small("llama3_70b_ragged_b100"), kv_dtype=kv)
+    w = W.make(spec)
+    run_prefix(w, workload_groups(w), partition, f"ragged small {kv}")
+
+
+def repoint(w, groups_spec):
+    """Make each group's members share the lead's first n blocks (tables only)."""
+    groups = []
+    for lead, others, nblk in groups_spec:
+        for b in others:
+            w.block_tables[b, :nblk] = w.block_tables[lead, :nblk]
+        groups.append(([lead] + others, nblk * w.spec.bs))
+    return groups
+
+
+@pytest.mark.parametrize("partition", [32, 96])
+def test_several_groups(partition):
+    spec = W.Spec("groups", B=9, N=32, K=8, H=128, ctx=[700, 400, 650, 90, 333, 800, 41, 512, 200],
+                  seed=61, max_blocks=60)
+    w = W.make(spec)
+    # group 0: 0, 2, 5 and 3 share 20 blocks (3 has only 90 tokens, fewer than
+    # the shared span); group 1: 1, 7 share 8; group 2: 4 alone
+    groups = repoint(w, [(0, [2, 5, 3], 20), (1, [7], 8), (4, [], 10)])
+    run_prefix(w, groups, partition, f"three groups part {partition}")
+
+
+def test_many_sharers_span_several_waves():
+    # 12 sharers x G = 8 -> 96 (sharer, head) pairs: three two-tile waves
+    spec = W.Spec("many", B=14, N=64, K=8, H=128, ctx=[600 + 17 * i for i in range(14)],
+                  seed=67, max_blocks=60)
+    w = W.make(spec)
+    groups = repoint(w, [(3, [0, 1, 2, 4, 5, 6, 7, 8, 9, 10, 11], 30)])
+    run_prefix(w, groups, 64, "12 sharers")
+
+
+@pytest.mark.parametrize("Hd", [64, 128])
+def test_mha_and_head_dim(Hd):
+    spec = W.Spec("mha", B=6, N=16, K=16, H=Hd, ctx=[300, 260, 700, 33, 480, 300], seed=71,
+                  max_blocks=50)
+    w = W.make(spec)
+    groups = repoint(w, [(0, [1, 4, 5], 16)])
+    run_prefix(w, groups, 32, f"MHA H={Hd}")
+
+
+# ------------------------------------------------------------- block copy --
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_copy_blocks_bit_exact(kv):
+    spec = W.Spec("copy", B=4, N=8, K=4, H=128, ctx=[100, 200, 50, 300], seed=73, kv_dtype=kv,
+                  pool_blocks=60)
+    w = W.make(spec)
+    src = torch.tensor([3, 17, -1, 40, 8, 70], dtype=torch.int32)   # -1 and 70: skipped
+    dst = torch.tensor([50, 51, 52, 53, 54, 55], dtype=torch.int32)
+    H.log(f"case copy blocks {kv}")
+    kc, vc = pool_bits(w.key_cache), pool_bits(w.value_cache)
+    oracle.copy_blocks(kc, vc, src.numpy(), np.where(src.numpy() >= w.num_blocks, -1,
+                                                      dst.numpy()).astype(np.int32))
+    g = w.to(DEV)
+    pkv.paged_kv_copy_blocks(g.key_cache, g.value_cache, src.to(DEV), dst.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_bits(g.key_cache), kc)
+    assert np.array_equal(pool_bits(g.value_cache), vc)
+
+
+def test_copy_on_write_divergence():
+    """Three sequences share a partly filled block; the third must write its
+    next token there: copy the block, re-point its table, append into the
+    copy.  The first two are unchanged; all three match the oracle."""
+    spec = W.Spec("cow", B=3, N=32, K=8, H=128, ctx=[37, 37, 38], seed=79, pool_blocks=20,
+                  max_blocks=4)
+    w = W.make(spec, poison=False)
+    bt = w.block_tables
+    bt[1, :3] = bt[0, :3]
+    bt[2, :3] = bt[0, :3]                      # all three share blocks 0..2 (block 2 holds 5 tokens)
+    shared = int(bt[0, 2])
+    used = set(bt[:, :3].flatten().tolist())
+    fresh = next(i for i in range(w.num_blocks) if i not in used)
+    g = w.to(DEV)
+    out0 = torch.empty((3, spec.N, spec.H), dtype=torch.float32, device=DEV)
+    before = dataclasses.replace(g, context_lens=torch.tensor([37, 37, 37], dtype=torch.int32,
+                                                              device=DEV))
+    # one fixed partition: each sequence's result is independent of the others'
+    H.gpu_decode(out0, before, w, partition=1024, max_context_len=38)
+    pkv.paged_kv_copy_blocks(g.key_cache, g.value_cache,
+                             torch.tensor([shared], dtype=torch.int32, device=DEV),
+                             torch.tensor([fresh], dtype=torch.int32, device=DEV))
+    g.block_tables[2, 2] = fresh
+    k_new = w.k_new[2:3].to(DEV)
+    v_new = w.v_new[2:3].to(DEV)
+    pkv.paged_kv_append(k_new, v_new, torch.tensor([fresh * 16 + 5], device=DEV),
+                        g.key_cache, g.value_cache)
+    out = torch.empty_like(out0)
+    H.gpu_decode(out, g, w, partition=1024, max_context_len=38)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:2], out0[:2]), "the other sharers' results changed"
+    # oracle: same steps on host copies
+    kc, vc = bits(w.key_cache), bits(w.value_cache)
+    oracle.copy_blocks(kc, vc, np.array([shared], np.int32), np.array([fresh], np.int32))
+    oracle.append(bits(w.k_new[2:3]), bits(w.v_new[2:3]),
+                  np.array([fresh * 16 + 5], np.int64), kc, vc)
+    tables = bt.numpy().astype(np.int32).copy()
+    tables[2, 2] = fresh
+    ref = oracle.decode(bits(w.q), kc, vc, tables, np.array([37, 37, 38], np.int32), w.scale)
+    assert np.array_equal(pool_bits(g.key_cache), kc) and np.array_equal(pool_bits(g.value_cache), vc)
+    H.assert_parity(out.cpu().numpy(), ref, "copy-on-write divergence")
