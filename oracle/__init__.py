@@ -82,6 +82,9 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.oracle_decode_multi_rows.restype = i32
     lib.oracle_copy_blocks.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i64]
     lib.oracle_copy_blocks.restype = i32
+    lib.oracle_decode_window.argtypes = [P, P, P, P, i32, f32, f32, P, P, f32, i32,
+                                         i32, i32, i32, i32, i32, i32, i64, P, i32]
+    lib.oracle_decode_window.restype = i32
     return lib
 
 
@@ -371,3 +374,26 @@ def copy_blocks(key_cache, value_cache, src, dst, lib=None) -> None:
         key_cache.dtype.itemsize, nb)
     if rc:
         raise ValueError("block id outside the pool")
+
+
+# ---------------------------------------------------- sliding window ----
+
+def decode_window(q, key_cache, value_cache, block_tables, context_lens, scale, window: int,
+                  k_scale: float = 1.0, v_scale: float = 1.0, lib=None) -> np.ndarray:
+    """Each sequence's query attends its last ``window`` positions only
+    (positions max(0, ctx - window) .. ctx - 1); bf16 or FP8 pools;
+    float64 [B, N, H]."""
+    kc = np.ascontiguousarray(key_cache)
+    if kc.dtype not in _KV_DTYPES:
+        raise TypeError("pools must be uint16 (bf16 bits) or uint8 (E4M3 codes)")
+    q, kc, vc, bt, cl, (B, N, H, nb, K, bs) = _decode_args(
+        q, kc, value_cache, block_tables, context_lens, kc.dtype.type)
+    out = np.zeros((B, N, H), np.float64)
+    scratch, stride = _scratch(cl)
+    rc = (lib or _load()).oracle_decode_window(
+        _ptr(out), _ptr(q), _ptr(kc), _ptr(vc), _KV_DTYPES[kc.dtype], float(np.float32(k_scale)),
+        float(np.float32(v_scale)), _ptr(bt), _ptr(cl), float(np.float32(scale)), int(window),
+        B, N, K, H, bs, bt.shape[1], nb, _ptr(scratch), stride)
+    if rc:
+        raise ValueError("invalid decode arguments (window, block id, shape or context)")
+    return out

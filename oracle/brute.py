@@ -117,3 +117,24 @@ def copy_blocks(key_cache, value_cache, src, dst):
             continue
         key_cache[b] = [[list(row) for row in head] for head in key_cache[a]]
         value_cache[b] = [[list(row) for row in head] for head in value_cache[a]]
+
+
+def paged_decode_window(q, key_cache, value_cache, block_tables, context_lens, scale, window):
+    """Sliding window: each query looks only at the last ``window`` tokens of
+    its sequence (the new one included).  Returns out[b][n][h]."""
+    out = []
+    bs = len(key_cache[0][0]) if key_cache else 1
+    K = len(key_cache[0]) if key_cache else 1
+    for b in range(len(q)):
+        ctx = context_lens[b]
+        last = list(range(ctx))[-window:] if window < ctx else list(range(ctx))
+        group = len(q[b]) // K
+        rows = []
+        for n in range(len(q[b])):
+            g = n // group
+            keys = [list(key_cache[block_tables[b][t // bs]][g][t % bs]) for t in last]
+            values = [[value_cache[block_tables[b][t // bs]][g][h][t % bs]
+                       for h in range(len(q[b][n]))] for t in last]
+            rows.append(attend_one(q[b][n], keys, values, scale))
+        out.append(rows)
+    return out

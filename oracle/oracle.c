@@ -227,14 +227,15 @@ int oracle_append_fp8(const uint16_t *k, const uint16_t *v, const int64_t *slot_
 
 /*
  * One output row (query row qrow of query head n): the definition of
- * softmax(q K^T * scale) V over the first ctx positions of the sequence
+ * softmax(q K^T * scale) V over positions first .. ctx - 1 of the sequence
  * whose block-table row is `table`, gathering each position t through it.
- * `scores` is caller scratch of length ctx.  Writes H doubles to `row`.
+ * `scores` is caller scratch of length ctx.  Writes H doubles to `row`
+ * (zeros when the range is empty).
  */
 static int decode_row(double *row, double *scores,
                       const uint16_t *qrow, const void *key_cache,
                       const void *value_cache, int dtype, double k_scale, double v_scale,
-                      const int32_t *table, int ctx, int n, float scale,
+                      const int32_t *table, int first, int ctx, int n, float scale,
                       int N, int K, int H, int bs, int64_t num_blocks)
 {
     int G = N / K;
@@ -243,11 +244,11 @@ static int decode_row(double *row, double *scores,
 
     for (int h = 0; h < H; h++)
         row[h] = 0.0;
-    if (ctx == 0)
+    if (first >= ctx)
         return 0;
 
     double m = -INFINITY;
-    for (int t = 0; t < ctx; t++) {
+    for (int t = first; t < ctx; t++) {
         int64_t p = table[t / bs];
         int o = t % bs;
         if (p < 0 || p >= num_blocks)
@@ -261,11 +262,11 @@ static int decode_row(double *row, double *scores,
             m = scores[t];
     }
     double z = 0.0;
-    for (int t = 0; t < ctx; t++) {
+    for (int t = first; t < ctx; t++) {
         scores[t] = exp(scores[t] - m);
         z += scores[t];
     }
-    for (int t = 0; t < ctx; t++) {
+    for (int t = first; t < ctx; t++) {
         int64_t p = table[t / bs];
         int o = t % bs;
         for (int h = 0; h < H; h++)
@@ -313,7 +314,7 @@ static int decode_all(double *out, const uint16_t *q, const void *key_cache,
         status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
                              q + ((size_t)b * N + n) * H, key_cache, value_cache, dtype,
                              k_scale, v_scale, block_tables + (size_t)b * max_blocks,
-                             context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
+                             0, context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
     }
     return status ? -1 : 0;
 }
@@ -343,7 +344,7 @@ static int decode_rows_all(double *out_rows, const int32_t *rows_b, const int32_
         status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
                              q + ((size_t)b * N + n) * H, key_cache, value_cache, dtype,
                              k_scale, v_scale, block_tables + (size_t)b * max_blocks,
-                             context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
+                             0, context_lens[b], n, scale, N, K, H, bs, num_blocks) != 0;
     }
     return status ? -1 : 0;
 }
@@ -436,7 +437,7 @@ int oracle_decode_multi(double *out, const uint16_t *q, const void *key_cache,
         status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
                              q + (size_t)r * H, key_cache, value_cache, kv_dtype, k_scale,
                              v_scale, block_tables + (size_t)b * max_blocks,
-                             visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
+                             0, visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
                              num_blocks) != 0;
     }
     return status ? -1 : 0;
@@ -467,8 +468,44 @@ int oracle_decode_multi_rows(double *out_rows, const int32_t *rows_b, const int3
         status |= decode_row(out_rows + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
                              q + (((size_t)b * Q + i) * N + n) * H, key_cache, value_cache,
                              kv_dtype, k_scale, v_scale, block_tables + (size_t)b * max_blocks,
-                             visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
+                             0, visible_positions(context_lens[b], Q, i), n, scale, N, K, H, bs,
                              num_blocks) != 0;
+    }
+    return status ? -1 : 0;
+}
+
+/*
+ * Sliding-window decode ("CS336 Lecture 10: Inference", part 6, local or
+ * sliding-window attention: each generated token looks only at the last
+ * window tokens; "Week 11. Inference", step 1: a window caps the cache at
+ * its size): sequence b's query attends positions
+ * max(0, ctx_b - window) .. ctx_b - 1, the new token included.  window >= 1.
+ * q and out are [B][N][H]; pools as for oracle_decode_multi.
+ */
+int oracle_decode_window(double *out, const uint16_t *q, const void *key_cache,
+                         const void *value_cache, int kv_dtype, float k_scale, float v_scale,
+                         const int32_t *block_tables, const int32_t *context_lens, float scale,
+                         int window, int B, int N, int K, int H, int bs, int max_blocks,
+                         int64_t num_blocks, double *scratch, int scratch_stride)
+{
+    if (window < 1 || (kv_dtype != KV_BF16 && kv_dtype != KV_FP8) ||
+        check_shape(context_lens, B, N, K, bs, max_blocks))
+        return -1;
+    int status = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : status)
+    for (int r = 0; r < B * N; r++) {
+        int b = r / N, n = r % N;
+        int tid = thread_id();
+        int ctx = context_lens[b];
+        int first = ctx - window > 0 ? ctx - window : 0;
+        if (ctx > scratch_stride) {
+            status |= 1;
+            continue;
+        }
+        status |= decode_row(out + (size_t)r * H, scratch + (size_t)tid * scratch_stride,
+                             q + (size_t)r * H, key_cache, value_cache, kv_dtype, k_scale,
+                             v_scale, block_tables + (size_t)b * max_blocks, first, ctx, n,
+                             scale, N, K, H, bs, num_blocks) != 0;
     }
     return status ? -1 : 0;
 }

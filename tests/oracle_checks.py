@@ -565,4 +565,51 @@ def check_copy_on_write_divergence(lib):
     assert np.array_equal(after[1], ref[1]), "diverged sharer differs from private copies"
 
 
+# --------------------------------------------------------- sliding window ----
+
+def check_window_brute_force(lib):
+    for seed, (N, K, bs, H, W) in enumerate([(4, 2, 4, 8, 7), (6, 1, 4, 4, 1),
+                                              (4, 4, 16, 8, 20)]):
+        c = Case(500 + seed, N=N, K=K, bs=bs, H=H, max_ctx=40)
+        got = oracle.decode_window(c.q, c.kc, c.vc, c.tables, c.ctx, c.scale, W, lib=lib)
+        ref = np.array(brute.paged_decode_window(
+            bits_to_f64(c.q).tolist(), bits_to_f64(c.kc).tolist(), bits_to_f64(c.vc).tolist(),
+            c.tables.tolist(), c.ctx.tolist(), c.scale, W))
+        assert_close(got, ref, 1e-12, f"sliding window brute force (W={W})")
+
+
+def check_window_special_cases(lib):
+    c = Case(511, B=5, N=4, K=2, H=8, bs=4, ctx=[1, 12, 16, 32, 9])
+    full = c.decode(lib)
+    wide = oracle.decode_window(c.q, c.kc, c.vc, c.tables, c.ctx, c.scale, 32, lib=lib)
+    assert np.array_equal(wide, full), "a window covering the context must be full attention"
+    one = oracle.decode_window(c.q, c.kc, c.vc, c.tables, c.ctx, c.scale, 1, lib=lib)
+    vf = bits_to_f64(c.vc)
+    G = c.N // c.K
+    for b in range(c.B):
+        t = int(c.ctx[b]) - 1
+        p, o = c.tables[b, t // c.bs], t % c.bs
+        for n in range(c.N):
+            assert np.array_equal(one[b, n], vf[p, n // G, :, o]), "window 1 must return the new V"
+    # a window of W equals full attention over a cache whose first ctx - W
+    # positions were never there: drop them by shifting the sequence's blocks
+    # (block-aligned drops: 0, 4, 8, 24 positions for the first four)
+    W = 8
+    got = oracle.decode_window(c.q, c.kc, c.vc, c.tables, c.ctx, c.scale, W, lib=lib)
+    checked = 0
+    for b in range(c.B):
+        ctx = int(c.ctx[b])
+        drop = max(ctx - W, 0)
+        if drop % c.bs:
+            continue               # only block-aligned drops are table shifts
+        t2 = c.tables.copy()
+        t2[b, :t2.shape[1] - drop // c.bs] = c.tables[b, drop // c.bs:]
+        cl2 = c.ctx.copy()
+        cl2[b] = ctx - drop
+        ref = oracle.decode(c.q, c.kc, c.vc, t2, cl2, c.scale, lib=lib)
+        assert np.array_equal(got[b], ref[b]), "window differs from the shortened cache"
+        checked += 1
+    assert checked == 4
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -24,7 +24,7 @@ MUTANTS = {
     "no_scale": ("scores[t] = sc * dot;", "scores[t] = dot;"),
     "value_index_transposed": ("value_index(p, g, h, o, K, bs, H)", "value_index(p, g, o % H, h % bs, K, bs, H)"),
     "key_index_transposed": ("key_index(p, g, o, h, K, bs, H)", "key_index(p, g, h % bs, o % H, K, bs, H)"),
-    "ctx_off_by_one": ("for (int t = 0; t < ctx; t++)", "for (int t = 0; t < ctx - 1; t++)"),
+    "ctx_off_by_one": ("for (int t = first; t < ctx; t++)", "for (int t = first; t < ctx - 1; t++)"),
     "append_v_from_k": ("value_cache[value_index(p, g, h, o, K, bs, H)] = v[src];",
                         "value_cache[value_index(p, g, h, o, K, bs, H)] = k[src];"),
     "append_negative_slot_not_skipped": ("if (s < 0)\n            continue;",
@@ -49,6 +49,9 @@ MUTANTS = {
     "copy_value_from_key": ("value_cache[vd] = value_cache[vs];", "value_cache[vd] = key_cache[ks];"),
     "copy_one_head": ("for (int g = 0; g < K; g++)\n            for (int o = 0; o < bs; o++)",
                       "for (int g = 0; g < 1; g++)\n            for (int o = 0; o < bs; o++)"),
+    "window_off_by_one": ("int first = ctx - window > 0 ? ctx - window : 0;",
+                          "int first = ctx - window + 1 > 0 ? ctx - window + 1 : 0;"),
+    "window_ignored": ("int first = ctx - window > 0 ? ctx - window : 0;", "int first = 0;"),
     "copy_low_bytes_only": ("for (int e = 0; e < elem_bytes; e++) {", "for (int e = 0; e < 1; e++) {"),
 }
 
