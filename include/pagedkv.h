@@ -263,6 +263,30 @@ int paged_decode_attention_mq(float *out, const void *q,
                               void *stream);
 
 /*
+ * paged_decode_attention_window -- sliding-window decode: each sequence's
+ * query attends only its last `window` positions, max(0, ctx_b - window) ..
+ * ctx_b - 1, the step's new token included ("CS336 Lecture 10: Inference",
+ * part 6: with local or sliding-window attention a generated token depends
+ * only on the last tokens; "Week 11. Inference", step 1: a window caps the
+ * cache at its size).  Positions before the window are never read (a 32-token
+ * chunk holding the window's start is read whole, its earlier positions
+ * masked), so the bytes read per step are bounded by the window.
+ *   window         >= 1; a window at least the context is full attention.
+ *   kv_dtype, k_scale, v_scale   as for paged_decode_attention_mq.
+ * Other arguments, the workspace (paged_decode_workspace_size with the same
+ * partition_size) and both partitioning modes as for paged_decode_attention.
+ */
+int paged_decode_attention_window(float *out, const void *q,
+                                  const void *key_cache, const void *value_cache,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  float scale, int32_t kv_dtype, float k_scale, float v_scale,
+                                  int32_t window, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int64_t num_blocks, int32_t partition_size,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Shared prompt prefixes.  Sequences that share a prefix point their block
  * tables at the same physical blocks; a block is copied before one of its
  * sharers writes into it ("CS336 Lecture 10: Inference", part 6: shared

@@ -19,6 +19,8 @@ computation runs in the library's HIP kernels.  The library must be built
                                   context_lens, scale, num_kv_heads, block_size, partition,
                                   seq_group, group_members, prefix_tokens)
     paged_kv_copy_blocks(key_cache, value_cache, src_blocks, dst_blocks)
+    paged_decode_attention_window(out, q, key_cache, value_cache, block_tables,
+                                  context_lens, scale, num_kv_heads, block_size, window)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
 [num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                                 i32, i32, i32, i32, i32, i64, i32, P, P, P, i32,
                                                 i32, i32, P, sz, P]
     L.paged_decode_attention_prefix.restype = ctypes.c_int
+    L.paged_decode_attention_window.argtypes = [P, P, P, P, P, P, f32, i32, f32, f32, i32, i32,
+                                                i32, i32, i32, i32, i32, i32, i64, i32, P, sz, P]
+    L.paged_decode_attention_window.restype = ctypes.c_int
     L.paged_kv_copy_blocks.argtypes = [P, P, P, P, i32, i32, i32, i32, i64, i32, P]
     L.paged_kv_copy_blocks.restype = ctypes.c_int
     L.pagedkv_stream_read_sink_bytes.argtypes = [sz]
@@ -329,6 +334,25 @@ def paged_decode_attention_prefix(out: torch.Tensor, q: torch.Tensor, key_cache:
         *head, float(scale), KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale), float(v_scale),
         K, bs, B, N, H, max_blocks, mcl, nb, part, psg, pgm, ppt, num_groups, max_members,
         int(max_prefix_tokens), pw, wbytes, stream), "paged_decode_attention_prefix")
+    return out
+
+
+def paged_decode_attention_window(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                                  value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                                  block_size: int, window: int, k_scale: float = 1.0,
+                                  v_scale: float = 1.0, max_context_len: Optional[int] = None,
+                                  partition: int = 0,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sliding-window decode: each query attends the last ``window`` positions
+    of its sequence (the new token included); bf16 or FP8 pools."""
+    fp8 = key_cache.dtype in FP8_DTYPES
+    head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
+                              num_kv_heads, block_size, max_context_len, partition, workspace,
+                              FP8_DTYPES if fp8 else torch.bfloat16)
+    _check(lib().paged_decode_attention_window(
+        *head, float(scale), KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale), float(v_scale),
+        int(window), *tail), "paged_decode_attention_window")
     return out
 
 

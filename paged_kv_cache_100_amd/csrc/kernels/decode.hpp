@@ -82,7 +82,14 @@ struct DecodeParams {
     const int32_t *prefix_tokens; // [num_groups]: shared positions 0 .. prefix_tokens - 1
     int32_t num_groups;
     int32_t max_members;
+    int32_t window;               // sliding window: attend the last `window` positions; 0 = all
 };
+
+// First position a sequence of ctx tokens attends (sliding window), else 0.
+__device__ __forceinline__ int window_start(const DecodeParams &d, int ctx)
+{
+    return d.window > 0 ? max(ctx - d.window, 0) : 0;
+}
 
 // Prefix-aware decode: the leading fixed partitions of sequence b that its
 // prefix group computes once for all sharers (0 when b shares nothing).
@@ -109,9 +116,13 @@ __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
 }
 
 // `qf(s)` yields the lane's query operand for k-step s (from registers or LDS).
+// kTail: a chunk with masked positions -- those at or past `rem` (the end of
+// the context: their values are zeroed too) and those before `head` (the
+// start of a sliding window: valid cached tokens, only their scores are
+// masked).
 template <class Fmt, int H, bool kTail, class QFrag>
 __device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H> &r, QFrag &&qf,
-                                             int rem, int quad,
+                                             int rem, int head, int quad,
                                              float scale_log2, float &m, float &l,
                                              f32x4 (&acc)[H / 16])
 {
@@ -130,11 +141,12 @@ __device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H
         x[4 + i] = s1[i] * scale_log2;
     }
     u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
-    if (kTail) {   // last, partial chunk of the partition: rem < 32 tokens valid
+    if (kTail) {   // rem - head < 32 tokens valid
         const int valid = min(max(rem - 8 * quad, 0), 8);
+        const int skip = min(max(head - 8 * quad, 0), 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (e >= valid)
+            if (e >= valid || e < skip)
                 x[e] = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w)
@@ -244,7 +256,10 @@ void decode_kernel(DecodeParams p)
     const bool live = col < p.group;
     const int n = kvh * p.group + col;
 
-    if (start >= ctx) {
+    // Sliding window: positions before lo are not attended; a partition that
+    // ends before lo is skipped (the merge starts at lo's partition).
+    const int lo = window_start(p, ctx);
+    if (start >= ctx || (kSplit && start + p.part <= lo)) {
         if (!kSplit && part_idx == 0 && live) {   // empty sequence: zeros
             float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
 #pragma unroll
@@ -276,12 +291,18 @@ void decode_kernel(DecodeParams p)
     const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
     const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
 
-    // Issue the loads of chunk ci (tokens start + 32ci ...); its second block
+    // Chunks start at cbeg: the partition's start, or the 32-token boundary
+    // at or below the window start.
+    const int cbeg = __builtin_amdgcn_readfirstlane(max(start, lo - lo % kChunk));
+    const int boff = (cbeg - start) / kBlockSize;   // table entries before cbeg
+    const int head = lo - cbeg;                      // masked leading positions of chunk 0
+
+    // Issue the loads of chunk ci (tokens cbeg + 32ci ...); its second block
     // is addressed only if the chunk reaches into it.
     auto issue = [&](Regs &r, int ci) {
-        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
-        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
-                                                : id0;
+        const int k0 = boff + 2 * ci;
+        const int id0 = __builtin_amdgcn_readlane(my_id, k0);
+        const int id1 = (k0 + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, k0 + 1) : id0;
         Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
                               vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
     };
@@ -292,15 +313,17 @@ void decode_kernel(DecodeParams p)
     for (int c = 0; c < H / 16; ++c)
         acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int n_full = (end - start) / kChunk;                // chunks of 32 valid tokens
-    const int n_chunks = n_full + ((end - start) % kChunk != 0);
-    const int tail_rem = end - start - n_full * kChunk;
+    const int n_full = (end - cbeg) / kChunk;                 // chunks of 32 tokens below end
+    const int n_chunks = n_full + ((end - cbeg) % kChunk != 0);
+    const int tail_rem = end - cbeg - n_full * kChunk;
     auto qfrag = [&](int s) { return qf[s]; };
     auto attend = [&](const Regs &r, int ci) {
-        if (ci < n_full)
-            attend_chunk<Fmt, H, false>(r, qfrag, kChunk, quad, p.scale_log2, m, l, acc);
+        const bool front = ci == 0 && head > 0;
+        if (ci < n_full && !front)
+            attend_chunk<Fmt, H, false>(r, qfrag, kChunk, 0, quad, p.scale_log2, m, l, acc);
         else
-            attend_chunk<Fmt, H, true>(r, qfrag, tail_rem, quad, p.scale_log2, m, l, acc);
+            attend_chunk<Fmt, H, true>(r, qfrag, ci < n_full ? kChunk : tail_rem,
+                                       front ? head : 0, quad, p.scale_log2, m, l, acc);
     };
 
     Regs ring[Fmt::kRing];
@@ -336,6 +359,7 @@ struct MergeParams {
     const float *part_ml;         // [B][Q][N][P][2]
     const int32_t *context_lens;  // [B]
     int32_t num_queries;          // Q (1 for plain decode)
+    int32_t window;               // sliding window (0 = none): earlier partitions are skipped
     int32_t num_heads;
     int32_t max_ctx;
     int32_t part;
@@ -384,16 +408,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
     const int tid = threadIdx.x;
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
     const int parts = (ctx + p.part - 1) / p.part;
+    const int first = p.window > 0 ? max(ctx - p.window, 0) / p.part : 0;
     const int64_t row = (int64_t)bq * p.num_heads + n;
     const float *ml = p.part_ml + row * p.num_parts * 2;
     const float *po = p.part_o + row * p.num_parts * H;
 
     float big = -INFINITY;
-    for (int j = tid; j < parts; j += kMergeThreads)
+    for (int j = first + tid; j < parts; j += kMergeThreads)
         big = fmaxf(big, ml[2 * j]);
     big = block_reduce<true>(big, red);
     float den = 0.f;
-    for (int j = tid; j < parts; j += kMergeThreads)
+    for (int j = first + tid; j < parts; j += kMergeThreads)
         den += __builtin_amdgcn_exp2f(ml[2 * j] - big) * ml[2 * j + 1];
     den = block_reduce<false>(den, red);
 
@@ -401,7 +426,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
     const int grp = tid / H;
     float num = 0.f;
 #pragma unroll 4
-    for (int j = grp; j < parts; j += kGroups)
+    for (int j = first + grp; j < parts; j += kGroups)
         num += __builtin_amdgcn_exp2f(ml[2 * j] - big) * po[(int64_t)j * H + h];
     part_sum[grp][h] = num;
     __syncthreads();

@@ -50,6 +50,17 @@ constexpr int kInlineScheduleSeqs = 256;   // largest B scanned inside every wav
 
 __device__ __forceinline__ int chunks_of(int ctx) { return (ctx + kChunk - 1) / kChunk; }
 
+// A segment's chunks run from the 32-token boundary at or below the sliding
+// window's start (0 without a window) to the end of the context.
+__device__ __forceinline__ int first_chunk(const DecodeParams &d, int ctx)
+{
+    return window_start(d, ctx) / kChunk;
+}
+__device__ __forceinline__ int seg_chunks(const DecodeParams &d, int ctx)
+{
+    return chunks_of(ctx) - first_chunk(d, ctx);
+}
+
 // Uniform (scalar) value of a load whose address is the same in every lane.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
     // Pass 1: T = K * sum_b nc_b (needed to place the wave boundaries).
     int mine = 0;
     for (int b = tid; b < B; b += kScheduleThreads)
-        mine += chunks_of(seq_ctx(p.d, b));
+        mine += seg_chunks(p.d, seq_ctx(p.d, b));
     incl[tid] = mine;
     __syncthreads();
     for (int off = kScheduleThreads / 2; off >= 1; off >>= 1) {
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
     // falls in this tile, found by binary search over the tile's prefix sums.
     for (int base = 0; base < B; base += kScheduleThreads) {
         const int b = base + tid;
-        const int nc = b < B ? chunks_of(seq_ctx(p.d, b)) : 0;
+        const int nc = b < B ? seg_chunks(p.d, seq_ctx(p.d, b)) : 0;
         incl[tid] = nc;
         __syncthreads();
         for (int off = 1; off < kScheduleThreads; off <<= 1) {   // Hillis-Steele scan
@@ -186,9 +197,10 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
 // ------------------------------------------------------------------ decode --
 
 // Position of one chunk in the flattened order: segment (b, kvh), chunk j of
-// the nc chunks of sequence b (ctx tokens).
+// the nc chunks of sequence b (ctx tokens); the segment's chunk j covers
+// positions 32 * (fc + j) .. (fc counts the chunks before the sliding window).
 struct Pos {
-    int b, kvh, j, nc, ctx;
+    int b, kvh, j, nc, ctx, fc;
 };
 
 // One ring slot: the chunk's key/value operands, plus the group's query
@@ -232,7 +244,7 @@ void decode_balanced_kernel(BalancedParams p)
         int total_seq = 0;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t)
-            total_seq += wave_sum(chunks_of(cx[t]));
+            total_seq += wave_sum(seg_chunks(d, cx[t]));
         T = (int64_t)uniform(total_seq) * K;
         if (T == 0)
             return;
@@ -246,7 +258,7 @@ void decode_balanced_kernel(BalancedParams p)
         bool found = false;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
-            const int nc = chunks_of(cx[t]);
+            const int nc = seg_chunks(d, cx[t]);
             const int incl = wave_inclusive_scan(nc, lane);
             const int tile_total = __shfl(incl, kWave - 1);
             if (!found && (int64_t)(carry + tile_total) * K > c_begin) {
@@ -279,7 +291,8 @@ void decode_balanced_kernel(BalancedParams p)
     start.kvh = uniform(st.y);
     start.j = uniform(st.z);
     start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
-    start.nc = chunks_of(start.ctx);
+    start.nc = seg_chunks(d, start.ctx);
+    start.fc = first_chunk(d, start.ctx);
     if (start.j >= start.nc)          // cannot happen for a consistent schedule
         return;
 
@@ -303,7 +316,8 @@ void decode_balanced_kernel(BalancedParams p)
         const int2 nx = next_seq(q.b);
         q.b = nx.x;
         q.ctx = nx.y;
-        q.nc = chunks_of(q.ctx);
+        q.nc = seg_chunks(d, q.ctx);
+        q.fc = first_chunk(d, q.ctx);
     };
 
     const int64_t tile_elems = (int64_t)kBlockSize * H;
@@ -314,10 +328,11 @@ void decode_balanced_kernel(BalancedParams p)
     Pos ip = start;
     int id0 = 0, id1 = 0;
     auto load_ids = [&](const Pos &q) {
-        const int32_t *row = d.block_tables + (int64_t)q.b * d.max_blocks + 2 * q.j;
+        const int jj = q.fc + q.j;    // chunk index within the sequence
+        const int32_t *row = d.block_tables + (int64_t)q.b * d.max_blocks + 2 * jj;
         const int nblk = (q.ctx + kBlockSize - 1) / kBlockSize;
         id0 = clamp_block(scalar_load(row), d.num_blocks);
-        id1 = 2 * q.j + 1 < nblk ? clamp_block(scalar_load(row + 1), d.num_blocks) : id0;
+        id1 = 2 * jj + 1 < nblk ? clamp_block(scalar_load(row + 1), d.num_blocks) : id0;
     };
     load_ids(ip);
     auto issue = [&](Buf &r, int k) {
@@ -361,11 +376,13 @@ void decode_balanced_kernel(BalancedParams p)
                 qcur[s] = r.q[s];
         }
         const bool seg_end = ap.j + 1 == ap.nc;
-        if (!seg_end || ap.ctx % kChunk == 0)
-            attend_chunk<Fmt, H, false>(r.kv, qfrag, kChunk, quad, d.scale_log2, m, l, acc);
+        // Leading positions of a segment's first chunk before the window start.
+        const int head = ap.j == 0 ? window_start(d, ap.ctx) - kChunk * ap.fc : 0;
+        if ((!seg_end || ap.ctx % kChunk == 0) && head == 0)
+            attend_chunk<Fmt, H, false>(r.kv, qfrag, kChunk, 0, quad, d.scale_log2, m, l, acc);
         else
-            attend_chunk<Fmt, H, true>(r.kv, qfrag, ap.ctx - kChunk * ap.j, quad, d.scale_log2,
-                                       m, l, acc);
+            attend_chunk<Fmt, H, true>(r.kv, qfrag, ap.ctx - kChunk * (ap.fc + ap.j), head, quad,
+                                       d.scale_log2, m, l, acc);
         if (!seg_end && k + 1 < total)
             return;
         // The piece ends here (segment end, or the wave's last chunk).
@@ -438,7 +455,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             const int bb = t * kWave + lane;
-            c[t] = bb < B ? chunks_of(seq_ctx(d, bb)) : 0;
+            c[t] = bb < B ? seg_chunks(d, seq_ctx(d, bb)) : 0;
         }
         int total = 0, before = 0, mine = 0;
 #pragma unroll
@@ -451,7 +468,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
         T = (int64_t)total * K;
         seq_first = before;
     } else {
-        nc = chunks_of(seq_ctx_uniform(d, b));
+        nc = seg_chunks(d, seq_ctx_uniform(d, b));
         T = scalar_load(p.total_chunks);
         seq_first = scalar_load(p.chunk_start + b);
     }

@@ -17,7 +17,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 3;
+constexpr int kVersionMinor = 4;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
@@ -160,13 +160,14 @@ bool valid_pool_scale(float s)
 template <class Fmt>
 int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
                 const int32_t *block_tables, const int32_t *context_lens, float scale,
-                float k_scale, float v_scale, int32_t num_kv_heads, int32_t block_size,
+                float k_scale, float v_scale, int32_t window, int32_t num_kv_heads,
+                int32_t block_size,
                 int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                 int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
                 int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-        max_context_len < 0 || num_blocks < 0)
+        max_context_len < 0 || num_blocks < 0 || window < 0)
         return PKV_ERR_SHAPE;
     if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
         return PKV_ERR_UNSUPPORTED;
@@ -225,6 +226,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.prefix_tokens = nullptr;
     p.num_groups = 0;
     p.max_members = 0;
+    p.window = window;
 
     if (partition_size == 0) {
         // Token-balanced: schedule, persistent decode, merge of split segments.
@@ -304,6 +306,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     mp.part_ml = p.part_ml;
     mp.context_lens = context_lens;
     mp.num_queries = 1;
+    mp.window = p.window;
     mp.num_heads = num_heads;
     mp.max_ctx = max_context_len;
     mp.part = part;
@@ -365,6 +368,7 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     mp.part_ml = p.part_ml;
     mp.context_lens = p.context_lens;
     mp.num_queries = num_queries;
+    mp.window = 0;
     mp.num_heads = num_heads;
     mp.max_ctx = max_context_len;
     mp.part = part;
@@ -441,6 +445,7 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     mp.part_ml = p.part_ml;
     mp.context_lens = p.context_lens;
     mp.num_queries = 1;
+    mp.window = p.window;
     mp.num_heads = num_heads;
     mp.max_ctx = max_context_len;
     mp.part = part;
@@ -544,7 +549,7 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
                            size_t workspace_bytes, void *stream)
 {
     return decode_impl<pkv::KvBf16>(out, q, key_cache, value_cache, block_tables, context_lens,
-                                    scale, 1.0f, 1.0f, num_kv_heads, block_size, num_seqs,
+                                    scale, 1.0f, 1.0f, 0, num_kv_heads, block_size, num_seqs,
                                     num_heads, head_dim, max_blocks_per_seq, max_context_len,
                                     num_blocks, partition_size, workspace, workspace_bytes,
                                     stream);
@@ -562,7 +567,7 @@ int paged_decode_attention_fp8(float *out, const void *q, const void *key_cache,
     if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
         return PKV_ERR_SHAPE;
     return decode_impl<pkv::KvFp8>(out, q, key_cache, value_cache, block_tables, context_lens,
-                                   scale, k_scale, v_scale, num_kv_heads, block_size, num_seqs,
+                                   scale, k_scale, v_scale, 0, num_kv_heads, block_size, num_seqs,
                                    num_heads, head_dim, max_blocks_per_seq, max_context_len,
                                    num_blocks, partition_size, workspace, workspace_bytes, stream);
 }
@@ -657,6 +662,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.prefix_tokens = nullptr;
     p.num_groups = 0;
     p.max_members = 0;
+    p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_mq_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_queries, num_heads,
                                             num_kv_heads, max_context_len, workspace,
@@ -664,6 +670,35 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     return decode_mq_launch<pkv::KvBf16>(p, head_dim, num_seqs, num_queries, num_heads,
                                          num_kv_heads, max_context_len, workspace,
                                          workspace_bytes, stream);
+}
+
+int paged_decode_attention_window(float *out, const void *q, const void *key_cache,
+                                  const void *value_cache, const int32_t *block_tables,
+                                  const int32_t *context_lens, float scale, int32_t kv_dtype,
+                                  float k_scale, float v_scale, int32_t window,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t num_seqs,
+                                  int32_t num_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                                  int64_t num_blocks, int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    if (window < 1)
+        return PKV_ERR_SHAPE;
+    if (kv_dtype == PKV_KV_BF16)
+        return decode_impl<pkv::KvBf16>(out, q, key_cache, value_cache, block_tables,
+                                        context_lens, scale, 1.0f, 1.0f, window, num_kv_heads,
+                                        block_size, num_seqs, num_heads, head_dim,
+                                        max_blocks_per_seq, max_context_len, num_blocks,
+                                        partition_size, workspace, workspace_bytes, stream);
+    if (kv_dtype != PKV_KV_FP8_E4M3)
+        return PKV_ERR_UNSUPPORTED;
+    if (!valid_pool_scale(k_scale) || !valid_pool_scale(v_scale))
+        return PKV_ERR_SHAPE;
+    return decode_impl<pkv::KvFp8>(out, q, key_cache, value_cache, block_tables, context_lens,
+                                   scale, k_scale, v_scale, window, num_kv_heads, block_size,
+                                   num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                                   max_context_len, num_blocks, partition_size, workspace,
+                                   workspace_bytes, stream);
 }
 
 int paged_decode_attention_prefix(float *out, const void *q, const void *key_cache,
@@ -754,6 +789,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     p.prefix_tokens = prefix_tokens;
     p.num_groups = num_groups;
     p.max_members = max_members;
+    p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_prefix_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_heads, num_kv_heads,
                                                 max_context_len, max_prefix_tokens, workspace,

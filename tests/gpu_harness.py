@@ -168,3 +168,20 @@ def oracle_step_mq(w):
                               inp["block_tables"], inp["context_lens"], w.scale, w.k_scale,
                               w.v_scale)
     return ref, inp
+
+
+# --------------------------------------------------------- sliding window ----
+
+def gpu_decode_window(out, g, w, window: int, partition: int = 0, max_context_len=None):
+    mcl = w.max_context_len if max_context_len is None else max_context_len
+    pkv.paged_decode_attention_window(out, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                      g.context_lens, w.scale, w.spec.K, w.spec.bs, window,
+                                      k_scale=w.k_scale, v_scale=w.v_scale, max_context_len=mcl,
+                                      partition=partition)
+    return out
+
+
+def oracle_decode_window(w, inp, window: int):
+    return oracle.decode_window(inp["q"], inp["key_cache"], inp["value_cache"],
+                                inp["block_tables"], inp["context_lens"], w.scale, window,
+                                w.k_scale, w.v_scale)

@@ -35,6 +35,7 @@ def test_every_declared_symbol_is_exported(L):
             "paged_kv_append_fp8", "paged_decode_attention_fp8",
             "paged_decode_attention_mq", "paged_decode_mq_workspace_size",
             "paged_decode_attention_prefix", "paged_kv_copy_blocks",
+            "paged_decode_attention_window",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
             "pagedkv_stream_copy"} <= set(names)
@@ -46,7 +47,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.3"
+    assert pkv.version() == "1.4"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -191,6 +192,24 @@ def test_copy_blocks_checks(L):
     assert copy_blocks(L, H=96) == UNSUP
     assert copy_blocks(L, dt=3) == UNSUP
     assert copy_blocks(L, kc=MIS) == ALIGN
+
+
+def decode_window(L, window=64, dt=0, ks=1.0, vs=1.0, out=A, q=A, kc=A, vc=A, bt=A, cl=A,
+                  scale=0.125, K=2, bs=16, B=4, N=8, H=64, maxblk=16, maxctx=256, nb=128,
+                  part=0, ws=A, wsb=1 << 30):
+    return L.paged_decode_attention_window(out, q, kc, vc, bt, cl, scale, dt, ks, vs, window, K,
+                                           bs, B, N, H, maxblk, maxctx, nb, part, ws, wsb, None)
+
+
+def test_decode_window_checks(L):
+    assert decode_window(L, B=0) == OK
+    assert decode_window(L, window=0) == SHAPE
+    assert decode_window(L, window=-3) == SHAPE
+    assert decode_window(L, dt=5) == UNSUP
+    assert decode_window(L, dt=1, vs=0.0) == SHAPE
+    assert decode_window(L, q=0) == NULL
+    assert decode_window(L, part=48) == SHAPE
+    assert decode_window(L, ws=0) == WS
 
 
 def test_workspace_sizes(L):
