@@ -35,6 +35,7 @@ DEFAULT_WORKLOAD = "llama3_8b_b64_ctx8k"
 KERNEL_SOURCES = ["paged_kv_cache_100_amd/csrc/kernels/decode.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/decode_balanced.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/decode_multi.hpp",
+                  "paged_kv_cache_100_amd/csrc/kernels/decode_prefix.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/kv_format.hpp",
                   "paged_kv_cache_100_amd/csrc/kernels/common.hpp",
                   "paged_kv_cache_100_amd/csrc/pagedkv.hip"]
@@ -48,19 +49,36 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, part: int) -> dict:
-    """Bytes the method must move for one step (not what the kernels move)."""
+def algorithmic_bytes(w, part: int, window: int = 0) -> dict:
+    """Bytes the method must move for one step (not what the kernels move).
+    With a sliding window a sequence contributes its last ``window`` tokens."""
     s = w.spec
     elem = 1 if w.kv_dtype == "fp8" else 2
     ctx = [int(c) for c in w.context_lens.tolist()]
+    if window > 0:
+        ctx = [min(c, window) for c in ctx]
     kv = sum(ctx) * s.K * s.H * 2 * elem               # K and V pools
     Q = s.queries
     q = s.B * Q * s.N * s.H * 2
     out = s.B * Q * s.N * s.H * 4
     tables = sum(-(-c // s.bs) for c in ctx) * 4 + s.B * 4
     append = 2 * (s.B * Q * s.K * s.H) * (2 + elem)    # read bf16 k, v; write them into the pools
-    return {"kv": kv, "q": q, "out": out, "tables": tables, "attention": kv + q + out + tables,
-            "append": append}
+    # Shared prefix blocks counted once (what a prefix-aware read must move).
+    shared = len(w.shared_blocks) * s.bs * max(len(w.sharer_ids) - 1, 0)
+    kv_unique = kv - shared * s.K * s.H * 2 * elem
+    return {"kv": kv, "kv_unique": kv_unique, "q": q, "out": out, "tables": tables,
+            "attention": kv + q + out + tables,
+            "attention_unique": kv_unique + q + out + tables, "append": append}
+
+
+def profile_name(args) -> str:
+    """Name of the committed counter summary for this bench configuration."""
+    name = args.workload
+    if args.mode == "prefix":
+        name += "_prefix"
+    if args.window > 0:
+        name += f"_window{args.window}"
+    return name
 
 
 def traffic_from_profile(workload: str):
@@ -76,7 +94,7 @@ def traffic_from_profile(workload: str):
     return rec.get("hbm_bytes_per_call")
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+def cpu_baseline(w, budget_s: float = 12.0, window: int = 0) -> dict:
     """The CPU oracle, untuned, on this host: the workload's decode step (after
     the oracle's own append) repeated until about ``budget_s`` seconds of
     work, or -- when one full step takes longer -- a prefix of the batch
@@ -100,6 +118,9 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         oracle.append(u16(w.k_new), u16(w.v_new), w.slot_mapping.numpy(), kc, vc)
 
     def decode(n):
+        if window > 0:
+            return oracle.decode_window(q[:n], kc, vc, bt[:n], cl[:n], w.scale, window,
+                                        w.k_scale, w.v_scale)
         if w.spec.queries > 1:
             return oracle.decode_multi(q[:n], kc, vc, bt[:n], cl[:n], w.scale, w.k_scale,
                                        w.v_scale)
@@ -123,7 +144,7 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         decode(B)
         spent += time.perf_counter() - t0
         reps += 1
-    tokens = int(cl[:n].sum()) * reps
+    tokens = int((np.minimum(cl[:n], window) if window > 0 else cl[:n]).sum()) * reps
     kv_bytes = tokens * w.spec.K * w.spec.H * 2 * (1 if fp8 else 2)
     what = (f"the full batch of {B} sequences, {reps} times" if n == B
             else f"the first {n} of {B} sequences")
@@ -142,6 +163,11 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=None,
                     help="tokens per fixed split; 0 = token-balanced schedule "
                          "(default: the workload's own, else 0)")
+    ap.add_argument("--mode", choices=["plain", "prefix"], default="plain",
+                    help="prefix: read each shared prefix once for its sharers "
+                         "(fixed partitions; workloads with shared prefixes)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: attend each sequence's last W positions (0 = all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -205,6 +231,42 @@ def main() -> int:
 
     if not multi:
         attend = attend_one
+    if args.window > 0:
+        if multi or args.mode != "plain":
+            print("--window applies to the plain single-query decode", file=sys.stderr)
+            return 2
+
+        def attend():
+            pkv.paged_decode_attention_window(out, g.q, g.key_cache, g.value_cache,
+                                              g.block_tables, g.context_lens, w.scale, s.K, s.bs,
+                                              args.window, k_scale=w.k_scale, v_scale=w.v_scale,
+                                              max_context_len=mcl, partition=part,
+                                              workspace=workspace)
+    prefix = args.mode == "prefix"
+    if prefix:
+        if multi or not w.sharer_ids:
+            print("--mode prefix needs a single-query workload with a shared prefix",
+                  file=sys.stderr)
+            return 2
+        if part == 0:
+            part = 256
+        seq_group = torch.full((s.B,), -1, dtype=torch.int32)
+        seq_group[w.sharer_ids] = 0
+        members = torch.tensor([w.sharer_ids], dtype=torch.int32)
+        shared_tokens = len(w.shared_blocks) * s.bs
+        prefix_tokens = torch.tensor([shared_tokens], dtype=torch.int32)
+        seq_group, members, prefix_tokens = (seq_group.to(dev), members.to(dev),
+                                             prefix_tokens.to(dev))
+        ws_bytes = pkv.workspace_size(s.B, s.N, s.K, s.H, mcl, part)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+        def attend():
+            pkv.paged_decode_attention_prefix(out, g.q, g.key_cache, g.value_cache,
+                                              g.block_tables, g.context_lens, w.scale, s.K, s.bs,
+                                              part, seq_group, members, prefix_tokens,
+                                              max_prefix_tokens=shared_tokens, k_scale=w.k_scale,
+                                              v_scale=w.v_scale, max_context_len=mcl,
+                                              workspace=workspace)
 
     # Achievable bandwidth: plain 16-byte streaming read of 1 GiB, and a 1 GiB
     # copy (its known read and write sizes also scale the HBM byte counters
@@ -268,10 +330,11 @@ def main() -> int:
     attn_avg = region(attend)
     append_avg = region(append)    # host-bound: an append alone is shorter than its launch path
     ms_per_step = wall * 1e3 / K
-    nbytes = algorithmic_bytes(w, part)
-    achieved = nbytes["attention"] / (attn_avg * 1e-3) / 1e9
+    nbytes = algorithmic_bytes(w, part, args.window)
+    alg_key = "attention_unique" if prefix else "attention"
+    achieved = nbytes[alg_key] / (attn_avg * 1e-3) / 1e9
     value = nbytes["kv"] / (ms_per_step * 1e-3) / 1e9
-    traffic = traffic_from_profile(args.workload)
+    traffic = traffic_from_profile(profile_name(args))
 
     rec = {
         "metric": METRIC,
@@ -288,11 +351,16 @@ def main() -> int:
         "data": ("synthetic: seeded N(0,1) bf16 q/k/v, block tables from a seeded permutation"
                  + ("; K/V pools as E4M3 codes with per-pool scales" if w.kv_dtype == "fp8"
                     else "")),
-        "config": {"workload": args.workload, "kv_dtype": w.kv_dtype, "queries": s.queries,
+        "config": {"workload": args.workload, "mode": args.mode, "window": args.window,
+                   "kv_dtype": w.kv_dtype,
+                   "queries": s.queries,
                    "B": s.B, "N": s.N, "K": s.K, "H": s.H,
                    "block_size": s.bs, "sum_context": int(w.context_lens.sum()),
                    "max_context": mcl, "partition": part, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "kv_bytes_logical": nbytes["kv"],
+        "kv_bytes_unique": nbytes["kv_unique"],
+        "unique_kv_GBps": round(nbytes["kv_unique"] / (ms_per_step * 1e-3) / 1e9, 1),
         "tokens_per_s_per_layer": round(s.B * s.queries / (ms_per_step * 1e-3), 1),
         "attention_tokens_per_s_per_layer": round(s.B * s.queries / (attn_avg * 1e-3), 1),
         "attention_ms": round(attn_avg, 5),
@@ -304,11 +372,11 @@ def main() -> int:
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_call": nbytes["attention"],
+                     "algorithmic_bytes_per_call": nbytes[alg_key],
                      "kernel_hash": kernel_hash()},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, args.window)
     rec["setup_s"] = round(gen_s, 1)
     print(json.dumps(rec), flush=True)
     return 0
