@@ -99,18 +99,16 @@ __device__ __forceinline__ int wave_begin(int64_t w, int64_t T, int log2W)
 {
     return (int)((w * T) >> log2W);
 }
-// The wave whose range holds chunk c < T: the largest w with wave_begin(w) <= c.
-// A floating-point estimate, corrected exactly with integer comparisons.
+// The wave whose range holds chunk c < T: the largest w with
+// floor(w T / W) <= c, i.e. w T < (c + 1) W: w = floor(((c + 1) W - 1) / T).
+// One integer division (32-bit when the operands fit).
 __device__ __forceinline__ int wave_of(int64_t c, int64_t T, int log2W)
 {
-    const int W = 1 << log2W;
-    int w = (int)(((double)c + 1.0) * (double)W / (double)T) - 1;
-    w = min(max(w, 0), W - 1);
-    while (w + 1 < W && wave_begin(w + 1, T, log2W) <= c)
-        ++w;
-    while (w > 0 && wave_begin(w, T, log2W) > c)
-        --w;
-    return w;
+    const uint64_t num = ((uint64_t)(c + 1) << log2W) - 1;
+    const uint64_t w = (num >> 32) == 0 && (T >> 32) == 0
+                           ? (uint64_t)((uint32_t)num / (uint32_t)T)
+                           : num / (uint64_t)T;
+    return (int)min(w, (uint64_t)((1 << log2W) - 1));
 }
 
 // ---------------------------------------------------------------- schedule --
@@ -244,7 +242,8 @@ void decode_balanced_kernel(BalancedParams p)
         int total_seq = 0;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t)
-            total_seq += wave_sum(seg_chunks(d, cx[t]));
+            if (t * kWave < B)             // tiles past the batch hold zeros
+                total_seq += wave_sum(seg_chunks(d, cx[t]));
         T = (int64_t)uniform(total_seq) * K;
         if (T == 0)
             return;
@@ -460,8 +459,11 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
         int total = 0, before = 0, mine = 0;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
+            if (t * kWave >= B)              // tiles past the batch hold zeros
+                break;
             total += wave_sum(c[t]);
-            before += wave_sum(t * kWave + lane < b ? c[t] : 0);
+            if (t * kWave < b)               // tiles wholly past b add nothing
+                before += wave_sum(t * kWave + lane < b ? c[t] : 0);
             mine = (t == b / kWave) ? __shfl(c[t], b % kWave) : mine;
         }
         nc = mine;
