@@ -13,20 +13,18 @@
 // Work decomposition: as in decode.hpp, a wave per (partition, KV head,
 // sequence), but the columns of the matrix-core tiles are now the Q * G
 // (query token, query head) pairs of the KV head's group: column c = 16t + col
-// of tile t is query token c / G, head c % G.  A wave carries up to two tiles
-// (32 columns; its key and value registers serve both, and the accumulators
-// of a third tile would not fit next to the load ring).  With more than 32
-// columns the pairs are split into column groups of two tiles, one wave each;
-// the waves of one (partition, KV head, sequence) are placed on the same XCD
-// at consecutive dispatch slots (workgroups go to the eight XCDs round-robin),
-// so the second wave's reads of the same blocks are served by that XCD's L2.
-// Each tile column keeps its own running maximum and sum.
+// of tile t is query token c / G, head c % G.  One wave carries all of a KV
+// head's pairs, up to four tiles (64 columns); its key and value registers
+// serve every tile, so the cache is read once however many tokens are
+// verified.  The load ring gets shallower as tiles are added (their
+// accumulators take its registers).  Each tile column keeps its own running
+// maximum and sum.
 //
-// Masking: a chunk entirely below the first query's limit (ctx - Q + 1)
-// needs none; the last one or two chunks of a sequence mask each score
-// against its own column's limit, zero value elements at or past ctx, and
-// keep an all-masked column's state finite (reference maximum 0 while the
-// column has seen no position).
+// Masking: each score is checked against its own column's limit and value
+// elements at or past ctx are zeroed, in every chunk (the checks only bite in
+// the last one or two chunks of a sequence; a single code path keeps the
+// loop small enough for the registers); an all-masked column's state stays
+// finite (reference maximum 0 while the column has seen no position).
 #pragma once
 
 #include "decode.hpp"
@@ -34,14 +32,16 @@
 namespace pkv {
 
 constexpr int kMaxQueryTiles = 4;   // Q * G <= 64
-constexpr int kTilesPerWave = 2;
+constexpr int kTilesPerWave = 4;
 constexpr int kXcds = 8;            // MI355X: workgroups are dealt to 8 XCDs in turn
 
-// Chunk buffers per wave: a second tile's accumulators take ring space.
+// Chunk buffers per wave for kTiles tiles (spill-free on gfx950): bf16 4, 3,
+// 3, 2; FP8 5, 4, 3, 2.
 template <class Fmt, int kTiles>
 constexpr int multi_ring_depth()
 {
-    return kTiles == 1 ? Fmt::kRing : (sizeof(typename Fmt::Elem) == 1 ? Fmt::kRing - 1 : 2);
+    return kTiles == 1 ? Fmt::kRing
+                       : kTiles == 2 ? Fmt::kRing - 1 : kTiles == 3 ? 3 : 2;
 }
 
 // One 32-token chunk for kTiles column tiles.  tok0 is the position of this
@@ -160,7 +160,7 @@ void decode_multi_kernel(DecodeParams p)
     int64_t orow[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-        const int c = 16 * (kTilesPerWave * cg + t) + col;
+        const int c = 16 * (kTiles * cg + t) + col;
         live[t] = c < Q * G;
         const int i = live[t] ? c / G : 0;
         const int g = live[t] ? c - (c / G) * G : 0;
@@ -227,10 +227,7 @@ void decode_multi_kernel(DecodeParams p)
             acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Chunks wholly below the first query's limit need no mask.
     const int n_chunks = (end - start + kChunk - 1) / kChunk;
-    const int lim_min = ctx - Q + 1;
-    const int n_plain = lim_min > start ? min((lim_min - start) / kChunk, n_chunks) : 0;
     auto attend = [&](const Regs &r, int ci) {
         // An index the compiler cannot see through, so that the LDS reads stay
         // inside the loop instead of being hoisted back into registers.
@@ -240,12 +237,8 @@ void decode_multi_kernel(DecodeParams p)
             return as_bf16x8(q_lds[(t * (H / 32) + s) * kWave + opaque]);
         };
         const int c0 = start + kChunk * ci;
-        if (ci < n_plain)
-            attend_chunk_multi<Fmt, H, kTiles, false>(r, qfrag, c0 + 8 * quad, lim, ctx - c0,
-                                                      quad, p.scale_log2, m, l, acc);
-        else
-            attend_chunk_multi<Fmt, H, kTiles, true>(r, qfrag, c0 + 8 * quad, lim, ctx - c0,
-                                                     quad, p.scale_log2, m, l, acc);
+        attend_chunk_multi<Fmt, H, kTiles, true>(r, qfrag, c0 + 8 * quad, lim, ctx - c0, quad,
+                                                 p.scale_log2, m, l, acc);
     };
 
     constexpr int kRing = multi_ring_depth<Fmt, kTiles>();

@@ -7,7 +7,7 @@
 // once per fixed partition of the shared region: the columns of the
 // matrix-core tiles are the (sharer, query head) pairs of a KV head's group,
 // so every load of a shared key or value serves all the sharers a wave
-// carries (two tiles, 32 pairs, per wave; more sharers take more waves,
+// carries (up to four tiles, 64 pairs, per wave; more sharers take more waves,
 // placed on one XCD at consecutive slots so their repeated reads meet in
 // its L2).  Each sharer gets the partition's partial (m, l, o) in its own
 // split-K slot, exactly as the per-sequence kernel would have written it; the
@@ -134,9 +134,7 @@ void decode_prefix_kernel(PrefixParams p)
                                                   end - start - kChunk * ci, quad, d.scale_log2,
                                                   m, l, acc);
     };
-    // No masked chunks here: a two-tile wave keeps a deeper ring than in
-    // decode_multi_kernel.
-    constexpr int kRing = kTiles == 1 ? Fmt::kRing : Fmt::kRing - 1;
+    constexpr int kRing = multi_ring_depth<Fmt, kTiles>();
     Regs ring[kRing];
     run_ring<kRing>(d.part / kChunk, ring, issue, attend);
 

@@ -317,15 +317,44 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
                   stream);
 }
 
-// Multi-query decode: kernel for a head dim, tiles per wave (1 or 2) and split.
+// Multi-query decode: kernel for a head dim, tiles per wave (1 to 4) and split.
 template <class Fmt, int H>
 const void *multi_kernel(int tiles, bool split)
 {
-    if (tiles == 1)
-        return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 1, true>
-                     : (const void *)pkv::decode_multi_kernel<Fmt, H, 1, false>;
-    return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 2, true>
-                 : (const void *)pkv::decode_multi_kernel<Fmt, H, 2, false>;
+    switch (tiles) {
+    case 1: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 1, true>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 1, false>;
+    case 2: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 2, true>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 2, false>;
+    case 3: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 3, true>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 3, false>;
+    default: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 4, true>
+                          : (const void *)pkv::decode_multi_kernel<Fmt, H, 4, false>;
+    }
+}
+
+// Tiles per wave of the shared-prefix group kernel: the fewest (most waves,
+// shortest kernel) that still fit one wave per SIMD of the chip; the waves
+// that split an item's columns re-read its blocks from their XCD's L2.
+int prefix_tiles_per_wave(int64_t items, int tiles)
+{
+    constexpr int64_t kWaveSlots = 256 * 4;   // MI355X: 256 CUs x 4 SIMDs
+    for (int pw = 1; pw < pkv::kTilesPerWave && pw < tiles; ++pw)
+        if (items * ceil_div(tiles, pw) <= kWaveSlots)
+            return pw;
+    return tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
+}
+
+// Shared-prefix group kernel for a head dim and tiles per wave (1 to 4).
+template <class Fmt, int H>
+const void *prefix_kernel(int tiles)
+{
+    switch (tiles) {
+    case 1: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 1>;
+    case 2: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 2>;
+    case 3: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 3>;
+    default: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 4>;
+    }
 }
 
 template <class Fmt>
@@ -414,22 +443,17 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     int rc = PKV_OK;
     if (prefix_parts > 0 && p.num_groups > 0) {
         const int tiles = (int)ceil_div((int64_t)p.max_members * (num_heads / num_kv_heads), 16);
-        const int per_wave = tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
+        const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
+        const int per_wave = prefix_tiles_per_wave(items, tiles);
         pkv::PrefixParams pp;
         pp.d = p;
         pp.d.col_groups = (int32_t)ceil_div(tiles, per_wave);
         pp.prefix_parts = (int32_t)prefix_parts;
-        const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
         const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * pp.d.col_groups;
         if (waves > INT32_MAX)
             return PKV_ERR_SHAPE;
-        const void *gk;
-        if (head_dim == 128)
-            gk = per_wave == 1 ? (const void *)pkv::decode_prefix_kernel<Fmt, 128, 1>
-                               : (const void *)pkv::decode_prefix_kernel<Fmt, 128, 2>;
-        else
-            gk = per_wave == 1 ? (const void *)pkv::decode_prefix_kernel<Fmt, 64, 1>
-                               : (const void *)pkv::decode_prefix_kernel<Fmt, 64, 2>;
+        const void *gk = head_dim == 128 ? prefix_kernel<Fmt, 128>(per_wave)
+                                         : prefix_kernel<Fmt, 64>(per_wave);
         rc = launch(gk, dim3((unsigned)waves), dim3(pkv::kWave), &pp, stream);
         if (rc != PKV_OK)
             return rc;

@@ -46,8 +46,10 @@ LAYOUTS = [  # (Q, N, K): Q * N / K (query, head) pairs per KV head
     (4, 32, 8),    # 16: one full tile
     (5, 32, 8),    # 20: two tiles
     (8, 32, 8),    # 32: two full tiles
-    (6, 64, 8),    # 48: two column groups
-    (16, 32, 8),   # 64: two full column groups
+    (6, 64, 8),    # 48: three tiles
+    (7, 64, 8),    # 56: four tiles, the last half used
+    (12, 40, 8),   # 60 (G = 5): four tiles
+    (16, 32, 8),   # 64: four full tiles
     (4, 16, 1),    # MQA: 64
 ]
 

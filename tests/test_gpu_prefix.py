@@ -6,7 +6,8 @@ checked against the oracle's decode (``oracle.decode``) and, bit for bit,
 against ``paged_decode_attention`` with the same partition size: one group
 (the reduced ragged workload and its 20-sharer full size), several groups
 built by re-pointing block tables, more sharers than one wave carries,
-members shorter than the shared span, and FP8 pools.
+every tiles-per-wave choice of the group kernel, members shorter than the
+shared span, and FP8 pools.
 
 ``paged_kv_copy_blocks`` is bit-exact against ``oracle.copy_blocks`` for
 bf16 and FP8 pools, and a copy-on-write divergence (copy a shared block,
@@ -100,13 +101,44 @@ def test_several_groups(partition):
     run_prefix(w, groups, partition, f"three groups part {partition}")
 
 
-def test_many_sharers_span_several_waves():
-    # 12 sharers x G = 8 -> 96 (sharer, head) pairs: three two-tile waves
+@pytest.mark.parametrize("sharers", [5, 8, 12])
+def test_many_sharers(sharers):
+    # sharers x G = 8 (sharer, head) pairs: 40 -> three tiles in one wave,
+    # 64 -> four, 96 -> two waves (four tiles, then two live of four)
     spec = W.Spec("many", B=14, N=64, K=8, H=128, ctx=[600 + 17 * i for i in range(14)],
                   seed=67, max_blocks=60)
     w = W.make(spec)
-    groups = repoint(w, [(3, [0, 1, 2, 4, 5, 6, 7, 8, 9, 10, 11], 30)])
-    run_prefix(w, groups, 64, "12 sharers")
+    others = [i for i in range(14) if i != 3][:sharers - 1]
+    groups = repoint(w, [(3, others, 30)])
+    run_prefix(w, groups, 64, f"{sharers} sharers")
+
+
+def tiles_per_wave(items, tiles):
+    """The library's choice for the group kernel: the fewest tiles per wave
+    whose waves fit one per SIMD (1024 on the chip), at most four."""
+    for pw in range(1, min(4, tiles)):
+        if items * -(-tiles // pw) <= 1024:
+            return pw
+    return min(4, tiles)
+
+
+# (members, shared blocks): K = 8 KV heads, G = 8, partition 32, so
+# items = 8 * shared blocks / 2 and tiles = members / 2
+TILING = [(8, 80, 2), (12, 96, 3), (8, 130, 4)]
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("members,nblk,per_wave", TILING,
+                         ids=[f"{pw}tiles" for _, _, pw in TILING])
+def test_tiles_per_wave(members, nblk, per_wave, kv):
+    items = 8 * (nblk * 16 // 32)
+    assert tiles_per_wave(items, -(-members * 8 // 16)) == per_wave
+    B = members + 1
+    spec = W.Spec("tiling", B=B, N=64, K=8, H=128, kv_dtype=kv,
+                  ctx=[nblk * 16 + 40 + 23 * i for i in range(B)], seed=79)
+    w = W.make(spec)
+    groups = repoint(w, [(0, list(range(2, B)), nblk)])
+    run_prefix(w, groups, 32, f"{members} sharers, {nblk} blocks, {per_wave} tiles per wave")
 
 
 @pytest.mark.parametrize("Hd", [64, 128])
