@@ -78,6 +78,7 @@ typedef enum pkv_status {
 #define PKV_MAX_GROUP 16           /* largest N / K (query heads per KV head)     */
 #define PKV_PARTITION_GRAIN 32     /* partition sizes are multiples of this       */
 #define PKV_MAX_PARTITION 1024
+#define PKV_MAX_MQ_PARTITION (1 << 20)  /* partition cap of the multi-query call  */
 #define PKV_MAX_QUERY_ROWS 64      /* num_queries * (N / K) for the multi-query call */
 #define PKV_MAX_PREFIX_ROWS 1024   /* max_members * (N / K) for the prefix-aware call */
 
@@ -149,9 +150,14 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  *                     holds at once, whatever the mix of context lengths
  *                     (three kernel launches);
  *                  P  fixed partitions of P tokens (a multiple of 32 in
- *                     [32, 1024]) of each sequence, one wave each (two
- *                     launches; one when a single partition covers
- *                     max_context_len).
+ *                     [32, 1024]) of each sequence.  When one partition
+ *                     covers max_context_len: one wave per (KV head,
+ *                     sequence), one launch.  Otherwise each wave of the
+ *                     token-balanced schedule takes a run of whole
+ *                     partitions and writes each one's partial, then the
+ *                     merge over partitions (two launches, three when
+ *                     num_seqs > 256); the result is the same as one wave
+ *                     per partition.
  *   workspace, workspace_bytes   device scratch of at least
  *                  paged_decode_workspace_size(...) bytes, 16-byte aligned;
  *                  may be NULL when that size is 0.  Its contents on entry
@@ -238,7 +244,11 @@ int paged_decode_attention_fp8(float *out, const void *q,
  *   kv_dtype       PKV_KV_BF16 (k_scale, v_scale ignored) or PKV_KV_FP8_E4M3
  *                  (pools of E4M3 codes; scales as for the _fp8 calls).
  *   num_queries    Q >= 1 with Q * (N / K) <= PKV_MAX_QUERY_ROWS.
- *   partition_size fixed partitions only: a multiple of 32 in [32, 1024].
+ *   partition_size fixed partitions only: a multiple of 32 in
+ *                  [32, PKV_MAX_MQ_PARTITION].  One wave per (partition, KV
+ *                  head, sequence, column group); a partition size that
+ *                  gives about as many waves as the device holds at once (4
+ *                  per CU) fills it in a single round.
  *   workspace      at least paged_decode_mq_workspace_size(num_seqs,
  *                  num_queries, num_heads, head_dim, max_context_len,
  *                  partition_size) bytes (0 when one partition covers

@@ -23,6 +23,16 @@
 // A one-workgroup schedule kernel runs first: it scans the context lengths
 // into chunk offsets cs[b] (exclusive prefix sum of nc_b) and writes each
 // wave's starting (b, kvh, chunk) so that a wave needs one load to begin.
+//
+// Fixed partitions (kFixed, part_chunks chunks each) run on the same
+// schedule: both ends of every wave's range move down to a partition
+// boundary (a multiple of part_chunks chunks, counted from position 0 of the
+// sequence), so each partition belongs to one wave, and a piece also ends at
+// every partition boundary.  Each partition's partial (m, l, o) goes to its
+// split-K slot, as the one-wave-per-partition grid would have written it
+// (the same chunks in the same order), and the log-sum-exp merge over
+// partitions finishes the rows.  The waves keep their load pipelines full
+// across partitions instead of paying a start-up per partition.
 #pragma once
 
 #include "decode.hpp"
@@ -44,6 +54,8 @@ struct BalancedParams {
     int32_t log2_waves;           // log2(W)
     int32_t num_seqs;             // B
     int32_t inline_schedule;      // 1: small batch, waves scan the context lengths themselves
+    int32_t part_chunks;          // kFixed: chunks per partition (partials to d.part_o /
+                                  // d.part_ml); else unused
 };
 
 constexpr int kInlineScheduleSeqs = 256;   // largest B scanned inside every wave
@@ -194,6 +206,18 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
 
 // ------------------------------------------------------------------ decode --
 
+// Staged results of the decode waves (see decode_balanced_kernel).
+constexpr uint32_t kStageDead = 0;      // lane of a column past the group: nothing
+constexpr uint32_t kStageFinal = 1;     // a whole segment: normalised row of `out`
+constexpr uint32_t kStagePiece = 2;     // a piece: piece_o / piece_ml row
+constexpr uint32_t kStagePartial = 3;   // a fixed partition: part_o / part_ml row
+
+// LDS a decode wave stages finished pieces in (eight pieces of a group of 8
+// at H = 128): with the per-column records 37 KiB per wave, so four waves
+// per CU fit in its 160 KiB.
+constexpr int kStageBytes = 32 * 1024;
+constexpr int kStageMax = 16;      // pieces staged at most
+
 // Position of one chunk in the flattened order: segment (b, kvh), chunk j of
 // the nc chunks of sequence b (ctx tokens); the segment's chunk j covers
 // positions 32 * (fc + j) .. (fc counts the chunks before the sliding window).
@@ -209,7 +233,7 @@ struct BalancedBuf {
     u32x4 q[H / 32];
 };
 
-template <class Fmt, int H>
+template <class Fmt, int H, bool kFixed = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
@@ -230,6 +254,7 @@ void decode_balanced_kernel(BalancedParams p)
     // kernel's table.
     int64_t T;
     int4 st = make_int4(0, 0, 0, 0);
+    int4 st_end = make_int4(0, 0, 0, 0);   // kFixed: the position of c_end (z, w used)
     int c_begin, c_end;
     if (p.inline_schedule) {
         constexpr int kTiles = kInlineScheduleSeqs / kWave;
@@ -252,9 +277,10 @@ void decode_balanced_kernel(BalancedParams p)
         if (c_begin >= c_end)
             return;
         // The sequence holding chunk c_begin: the last b whose chunks start at
-        // or before it (empty sequences start where the next one does).
+        // or before it (empty sequences start where the next one does).  With
+        // fixed partitions, also the position of c_end (the next wave's start).
         int carry = 0;
-        bool found = false;
+        bool found = false, found_end = !kFixed || c_end >= T;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             const int nc = seg_chunks(d, cx[t]);
@@ -271,6 +297,16 @@ void decode_balanced_kernel(BalancedParams p)
                 st = make_int4(t * kWave + src, kvh, local - kvh * ncb, __shfl(cx[t], src));
                 found = true;
             }
+            if (kFixed && !found_end && (int64_t)(carry + tile_total) * K > c_end) {
+                const int excl = carry + incl - nc;
+                const uint64_t mask = __builtin_amdgcn_ballot_w64(t * kWave + lane < B &&
+                                                                  (int64_t)excl * K <= c_end);
+                const int src = 63 - __builtin_clzll(mask);
+                const int ncb = __shfl(nc, src);
+                const int local = c_end - __shfl(excl, src) * K;
+                st_end = make_int4(0, 0, local - (local / ncb) * ncb, __shfl(cx[t], src));
+                found_end = true;
+            }
             carry += tile_total;
         }
     } else {
@@ -282,6 +318,25 @@ void decode_balanced_kernel(BalancedParams p)
         if (c_begin >= c_end)
             return;
         st = p.wave_start[wv];
+        if (kFixed && c_end < T)
+            st_end = p.wave_start[wv + 1];
+    }
+    const int pc = p.part_chunks;
+    if constexpr (kFixed) {
+        // Fixed partitions: move both ends down to a partition boundary (the
+        // next wave moves its start the same way).  back(j, ctx): chunks from
+        // the start of chunk j's partition (or of the segment) to chunk j.
+        auto back = [&](int j, int ctx) {
+            const int fc = first_chunk(d, min(max(ctx, 0), d.max_ctx));
+            return j - (max(fc, ((fc + j) / pc) * pc) - fc);
+        };
+        const int ob = back(uniform(st.z), uniform(st.w));
+        const int oe = c_end < T ? back(uniform(st_end.z), uniform(st_end.w)) : 0;
+        c_begin -= ob;
+        st.z = uniform(st.z) - ob;
+        c_end -= oe;
+        if (c_begin >= c_end)
+            return;
     }
     const int total = c_end - c_begin;           // chunks of this wave
 
@@ -364,6 +419,49 @@ void decode_balanced_kernel(BalancedParams p)
     for (int c = 0; c < H / 16; ++c)
         acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool piece_from_start = start.j == 0;   // this wave's piece began at the segment start
+
+    // Finished pieces are staged in LDS (each lane its own values, the
+    // quad-0 lane of a column its row, m and l) and written out once the
+    // load pipeline has drained, or when the stage is
+    // full: a global store issued while chunk loads are in flight turns the
+    // next wait for chunk data into a wait for everything outstanding
+    // (loads and stores share one completion counter and may complete out
+    // of order), which stalls the wave for a full memory latency.
+    // Only the G live columns are kept: a piece takes G * H * 4 bytes, so
+    // the stage holds more pieces for smaller groups (up to kStageMax).
+    __shared__ f32x4 stage_o[kStageBytes / 16];
+    __shared__ int64_t stage_row[kStageMax][16];   // destination row of each column
+    __shared__ float stage_m[kStageMax][16];
+    __shared__ float stage_l[kStageMax][16];
+    __shared__ uint32_t stage_kind[kStageMax][16];
+    const int G = d.group;
+    const int slot_vecs = G * H / 4;                // f32x4 per staged piece
+    const int cap = min(kStageMax, (kStageBytes / 16) / slot_vecs);
+    int staged = 0;
+    auto flush = [&]() {
+        if (live) {
+            for (int s = 0; s < staged; ++s) {
+                const uint32_t kind = stage_kind[s][col];
+                const int64_t row = stage_row[s][col];
+                float *o = (kind == kStageFinal ? d.out
+                                                : kind == kStagePiece ? p.piece_o : d.part_o) +
+                           row * H;
+                const f32x4 *src = stage_o + s * slot_vecs + quad * G + col;
+#pragma unroll
+                for (int c = 0; c < H / 16; ++c)
+                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = src[4 * c * G];
+                if (kind != kStageFinal && quad == 0) {
+                    float *ml = kind == kStagePiece ? p.piece_ml : d.part_ml;
+                    ml[2 * row] = stage_m[s][col];
+                    ml[2 * row + 1] = stage_l[s][col];
+                }
+            }
+        }
+        staged = 0;
+    };
+    // kFixed: partition of the current chunk and chunks left in it
+    // (counting the current one); divisions only where a segment begins.
+    int pidx = 0, pleft = 0;
     auto qfrag = [&](int s) { return as_bf16x8(qcur[s]); };
 
     auto attend = [&](const Buf &r, int k) {
@@ -373,6 +471,11 @@ void decode_balanced_kernel(BalancedParams p)
 #pragma unroll
             for (int s = 0; s < H / 32; ++s)
                 qcur[s] = r.q[s];
+            if constexpr (kFixed) {
+                const int a = ap.fc + ap.j;
+                pidx = a / pc;
+                pleft = pc - (a - pidx * pc);
+            }
         }
         const bool seg_end = ap.j + 1 == ap.nc;
         // Leading positions of a segment's first chunk before the window start.
@@ -382,40 +485,63 @@ void decode_balanced_kernel(BalancedParams p)
         else
             attend_chunk<Fmt, H, true>(r.kv, qfrag, ap.ctx - kChunk * (ap.fc + ap.j), head, quad,
                                        d.scale_log2, m, l, acc);
-        if (!seg_end && k + 1 < total)
-            return;
-        // The piece ends here (segment end, or the wave's last chunk).
+        if constexpr (kFixed) {
+            if (!seg_end && pleft != 1 && k + 1 < total) {
+                --pleft;
+                return;
+            }
+        } else {
+            if (!seg_end && k + 1 < total)
+                return;
+        }
+        // The piece ends here (segment end, partition end with kFixed, or the
+        // wave's last chunk): stage it.
+        if (staged == cap)
+            flush();
         const float lt = sum_over_rows(l);
-        const int n = ap.kvh * d.group + col;
         if (live) {
-            if (piece_from_start && seg_end) {          // the whole segment: final output
-                const float inv = d.out_scale / lt;
-                float *o = d.out + ((int64_t)ap.b * d.num_heads + n) * H;
-#pragma unroll
-                for (int c = 0; c < H / 16; ++c)
-                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
+            const int n = ap.kvh * G + col;
+            uint32_t kind;
+            int64_t row;
+            float scl = d.out_scale;
+            if (kFixed) {                               // a partition's split-K partial
+                kind = kStagePartial;
+                row = ((int64_t)ap.b * d.num_heads + n) * d.num_parts + pidx;
+            } else if (piece_from_start && seg_end) {   // the whole segment: final output
+                kind = kStageFinal;
+                row = (int64_t)ap.b * d.num_heads + n;
+                scl = d.out_scale / lt;
             } else {
-                const int64_t slot = ((int64_t)wv + (int64_t)ap.b * K + ap.kvh) * d.group + col;
-                float *o = p.piece_o + slot * H;
+                kind = kStagePiece;
+                row = ((int64_t)wv + (int64_t)ap.b * K + ap.kvh) * G + col;
+            }
+            f32x4 *dst = stage_o + staged * slot_vecs + quad * G + col;
 #pragma unroll
-                for (int c = 0; c < H / 16; ++c)
-                    *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * d.out_scale;
-                if (quad == 0) {
-                    p.piece_ml[2 * slot] = m;
-                    p.piece_ml[2 * slot + 1] = lt;
-                }
+            for (int c = 0; c < H / 16; ++c)
+                dst[4 * c * G] = acc[c] * scl;
+            if (quad == 0) {
+                stage_kind[staged][col] = kind;
+                stage_row[staged][col] = row;
+                stage_m[staged][col] = m;
+                stage_l[staged][col] = lt;
             }
         }
+        ++staged;
         m = -INFINITY;
         l = 0.f;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
             acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         piece_from_start = true;                    // the next piece opens a segment
+        if constexpr (kFixed) {                     // the next chunk opens a partition
+            ++pidx;
+            pleft = pc;
+        }
     };
 
     Buf ring[Fmt::kBalancedRing];
     run_ring<Fmt::kBalancedRing>(total, ring, issue, attend);
+    flush();
 }
 
 // ------------------------------------------------------------------- merge --

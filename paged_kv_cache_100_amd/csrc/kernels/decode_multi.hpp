@@ -146,10 +146,6 @@ void decode_multi_kernel(DecodeParams p)
     const int start = part_idx * p.part;
     const int first_block = start / kBlockSize;
     const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks + first_block;
-    const int table_avail = min(p.part / kBlockSize, p.max_blocks - first_block);
-    int my_id = 0;
-    if (lane < table_avail)
-        my_id = table[lane];
 
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
 
@@ -184,7 +180,7 @@ void decode_multi_kernel(DecodeParams p)
     }
     const int end = min(start + p.part, ctx);
     const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
-    my_id = clamp_block(my_id, p.num_blocks);
+    const int n_chunks = (end - start + kChunk - 1) / kChunk;
 
     // The query fragments live in this wave's LDS (each lane reads back only
     // what it wrote): registers go to the accumulators and the chunk ring.
@@ -208,12 +204,20 @@ void decode_multi_kernel(DecodeParams p)
     const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
     const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
 
+    // A chunk's two block ids come from scalar loads made one chunk ahead,
+    // so a partition may span any number of blocks.
+    int id0 = 0, id1 = 0;
+    auto load_ids = [&](int ci) {
+        id0 = clamp_block(scalar_load(table + 2 * ci), p.num_blocks);
+        id1 = 2 * ci + 1 < n_blocks ? clamp_block(scalar_load(table + 2 * ci + 1), p.num_blocks)
+                                    : id0;
+    };
+    load_ids(0);
     auto issue = [&](Regs &r, int ci) {
-        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
-        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
-                                                : id0;
         Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
                               vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+        if (ci + 1 < n_chunks)
+            load_ids(ci + 1);
     };
 
     float m[kTiles], l[kTiles];
@@ -227,7 +231,6 @@ void decode_multi_kernel(DecodeParams p)
             acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int n_chunks = (end - start + kChunk - 1) / kChunk;
     auto attend = [&](const Regs &r, int ci) {
         // An index the compiler cannot see through, so that the LDS reads stay
         // inside the loop instead of being hoisted back into registers.

@@ -17,24 +17,62 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 4;
+constexpr int kVersionMinor = 5;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Fixed-partition mode: bytes of partial results ([B][N][P][H] o, then
-// [B][N][P][2] (m, l)); 0 when one partition covers the context.
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Fixed-partition mode: partial results ([B][N][P][H] o, then [B][N][P][2]
+// (m, l)), then the schedule of the single-query path's persistent waves
+// (T, chunk offsets, wave starts); 0 bytes when one partition covers the
+// context.
+struct FixedLayout {
+    size_t total, part_o, part_ml, total_chunks, chunk_start, wave_start;
+};
+
+FixedLayout fixed_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_ctx,
+                         int32_t part)
+{
+    FixedLayout L{};
+    const int64_t parts = ceil_div(max_ctx, part);
+    if (parts <= 1)
+        return L;
+    const int64_t rows = (int64_t)num_seqs * num_heads * parts;
+    size_t off = 0;
+    L.part_o = off;
+    off = align256(off + (size_t)(rows * head_dim * 4));
+    L.part_ml = off;
+    off = align256(off + (size_t)(rows * 2 * 4));
+    L.total_chunks = off;
+    off = align256(off + 16);
+    L.chunk_start = off;
+    off = align256(off + (size_t)(num_seqs + 1) * 4);
+    L.wave_start = off;
+    off = align256(off + (size_t)pkv::kMaxBalancedWaves * 16);
+    L.total = off;
+    return L;
+}
+
 size_t fixed_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                              int32_t max_ctx, int32_t part)
+{
+    return fixed_layout(num_seqs, num_heads, head_dim, max_ctx, part).total;
+}
+
+// The partials alone (the multi-query and prefix-group paths, which run one
+// wave per partition and need no schedule).
+size_t partials_bytes(int32_t num_rows, int32_t num_heads, int32_t head_dim, int32_t max_ctx,
+                      int32_t part)
 {
     const int64_t parts = ceil_div(max_ctx, part);
     if (parts <= 1)
         return 0;
-    const int64_t rows = (int64_t)num_seqs * num_heads * parts;
-    const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
-    return (size_t)(o_bytes + rows * 2 * 4);
+    const int64_t rows = (int64_t)num_rows * num_heads * parts;
+    return align256((size_t)(rows * head_dim * 4)) + (size_t)(rows * 2 * 4);
 }
 
 // Token-balanced mode: the layout of its workspace, sized for the largest
@@ -42,8 +80,6 @@ size_t fixed_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_d
 struct BalancedLayout {
     size_t total, chunk_start, total_chunks, wave_start, piece_ml, piece_o;
 };
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                int32_t head_dim)
@@ -254,6 +290,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
         bp.log2_waves = log2_waves;
         bp.num_seqs = num_seqs;
         bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
+        bp.part_chunks = 0;
         if (!bp.inline_schedule) {
             rc = launch((const void *)pkv::schedule_kernel, dim3(1), dim3(pkv::kScheduleThreads),
                         &bp, stream);
@@ -270,34 +307,56 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
                       stream);
     }
 
-    // Fixed partitions of partition_size tokens, one wave each.
+    // Fixed partitions of partition_size tokens.  One partition: one wave per
+    // (KV head, sequence) writes the output.  Several: persistent waves on
+    // the token-balanced schedule, each taking a run of whole partitions and
+    // writing their partials, then the merge over partitions.
     const int32_t part = partition_size;
     const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
     const bool split = parts > 1;
-    if (split) {
-        const size_t need = fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
-                                                  part);
-        if (!workspace || workspace_bytes < need)
-            return PKV_ERR_WORKSPACE;
-        if (!aligned16(workspace))
-            return PKV_ERR_ALIGN;
-        const int64_t rows = (int64_t)num_seqs * num_heads * parts;
-        const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
-        p.part_o = static_cast<float *>(workspace);
-        p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
-    }
     p.num_parts = (int32_t)parts;
-
-    const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
-    const void *kern;
-    if (head_dim == 128)
-        kern = split ? (const void *)pkv::decode_kernel<Fmt, 128, true>
-                     : (const void *)pkv::decode_kernel<Fmt, 128, false>;
-    else
-        kern = split ? (const void *)pkv::decode_kernel<Fmt, 64, true>
-                     : (const void *)pkv::decode_kernel<Fmt, 64, false>;
-    int rc = launch(kern, grid, dim3(pkv::kWave), &p, stream);
-    if (rc != PKV_OK || !split)
+    if (!split) {
+        const dim3 grid(1u, (unsigned)num_kv_heads, (unsigned)num_seqs);
+        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, false>
+                                           : (const void *)pkv::decode_kernel<Fmt, 64, false>;
+        return launch(kern, grid, dim3(pkv::kWave), &p, stream);
+    }
+    const FixedLayout FL = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, part);
+    if (!workspace || workspace_bytes < FL.total)
+        return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return PKV_ERR_ALIGN;
+    if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
+        return PKV_ERR_SHAPE;
+    char *ws = static_cast<char *>(workspace);
+    p.part_o = reinterpret_cast<float *>(ws + FL.part_o);
+    p.part_ml = reinterpret_cast<float *>(ws + FL.part_ml);
+    int log2_waves = 0;
+    int rc = device_waves(&log2_waves);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::BalancedParams bp;
+    bp.d = p;
+    bp.total_chunks = reinterpret_cast<int32_t *>(ws + FL.total_chunks);
+    bp.chunk_start = reinterpret_cast<int32_t *>(ws + FL.chunk_start);
+    bp.wave_start = reinterpret_cast<int4 *>(ws + FL.wave_start);
+    bp.piece_o = nullptr;
+    bp.piece_ml = nullptr;
+    bp.num_waves = 1 << log2_waves;
+    bp.log2_waves = log2_waves;
+    bp.num_seqs = num_seqs;
+    bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
+    bp.part_chunks = part / pkv::kChunk;
+    if (!bp.inline_schedule) {
+        rc = launch((const void *)pkv::schedule_kernel, dim3(1), dim3(pkv::kScheduleThreads), &bp,
+                    stream);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true>
+                                     : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true>;
+    rc = launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+    if (rc != PKV_OK)
         return rc;
 
     pkv::MergeParams mp;
@@ -366,7 +425,7 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
     const bool split = parts > 1;
     if (split) {
-        const size_t need = fixed_workspace_bytes(num_seqs * num_queries, num_heads, head_dim,
+        const size_t need = partials_bytes(num_seqs * num_queries, num_heads, head_dim,
                                                   max_context_len, part);
         if (!workspace || workspace_bytes < need)
             return PKV_ERR_WORKSPACE;
@@ -427,7 +486,7 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
                                            : (const void *)pkv::decode_kernel<Fmt, 64, false>;
         return launch(kern, grid, dim3(pkv::kWave), &p, stream);
     }
-    const size_t need = fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, part);
+    const size_t need = partials_bytes(num_seqs, num_heads, head_dim, max_context_len, part);
     if (!workspace || workspace_bytes < need)
         return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace))
@@ -603,7 +662,7 @@ size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int
     if (num_seqs <= 0 || num_queries <= 0 || num_heads <= 0 || head_dim <= 0 ||
         max_context_len <= 0 || partition_size <= 0)
         return 0;
-    return fixed_workspace_bytes((int32_t)((int64_t)num_seqs * num_queries > INT32_MAX
+    return partials_bytes((int32_t)((int64_t)num_seqs * num_queries > INT32_MAX
                                                ? INT32_MAX
                                                : (int64_t)num_seqs * num_queries),
                                  num_heads, head_dim, max_context_len, partition_size);
@@ -634,7 +693,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
         return PKV_ERR_SHAPE;
     if ((int64_t)num_seqs * num_queries > 65535 || num_kv_heads > 65535)
         return PKV_ERR_SHAPE;
-    if (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_PARTITION ||
+    if (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_MQ_PARTITION ||
         partition_size % PKV_PARTITION_GRAIN != 0)
         return PKV_ERR_SHAPE;
     if (kv_dtype == PKV_KV_BF16) {

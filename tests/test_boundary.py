@@ -47,7 +47,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.4"
+    assert pkv.version() == "1.5"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -147,6 +147,8 @@ def test_decode_mq_checks(L):
     assert decode_mq(L, Q=16, N=8, K=2) != UNSUP           # 64 rows: allowed
     assert decode_mq(L, part=0) == SHAPE                   # fixed partitions only
     assert decode_mq(L, part=48) == SHAPE
+    assert decode_mq(L, part=(1 << 20) + 32) == SHAPE       # past PKV_MAX_MQ_PARTITION
+    assert decode_mq(L, part=4096, maxblk=512, maxctx=8192) != SHAPE   # > 1024: allowed here
     assert decode_mq(L, H=96) == UNSUP
     assert decode_mq(L, maxctx=257) == SHAPE
     assert decode_mq(L, B=40000, Q=2) == SHAPE             # B * Q rows of the merge grid
@@ -215,9 +217,13 @@ def test_decode_window_checks(L):
 def test_workspace_sizes(L):
     # fixed partitions: one partition covers the context -> no workspace
     assert pkv.workspace_size(4, 8, 2, 64, 32, 32) == 0
-    # B=4, N=64, H=128, 256 partitions of 512: o (B*N*P*H*4) then (m, l) (B*N*P*2*4)
+    # B=4, N=64, H=128, 256 partitions of 512: o (B*N*P*H*4) then (m, l)
+    # (B*N*P*2*4), then the persistent waves' schedule (T; B + 1 chunk
+    # offsets; 16 bytes per wave for up to 4096 waves), each part 256-aligned
     rows = 4 * 64 * 256
-    assert pkv.workspace_size(4, 64, 8, 128, 131072, 512) == rows * 128 * 4 + rows * 8
+    a256 = lambda x: -(-x // 256) * 256
+    assert pkv.workspace_size(4, 64, 8, 128, 131072, 512) == (
+        a256(rows * 128 * 4) + a256(rows * 8) + 256 + a256(5 * 4) + a256(4096 * 16))
     # token-balanced: independent of the context bound, grows with B*K
     a = pkv.workspace_size(64, 32, 8, 128, 8192, 0)
     assert a > 0 and a == pkv.workspace_size(64, 32, 8, 128, 100, 0)

@@ -72,6 +72,15 @@ def test_context_edges(kv, partition):
     run_case(spec, partition, f"edges Q=5 {kv} part {partition}")
 
 
+@pytest.mark.parametrize("partition", [1056, 2080, 4096])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_partitions_past_1024(kv, partition):
+    # partitions of more than 64 blocks: their block ids are read one chunk ahead
+    spec = W.Spec("long parts", B=4, N=64, K=8, H=128, ctx=[5000, 2100, 40, 4097], queries=3,
+                  seed=61, kv_dtype=kv)
+    run_case(spec, partition, f"Q=3 {kv} part {partition}")
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_b64_ctx8k_spec4", "llama3_70b_b64_ctx4k_spec6"])
 def test_fp8_pools(name):
     spec = dataclasses.replace(W.small(name), kv_dtype="fp8")
