@@ -224,17 +224,16 @@ __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&i
     }
 }
 
-// kPrefix: prefix-aware decode; partitions the sequence's prefix group
-// computes are skipped (their split-K slots are written by that group).
-template <class Fmt, int H, bool kSplit, bool kPrefix = false>
+// One wave per (partition, KV head, sequence).  The library launches it with
+// one partition per sequence (kSplit false); several partitions run on the
+// persistent waves of decode_balanced.hpp, which compute the same partials.
+template <class Fmt, int H, bool kSplit>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
     const int part_idx = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
-    if (kPrefix && part_idx < prefix_shared_parts(p, b))
-        return;
     const int lane = threadIdx.x;
     const int col = lane & 15;    // query head within the group (tile column)
     const int quad = lane >> 4;   // 0..3

@@ -63,14 +63,21 @@ constexpr int kInlineScheduleSeqs = 256;   // largest B scanned inside every wav
 __device__ __forceinline__ int chunks_of(int ctx) { return (ctx + kChunk - 1) / kChunk; }
 
 // A segment's chunks run from the 32-token boundary at or below the sliding
-// window's start (0 without a window) to the end of the context.
-__device__ __forceinline__ int first_chunk(const DecodeParams &d, int ctx)
+// window's start (0 without a window) to the end of the context of sequence
+// b.  kPrefix (shared-prefix decode, fixed partitions, no window): from the
+// end of the partitions that b's prefix group computes for it.
+template <bool kPrefix = false>
+__device__ __forceinline__ int first_chunk(const DecodeParams &d, int b, int ctx)
 {
-    return window_start(d, ctx) / kChunk;
+    if constexpr (kPrefix)
+        return ctx > 0 ? prefix_shared_parts(d, b) * (d.part / kChunk) : 0;
+    else
+        return window_start(d, ctx) / kChunk;
 }
-__device__ __forceinline__ int seg_chunks(const DecodeParams &d, int ctx)
+template <bool kPrefix = false>
+__device__ __forceinline__ int seg_chunks(const DecodeParams &d, int b, int ctx)
 {
-    return chunks_of(ctx) - first_chunk(d, ctx);
+    return chunks_of(ctx) - first_chunk<kPrefix>(d, b, ctx);
 }
 
 // Uniform (scalar) value of a load whose address is the same in every lane.
@@ -125,6 +132,7 @@ __device__ __forceinline__ int wave_of(int64_t c, int64_t T, int log2W)
 
 // ---------------------------------------------------------------- schedule --
 
+template <bool kPrefix = false>
 __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedParams p)
 {
     __shared__ int32_t incl[kScheduleThreads];   // inclusive prefix of nc within the tile
@@ -139,7 +147,7 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
     // Pass 1: T = K * sum_b nc_b (needed to place the wave boundaries).
     int mine = 0;
     for (int b = tid; b < B; b += kScheduleThreads)
-        mine += seg_chunks(p.d, seq_ctx(p.d, b));
+        mine += seg_chunks<kPrefix>(p.d, b, seq_ctx(p.d, b));
     incl[tid] = mine;
     __syncthreads();
     for (int off = kScheduleThreads / 2; off >= 1; off >>= 1) {
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(BalancedPara
     // falls in this tile, found by binary search over the tile's prefix sums.
     for (int base = 0; base < B; base += kScheduleThreads) {
         const int b = base + tid;
-        const int nc = b < B ? seg_chunks(p.d, seq_ctx(p.d, b)) : 0;
+        const int nc = b < B ? seg_chunks<kPrefix>(p.d, b, seq_ctx(p.d, b)) : 0;
         incl[tid] = nc;
         __syncthreads();
         for (int off = 1; off < kScheduleThreads; off <<= 1) {   // Hillis-Steele scan
@@ -233,7 +241,7 @@ struct BalancedBuf {
     u32x4 q[H / 32];
 };
 
-template <class Fmt, int H, bool kFixed = false>
+template <class Fmt, int H, bool kFixed = false, bool kPrefix = false>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
@@ -254,7 +262,7 @@ void decode_balanced_kernel(BalancedParams p)
     // kernel's table.
     int64_t T;
     int4 st = make_int4(0, 0, 0, 0);
-    int4 st_end = make_int4(0, 0, 0, 0);   // kFixed: the position of c_end (z, w used)
+    int4 st_end = make_int4(0, 0, 0, 0);   // kFixed: the position of c_end (x, z, w used)
     int c_begin, c_end;
     if (p.inline_schedule) {
         constexpr int kTiles = kInlineScheduleSeqs / kWave;
@@ -268,7 +276,7 @@ void decode_balanced_kernel(BalancedParams p)
 #pragma unroll
         for (int t = 0; t < kTiles; ++t)
             if (t * kWave < B)             // tiles past the batch hold zeros
-                total_seq += wave_sum(seg_chunks(d, cx[t]));
+                total_seq += wave_sum(seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]));
         T = (int64_t)uniform(total_seq) * K;
         if (T == 0)
             return;
@@ -283,7 +291,7 @@ void decode_balanced_kernel(BalancedParams p)
         bool found = false, found_end = !kFixed || c_end >= T;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
-            const int nc = seg_chunks(d, cx[t]);
+            const int nc = seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]);
             const int incl = wave_inclusive_scan(nc, lane);
             const int tile_total = __shfl(incl, kWave - 1);
             if (!found && (int64_t)(carry + tile_total) * K > c_begin) {
@@ -304,7 +312,8 @@ void decode_balanced_kernel(BalancedParams p)
                 const int src = 63 - __builtin_clzll(mask);
                 const int ncb = __shfl(nc, src);
                 const int local = c_end - __shfl(excl, src) * K;
-                st_end = make_int4(0, 0, local - (local / ncb) * ncb, __shfl(cx[t], src));
+                st_end = make_int4(t * kWave + src, 0, local - (local / ncb) * ncb,
+                                   __shfl(cx[t], src));
                 found_end = true;
             }
             carry += tile_total;
@@ -324,14 +333,15 @@ void decode_balanced_kernel(BalancedParams p)
     const int pc = p.part_chunks;
     if constexpr (kFixed) {
         // Fixed partitions: move both ends down to a partition boundary (the
-        // next wave moves its start the same way).  back(j, ctx): chunks from
-        // the start of chunk j's partition (or of the segment) to chunk j.
-        auto back = [&](int j, int ctx) {
-            const int fc = first_chunk(d, min(max(ctx, 0), d.max_ctx));
+        // next wave moves its start the same way).  back(b, j, ctx): chunks
+        // from the start of chunk j's partition (or of the segment) to chunk j.
+        auto back = [&](int b, int j, int ctx) {
+            const int fc = first_chunk<kPrefix>(d, b, min(max(ctx, 0), d.max_ctx));
             return j - (max(fc, ((fc + j) / pc) * pc) - fc);
         };
-        const int ob = back(uniform(st.z), uniform(st.w));
-        const int oe = c_end < T ? back(uniform(st_end.z), uniform(st_end.w)) : 0;
+        const int ob = back(uniform(st.x), uniform(st.z), uniform(st.w));
+        const int oe =
+            c_end < T ? back(uniform(st_end.x), uniform(st_end.z), uniform(st_end.w)) : 0;
         c_begin -= ob;
         st.z = uniform(st.z) - ob;
         c_end -= oe;
@@ -345,16 +355,18 @@ void decode_balanced_kernel(BalancedParams p)
     start.kvh = uniform(st.y);
     start.j = uniform(st.z);
     start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
-    start.nc = seg_chunks(d, start.ctx);
-    start.fc = first_chunk(d, start.ctx);
+    start.nc = seg_chunks<kPrefix>(d, start.b, start.ctx);
+    start.fc = first_chunk<kPrefix>(d, start.b, start.ctx);
     if (start.j >= start.nc)          // cannot happen for a consistent schedule
         return;
 
     // The chunk after q in flattened order (the caller knows one exists).
-    auto next_seq = [&](int b) {      // next sequence after b with tokens
+    auto next_seq = [&](int b) {      // next sequence after b with chunks
         int nb = b + 1;
         int ctx = nb < B ? seq_ctx_uniform(d, nb) : 0;
-        while (ctx == 0 && nb + 1 < B) {
+        // Without kPrefix only an empty context has no chunks; with it, so has
+        // a sharer whose context lies wholly in its group's partitions.
+        while ((kPrefix ? seg_chunks<kPrefix>(d, nb, ctx) == 0 : ctx == 0) && nb + 1 < B) {
             ++nb;
             ctx = seq_ctx_uniform(d, nb);
         }
@@ -370,8 +382,8 @@ void decode_balanced_kernel(BalancedParams p)
         const int2 nx = next_seq(q.b);
         q.b = nx.x;
         q.ctx = nx.y;
-        q.nc = seg_chunks(d, q.ctx);
-        q.fc = first_chunk(d, q.ctx);
+        q.nc = seg_chunks<kPrefix>(d, q.b, q.ctx);
+        q.fc = first_chunk<kPrefix>(d, q.b, q.ctx);
     };
 
     const int64_t tile_elems = (int64_t)kBlockSize * H;
@@ -580,7 +592,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             const int bb = t * kWave + lane;
-            c[t] = bb < B ? seg_chunks(d, seq_ctx(d, bb)) : 0;
+            c[t] = bb < B ? seg_chunks(d, bb, seq_ctx(d, bb)) : 0;
         }
         int total = 0, before = 0, mine = 0;
 #pragma unroll
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
         T = (int64_t)total * K;
         seq_first = before;
     } else {
-        nc = seg_chunks(d, seq_ctx_uniform(d, b));
+        nc = seg_chunks(d, b, seq_ctx_uniform(d, b));
         T = scalar_load(p.total_chunks);
         seq_first = scalar_load(p.chunk_start + b);
     }

@@ -193,6 +193,55 @@ bool valid_pool_scale(float s)
 }
 
 // Both decode entry points: bf16 pools (k_scale = v_scale = 1) or FP8 pools.
+// Fixed partitions (several) on persistent waves: schedule (large batches),
+// then the balanced kernel in partition mode writing every partition's
+// partial to the workspace's split-K slots; the caller launches the merge.
+// kPrefix: sequences skip the partitions their prefix group computes.
+template <class Fmt, bool kPrefix>
+int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t max_context_len, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    const int32_t part = p.part;
+    const FixedLayout FL = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, part);
+    if (!workspace || workspace_bytes < FL.total)
+        return PKV_ERR_WORKSPACE;
+    if (!aligned16(workspace))
+        return PKV_ERR_ALIGN;
+    if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
+        return PKV_ERR_SHAPE;
+    char *ws = static_cast<char *>(workspace);
+    p.part_o = reinterpret_cast<float *>(ws + FL.part_o);
+    p.part_ml = reinterpret_cast<float *>(ws + FL.part_ml);
+    p.num_parts = (int32_t)ceil_div(max_context_len, part);
+    int log2_waves = 0;
+    int rc = device_waves(&log2_waves);
+    if (rc != PKV_OK)
+        return rc;
+    pkv::BalancedParams bp;
+    bp.d = p;
+    bp.total_chunks = reinterpret_cast<int32_t *>(ws + FL.total_chunks);
+    bp.chunk_start = reinterpret_cast<int32_t *>(ws + FL.chunk_start);
+    bp.wave_start = reinterpret_cast<int4 *>(ws + FL.wave_start);
+    bp.piece_o = nullptr;
+    bp.piece_ml = nullptr;
+    bp.num_waves = 1 << log2_waves;
+    bp.log2_waves = log2_waves;
+    bp.num_seqs = num_seqs;
+    bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
+    bp.part_chunks = part / pkv::kChunk;
+    if (!bp.inline_schedule) {
+        rc = launch((const void *)pkv::schedule_kernel<kPrefix>, dim3(1),
+                    dim3(pkv::kScheduleThreads), &bp, stream);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    const void *dk = head_dim == 128
+                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, kPrefix>
+                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, kPrefix>;
+    return launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+}
+
 template <class Fmt>
 int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
                 const int32_t *block_tables, const int32_t *context_lens, float scale,
@@ -292,7 +341,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
         bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
         bp.part_chunks = 0;
         if (!bp.inline_schedule) {
-            rc = launch((const void *)pkv::schedule_kernel, dim3(1), dim3(pkv::kScheduleThreads),
+            rc = launch((const void *)pkv::schedule_kernel<false>, dim3(1),
+                        dim3(pkv::kScheduleThreads),
                         &bp, stream);
             if (rc != PKV_OK)
                 return rc;
@@ -321,41 +371,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
                                            : (const void *)pkv::decode_kernel<Fmt, 64, false>;
         return launch(kern, grid, dim3(pkv::kWave), &p, stream);
     }
-    const FixedLayout FL = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, part);
-    if (!workspace || workspace_bytes < FL.total)
-        return PKV_ERR_WORKSPACE;
-    if (!aligned16(workspace))
-        return PKV_ERR_ALIGN;
-    if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
-        return PKV_ERR_SHAPE;
-    char *ws = static_cast<char *>(workspace);
-    p.part_o = reinterpret_cast<float *>(ws + FL.part_o);
-    p.part_ml = reinterpret_cast<float *>(ws + FL.part_ml);
-    int log2_waves = 0;
-    int rc = device_waves(&log2_waves);
-    if (rc != PKV_OK)
-        return rc;
-    pkv::BalancedParams bp;
-    bp.d = p;
-    bp.total_chunks = reinterpret_cast<int32_t *>(ws + FL.total_chunks);
-    bp.chunk_start = reinterpret_cast<int32_t *>(ws + FL.chunk_start);
-    bp.wave_start = reinterpret_cast<int4 *>(ws + FL.wave_start);
-    bp.piece_o = nullptr;
-    bp.piece_ml = nullptr;
-    bp.num_waves = 1 << log2_waves;
-    bp.log2_waves = log2_waves;
-    bp.num_seqs = num_seqs;
-    bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
-    bp.part_chunks = part / pkv::kChunk;
-    if (!bp.inline_schedule) {
-        rc = launch((const void *)pkv::schedule_kernel, dim3(1), dim3(pkv::kScheduleThreads), &bp,
-                    stream);
-        if (rc != PKV_OK)
-            return rc;
-    }
-    const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true>
-                                     : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true>;
-    rc = launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+    int rc = persistent_launch<Fmt, false>(p, head_dim, num_seqs, num_heads, num_kv_heads,
+                                           max_context_len, workspace, workspace_bytes, stream);
     if (rc != PKV_OK)
         return rc;
 
@@ -467,10 +484,10 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
                   dim3(pkv::kMergeThreads), &mp, stream);
 }
 
-// Prefix-aware decode: group kernel (shared partitions), per-sequence kernel
-// (the rest), merge.  With a single partition no partition can lie wholly
-// inside a shared prefix (which ends before the context does), so that case
-// is the plain kernel.
+// Prefix-aware decode: group kernel (shared partitions), persistent waves for
+// the rest of every sequence, merge.  With a single partition no partition
+// can lie wholly inside a shared prefix (which ends before the context does),
+// so that case is the plain kernel.
 template <class Fmt>
 int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
                          int32_t num_kv_heads, int32_t max_context_len, int32_t max_prefix_tokens,
@@ -479,22 +496,23 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     const int32_t part = p.part;
     const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
     const bool split = parts > 1;
-    const dim3 grid((unsigned)parts, (unsigned)num_kv_heads, (unsigned)num_seqs);
     if (!split) {
         p.num_parts = 1;
         const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, false>
                                            : (const void *)pkv::decode_kernel<Fmt, 64, false>;
-        return launch(kern, grid, dim3(pkv::kWave), &p, stream);
+        return launch(kern, dim3(1u, (unsigned)num_kv_heads, (unsigned)num_seqs),
+                      dim3(pkv::kWave), &p, stream);
     }
-    const size_t need = partials_bytes(num_seqs, num_heads, head_dim, max_context_len, part);
-    if (!workspace || workspace_bytes < need)
+    // Everything the persistent launch checks, before the group kernel runs.
+    const FixedLayout FL = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, part);
+    if (!workspace || workspace_bytes < FL.total)
         return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace))
         return PKV_ERR_ALIGN;
-    const int64_t rows = (int64_t)num_seqs * num_heads * parts;
-    const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
-    p.part_o = static_cast<float *>(workspace);
-    p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
+        return PKV_ERR_SHAPE;
+    p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + FL.part_o);
+    p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + FL.part_ml);
     p.num_parts = (int32_t)parts;
 
     const int64_t prefix_parts =
@@ -517,9 +535,8 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
         if (rc != PKV_OK)
             return rc;
     }
-    const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, true, true>
-                                       : (const void *)pkv::decode_kernel<Fmt, 64, true, true>;
-    rc = launch(kern, grid, dim3(pkv::kWave), &p, stream);
+    rc = persistent_launch<Fmt, true>(p, head_dim, num_seqs, num_heads, num_kv_heads,
+                                      max_context_len, workspace, workspace_bytes, stream);
     if (rc != PKV_OK)
         return rc;
     pkv::MergeParams mp;

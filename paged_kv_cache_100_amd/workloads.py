@@ -99,11 +99,13 @@ SPECS = {
     "llama3_70b_long_b4_ctx128k": Spec("llama3_70b_long_b4_ctx128k", B=4, N=64, K=8, H=128,
                                        bs=16, ctx=131072, partition_size=512, seed=1005),
     # Speculative verification: gamma draft tokens plus one, all queried at once.
+    # Partition sizes: one wave per (sequence, KV head) fills half the chip and
+    # needs no merge (8B); two per pair fill it (70B, three tiles per wave).
     "llama3_8b_b64_ctx8k_spec4": Spec("llama3_8b_b64_ctx8k_spec4", B=64, N=32, K=8, H=128,
-                                      bs=16, ctx=8192, queries=4, partition_size=1024,
+                                      bs=16, ctx=8192, queries=4, partition_size=8192,
                                       seed=1006),
     "llama3_70b_b64_ctx4k_spec6": Spec("llama3_70b_b64_ctx4k_spec6", B=64, N=64, K=8, H=128,
-                                       bs=16, ctx=4096, queries=6, partition_size=1024,
+                                       bs=16, ctx=4096, queries=6, partition_size=2048,
                                        seed=1007),
 }
 # The same draws in FP8 pools.

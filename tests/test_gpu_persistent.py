@@ -5,9 +5,9 @@ sliding-window forms) runs fixed partitions on the token-balanced schedule:
 each wave takes a run of whole partitions and writes each one's split-K
 partial, then the log-sum-exp merge over partitions.  Every partition is the
 same chunks in the same order as in the one-wave-per-partition grid, so the
-results must be bit-identical to that grid -- which the prefix-aware call
-still runs for partitions no prefix group covers (here: one group whose
-shared prefix is empty).  Also checked against the oracle, with more than 256
+results must be bit-identical to that grid -- which the multi-query call
+still runs (one wave per partition; with one query token per sequence it is
+the single-query decode).  Also checked against the oracle, with more than 256
 sequences (the schedule kernel's table instead of the in-wave scan), and at
 the full 128K-context size.
 """
@@ -27,20 +27,14 @@ DEV = "cuda:0"
 
 
 def grid_decode(g, w, partition):
-    """The one-wave-per-partition grid: the prefix-aware call with one group
-    whose shared prefix is empty, so no partition is taken from the grid."""
-    B = w.spec.B
-    seq_group = torch.full((B,), -1, dtype=torch.int32)
-    seq_group[0] = 0
-    members = torch.tensor([[0]], dtype=torch.int32)
-    tokens = torch.zeros(1, dtype=torch.int32)
-    out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=DEV)
-    pkv.paged_decode_attention_prefix(out, g.q, g.key_cache, g.value_cache, g.block_tables,
-                                      g.context_lens, w.scale, w.spec.K, w.spec.bs, partition,
-                                      seq_group.to(DEV), members.to(DEV), tokens.to(DEV),
-                                      max_prefix_tokens=0, k_scale=w.k_scale,
-                                      v_scale=w.v_scale, max_context_len=w.max_context_len)
-    return out
+    """One wave per partition: the multi-query call with one query token per
+    sequence (its kernel computes each partition's partial with the same
+    arithmetic, and merges with the same kernel)."""
+    B, N, Hd = w.spec.B, w.spec.N, w.spec.H
+    out = torch.full((B, 1, N, Hd), float("nan"), dtype=torch.float32, device=DEV)
+    gq = dataclasses.replace(g, q=g.q.reshape(B, 1, N, Hd).contiguous())
+    H.gpu_decode_mq(out, gq, w, partition)
+    return out[:, 0]
 
 
 def check(spec, partition, what, oracle_rows=None):

@@ -113,6 +113,29 @@ def test_many_sharers(sharers):
     run_prefix(w, groups, 64, f"{sharers} sharers")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sharers_wholly_shared(kv):
+    # sequences 1 and 2 (64 tokens) lie wholly in their group's partitions:
+    # no chunk of their own is left for the per-sequence waves
+    spec = W.Spec("whole", B=6, N=32, K=8, H=128, ctx=[700, 64, 64, 300, 33, 96], seed=97,
+                  kv_dtype=kv)
+    w = W.make(spec)
+    groups = repoint(w, [(0, [1, 2, 5], 10)])
+    run_prefix(w, groups, 32, f"wholly shared {kv}")
+
+
+def test_large_batch():
+    # more than 256 sequences: the schedule kernel's table, with shared
+    # partitions skipped
+    gen = np.random.default_rng(101)
+    ctx = [int(c) for c in gen.integers(1, 600, size=300)]
+    ctx[:40] = [400 + i for i in range(40)]
+    spec = W.Spec("b300", B=300, N=16, K=4, H=64, ctx=ctx, seed=101)
+    w = W.make(spec)
+    groups = repoint(w, [(0, list(range(1, 30)), 20), (30, list(range(31, 40)), 12)])
+    run_prefix(w, groups, 64, "B=300 two groups")
+
+
 def tiles_per_wave(items, tiles):
     """The library's choice for the group kernel: the fewest tiles per wave
     whose waves fit one per SIMD (1024 on the chip), at most four."""
