@@ -363,6 +363,7 @@ struct MergeParams {
     int32_t max_ctx;
     int32_t part;
     int32_t num_parts;
+    int32_t group;                // G = N / K (merge_parts_kernel)
 };
 
 constexpr int kMergeThreads = 256;
@@ -435,6 +436,84 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
         for (int g2 = 0; g2 < kGroups; ++g2)
             total += part_sum[g2][h];
         p.out[row * H + h] = (parts && den > 0.f) ? total / den : 0.f;
+    }
+}
+
+// The same merge for rows of few partitions (at most kMergePartsMax): one
+// wave per (query row, KV head) combines the partials of the group's G heads,
+// up to eight partitions per memory round trip, with the running maximum
+// rescaled as it grows.  Lane layout: heads padded to Gp (a power of two >=
+// G), 64/Gp lanes per head, each lane H*Gp/64 consecutive values of its
+// head's row.  A partial that saw no position (m = -inf, l = 0: a query
+// token of the multi-query call whose positions end before the partition)
+// takes no part.  Grid: (K, B * Q).
+constexpr int kMergePartsMax = 16;
+
+template <int H, int Gp>
+__global__ __launch_bounds__(kWave) void merge_parts_kernel(MergeParams p)
+{
+    constexpr int kLanesPerHead = kWave / Gp;
+    constexpr int kVals = H / kLanesPerHead;      // values per lane (multiple of 4)
+    constexpr int kBatch = kVals / 4 >= 8 ? 4 : 8;
+    const int kvh = blockIdx.x;
+    const int bq = blockIdx.y;                     // b * Q + query token
+    const int b = bq / p.num_queries;
+    const int lane = threadIdx.x;
+    const int g = lane / kLanesPerHead;
+    const int h0 = (lane % kLanesPerHead) * kVals;
+    const bool live = g < p.group;
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int parts = (ctx + p.part - 1) / p.part;
+    const int first = p.window > 0 ? max(ctx - p.window, 0) / p.part : 0;
+    const int64_t row = (int64_t)bq * p.num_heads + kvh * p.group + (live ? g : 0);
+    const float *ml = p.part_ml + row * p.num_parts * 2;
+    const float *po = p.part_o + row * p.num_parts * H + h0;
+
+    float big = -INFINITY, den = 0.f;
+    f32x4 num[kVals / 4];
+#pragma unroll
+    for (int v = 0; v < kVals / 4; ++v)
+        num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = first; j0 < parts; j0 += kBatch) {
+        float mv[kBatch], lv[kBatch];
+        f32x4 ov[kBatch][kVals / 4];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = min(j0 + u, parts - 1);  // in range; unused ones are masked below
+            mv[u] = ml[2 * j];
+            lv[u] = ml[2 * j + 1];
+#pragma unroll
+            for (int v = 0; v < kVals / 4; ++v)
+                ov[u][v] = *reinterpret_cast<const f32x4 *>(po + (int64_t)j * H + 4 * v);
+        }
+        bool use[kBatch];
+        float nb = big;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            use[u] = j0 + u < parts && mv[u] > -INFINITY;
+            nb = use[u] ? fmaxf(nb, mv[u]) : nb;
+        }
+        const float sc = big == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(big - nb);
+        den *= sc;
+#pragma unroll
+        for (int v = 0; v < kVals / 4; ++v)
+            num[v] *= sc;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const float wt = use[u] ? __builtin_amdgcn_exp2f(mv[u] - nb) : 0.f;
+            den += use[u] ? wt * lv[u] : 0.f;
+#pragma unroll
+            for (int v = 0; v < kVals / 4; ++v)
+                num[v] += use[u] ? wt * ov[u][v] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        big = nb;
+    }
+    if (live) {
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        float *o = p.out + row * H + h0;
+#pragma unroll
+        for (int v = 0; v < kVals / 4; ++v)
+            *reinterpret_cast<f32x4 *>(o + 4 * v) = num[v] * inv;
     }
 }
 

@@ -114,7 +114,7 @@ struct KvFp8 {
     // An FP8 chunk is 32 registers per lane.  Rings of 5 and 4 (16 and 12
     // KiB in flight per wave) measured as fast as deeper ones (up to 8 and 5).
     static constexpr int kRing = 5;
-    static constexpr int kBalancedRing = 4;
+    static constexpr int kBalancedRing = 2;
 
     template <int H>
     struct Regs {

@@ -193,6 +193,35 @@ bool valid_pool_scale(float s)
 }
 
 // Both decode entry points: bf16 pools (k_scale = v_scale = 1) or FP8 pools.
+// The log-sum-exp merge over fixed partitions: one wave per (query row, KV
+// head) for rows of at most kMergePartsMax partitions, else one workgroup
+// per (query row, head).  rows = num_seqs * num_queries.
+int launch_merge(pkv::MergeParams &mp, int head_dim, int32_t num_kv_heads, int64_t rows,
+                 void *stream)
+{
+    if (mp.num_parts <= pkv::kMergePartsMax) {
+        const int kmin = 256 / head_dim;
+        const int g = mp.group;
+        const int gp = g <= kmin ? kmin : g <= 4 ? 4 : g <= 8 ? 8 : 16;
+        const void *mk;
+        if (head_dim == 128)
+            mk = gp == 2   ? (const void *)pkv::merge_parts_kernel<128, 2>
+                 : gp == 4 ? (const void *)pkv::merge_parts_kernel<128, 4>
+                 : gp == 8 ? (const void *)pkv::merge_parts_kernel<128, 8>
+                           : (const void *)pkv::merge_parts_kernel<128, 16>;
+        else
+            mk = gp == 4   ? (const void *)pkv::merge_parts_kernel<64, 4>
+                 : gp == 8 ? (const void *)pkv::merge_parts_kernel<64, 8>
+                           : (const void *)pkv::merge_parts_kernel<64, 16>;
+        return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)rows), dim3(pkv::kWave), &mp,
+                      stream);
+    }
+    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
+                                     : (const void *)pkv::merge_kernel<64>;
+    return launch(mk, dim3((unsigned)mp.num_heads, (unsigned)rows), dim3(pkv::kMergeThreads), &mp,
+                  stream);
+}
+
 // Fixed partitions (several) on persistent waves: schedule (large batches),
 // then the balanced kernel in partition mode writing every partition's
 // partial to the workspace's split-K slots; the caller launches the merge.
@@ -387,10 +416,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     mp.max_ctx = max_context_len;
     mp.part = part;
     mp.num_parts = (int32_t)parts;
-    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
-                                     : (const void *)pkv::merge_kernel<64>;
-    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads), &mp,
-                  stream);
+    mp.group = num_heads / num_kv_heads;
+    return launch_merge(mp, head_dim, num_kv_heads, num_seqs, stream);
 }
 
 // Multi-query decode: kernel for a head dim, tiles per wave (1 to 4) and split.
@@ -478,10 +505,8 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     mp.max_ctx = max_context_len;
     mp.part = part;
     mp.num_parts = (int32_t)parts;
-    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
-                                     : (const void *)pkv::merge_kernel<64>;
-    return launch(mk, dim3((unsigned)num_heads, (unsigned)(num_seqs * num_queries)),
-                  dim3(pkv::kMergeThreads), &mp, stream);
+    mp.group = num_heads / num_kv_heads;
+    return launch_merge(mp, head_dim, num_kv_heads, (int64_t)num_seqs * num_queries, stream);
 }
 
 // Prefix-aware decode: group kernel (shared partitions), persistent waves for
@@ -550,10 +575,8 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     mp.max_ctx = max_context_len;
     mp.part = part;
     mp.num_parts = (int32_t)parts;
-    const void *mk = head_dim == 128 ? (const void *)pkv::merge_kernel<128>
-                                     : (const void *)pkv::merge_kernel<64>;
-    return launch(mk, dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(pkv::kMergeThreads),
-                  &mp, stream);
+    mp.group = num_heads / num_kv_heads;
+    return launch_merge(mp, head_dim, num_kv_heads, num_seqs, stream);
 }
 
 }  // namespace
