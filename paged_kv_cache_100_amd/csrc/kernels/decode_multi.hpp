@@ -46,23 +46,23 @@ constexpr int multi_ring_depth()
 
 // One 32-token chunk for kTiles column tiles.  tok0 is the position of this
 // lane's first token (chunk start + 8 * quad); column t of this lane sees
-// positions below lim[t]; vrem = ctx - chunk start (value elements at or
-// past it are zeroed).  qf(t, s) yields the lane's query operand.
+// positions below lim[t]; vrem = ctx - chunk start.  qf(t, s) yields the
+// lane's query operand.  kMasked: the chunk may hold positions some column
+// does not see; mask_scores (uniform) says whether it does, and value
+// elements at or past ctx are zeroed in place, once for all tiles, in the
+// chunk that holds the end of the context (both only near a sequence's end,
+// so the other chunks pay for neither).
 template <class Fmt, int H, int kTiles, bool kMasked, class QFrag>
-__device__ __forceinline__ void attend_chunk_multi(const typename Fmt::template Regs<H> &r,
+__device__ __forceinline__ void attend_chunk_multi(typename Fmt::template Regs<H> &r,
                                                    QFrag &&qf, int tok0,
                                                    const int (&lim)[kTiles], int vrem, int quad,
                                                    float scale_log2, float (&m)[kTiles],
                                                    float (&l)[kTiles],
-                                                   f32x4 (&acc)[kTiles][H / 16])
+                                                   f32x4 (&acc)[kTiles][H / 16],
+                                                   bool mask_scores = true)
 {
-    u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
-    if (kMasked) {
-        const int valid = min(max(vrem - 8 * quad, 0), 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            vmask[w] = (2 * w < valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
-    }
+    if (kMasked && vrem < kChunk)
+        Fmt::template zero_values<H>(r, min(max(vrem - 8 * quad, 0), 8));
     // One tile at a time (scores, softmax, P.V), so only one tile's P is live.
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
@@ -79,7 +79,7 @@ __device__ __forceinline__ void attend_chunk_multi(const typename Fmt::template 
             x[i] = s0[i] * scale_log2;
             x[4 + i] = s1[i] * scale_log2;
         }
-        if (kMasked) {
+        if (kMasked && mask_scores) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (tok0 + e >= lim[t])
@@ -112,8 +112,7 @@ __device__ __forceinline__ void attend_chunk_multi(const typename Fmt::template 
         }
 #pragma unroll
         for (int c = 0; c < H / 16; ++c) {
-            const u32x4 vbits = Fmt::value(r, c);
-            const bf16x8 vv = as_bf16x8(kMasked ? (vbits & vmask) : vbits);
+            const bf16x8 vv = as_bf16x8(Fmt::value(r, c));
             acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, acc[t][c], 0, 0, 0);
             acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, acc[t][c], 0, 0, 0);
         }
@@ -231,7 +230,10 @@ void decode_multi_kernel(DecodeParams p)
             acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto attend = [&](const Regs &r, int ci) {
+    // Query token 0 sees positions below ctx - Q + 1: chunks wholly below
+    // that need no score mask.
+    const int lim_min = ctx - Q + 1;
+    auto attend = [&](Regs &r, int ci) {
         // An index the compiler cannot see through, so that the LDS reads stay
         // inside the loop instead of being hoisted back into registers.
         int opaque = lane;
@@ -241,7 +243,8 @@ void decode_multi_kernel(DecodeParams p)
         };
         const int c0 = start + kChunk * ci;
         attend_chunk_multi<Fmt, H, kTiles, true>(r, qfrag, c0 + 8 * quad, lim, ctx - c0, quad,
-                                                 p.scale_log2, m, l, acc);
+                                                 p.scale_log2, m, l, acc,
+                                                 c0 + kChunk > lim_min);
     };
 
     constexpr int kRing = multi_ring_depth<Fmt, kTiles>();

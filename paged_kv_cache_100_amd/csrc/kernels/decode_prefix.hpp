@@ -124,7 +124,7 @@ void decode_prefix_kernel(PrefixParams p)
             acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // Every position of the partition is valid for every live sharer.
-    auto attend = [&](const Regs &r, int ci) {
+    auto attend = [&](Regs &r, int ci) {
         int opaque = lane;
         asm volatile("" : "+v"(opaque));
         auto qfrag = [&](int t, int s) {

@@ -84,6 +84,18 @@ struct KvBf16 {
     {
         return r.v[c];
     }
+    // Zeroes the lane's value elements from token `valid` (0..8) on, in place.
+    template <int H>
+    __device__ static __forceinline__ void zero_values(Regs<H> &r, int valid)
+    {
+        u32x4 mask;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            mask[w] = (2 * w < valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            r.v[c] &= mask;
+    }
 };
 
 // Four E4M3 codes (bytes of w, lowest first) as four bf16, exactly.
@@ -157,6 +169,24 @@ struct KvFp8 {
     __device__ static __forceinline__ u32x4 value(const Regs<H> &r, int c)
     {
         return __builtin_bit_cast(u32x4, widen8(r.v[c][0], r.v[c][1]));
+    }
+    // Zeroes the lane's value codes from token `valid` (0..8) on, in place
+    // (code 0 is +0).
+    template <int H>
+    __device__ static __forceinline__ void zero_values(Regs<H> &r, int valid)
+    {
+        u32x2 mask;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            uint32_t mw = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                mw |= (4 * w + b < valid ? 0xFFu : 0u) << (8 * b);
+            mask[w] = mw;
+        }
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            r.v[c] &= mask;
     }
 };
 
