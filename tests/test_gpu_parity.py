@@ -81,6 +81,15 @@ def test_many_sequences_and_empty_ones():
         run_case(spec, partition=partition, what=f"B=1300 part {partition}")
 
 
+def test_more_pieces_than_the_stage_holds():
+    # G = 16, H = 128: a wave stages at most four finished pieces in LDS; here
+    # about five one-chunk segments fall to every wave, so stages fill and are
+    # written out while loads are still in flight
+    spec = W.Spec("stage", B=5200, N=16, K=1, H=128, ctx=[16 + (i % 17) for i in range(5200)],
+                  seed=43)
+    run_case(spec, partition=0, what="stage overflow")
+
+
 def test_one_long_sequence_among_short_ones():
     # one segment spread over many waves, the others each inside one wave
     spec = W.Spec("skew", B=9, N=64, K=8, H=128, ctx=[6000] + [40] * 8, seed=41)

@@ -80,6 +80,14 @@ def test_large_batch_schedule_table(partition):
     check(spec, partition, "B=300")
 
 
+def test_more_partitions_than_the_stage_holds():
+    # G = 16, H = 128 and one-chunk partitions: about eight partition partials
+    # per wave against a stage of four
+    spec = W.Spec("stage", B=64, N=16, K=1, H=128, ctx=[4096 - 3 * i for i in range(64)],
+                  seed=47)
+    check(spec, 32, "stage overflow, fixed")
+
+
 def test_long_context_full_size():
     # 4 x 131072 tokens in 512-token partitions, bit-identical to the grid (its
     # parity against the oracle is the full-size suite's)
