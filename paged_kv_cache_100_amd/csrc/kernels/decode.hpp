@@ -224,29 +224,27 @@ __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&i
     }
 }
 
-// One wave per (partition, KV head, sequence).  The library launches it with
-// one partition per sequence (kSplit false); several partitions run on the
-// persistent waves of decode_balanced.hpp, which compute the same partials.
-template <class Fmt, int H, bool kSplit>
+// One wave per (KV head, sequence) when a single partition (at most 1,024
+// tokens) covers every context: the wave normalises and writes its rows.
+// Several partitions run on the persistent waves of decode_balanced.hpp.
+// Grid: (1, K, B).
+template <class Fmt, int H>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
-    const int part_idx = blockIdx.x;
     const int kvh = blockIdx.y;
     const int b = blockIdx.z;
     const int lane = threadIdx.x;
     const int col = lane & 15;    // query head within the group (tile column)
     const int quad = lane >> 4;   // 0..3
 
-    // The partition's block ids (at most 64: partitions hold <= 1024 tokens),
-    // one per lane, so a chunk reads its two ids with v_readlane instead of a
-    // memory round trip.  They are fetched before the context length is known
-    // (every entry up to the table row's end is in bounds), so the two loads
-    // overlap; entries past the sequence's last block are loaded but unused.
-    const int start = part_idx * p.part;
-    const int first_block = start / kBlockSize;
-    const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks + first_block;
-    const int table_avail = min(p.part / kBlockSize, p.max_blocks - first_block);
+    // The sequence's block ids (at most 64: the partition holds <= 1024
+    // tokens), one per lane, so a chunk reads its two ids with v_readlane
+    // instead of a memory round trip.  They are fetched before the context
+    // length is known (every entry up to the table row's end is in bounds),
+    // so the two loads overlap; entries past the last block are unused.
+    const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks;
+    const int table_avail = min(p.part / kBlockSize, p.max_blocks);
     int my_id = 0;
     if (lane < table_avail)
         my_id = table[lane];
@@ -255,11 +253,10 @@ void decode_kernel(DecodeParams p)
     const bool live = col < p.group;
     const int n = kvh * p.group + col;
 
-    // Sliding window: positions before lo are not attended; a partition that
-    // ends before lo is skipped (the merge starts at lo's partition).
+    // Sliding window: positions before lo are not attended.
     const int lo = window_start(p, ctx);
-    if (start >= ctx || (kSplit && start + p.part <= lo)) {
-        if (!kSplit && part_idx == 0 && live) {   // empty sequence: zeros
+    if (ctx == 0) {                       // empty sequence: zeros
+        if (live) {
             float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
 #pragma unroll
             for (int c = 0; c < H / 16; ++c)
@@ -267,8 +264,8 @@ void decode_kernel(DecodeParams p)
         }
         return;
     }
-    const int end = min(start + p.part, ctx);
-    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
+    const int end = min(p.part, ctx);
+    const int n_blocks = (end - 1) / kBlockSize + 1;
     my_id = clamp_block(my_id, p.num_blocks);
 
     bf16x8 qf[H / 32];
@@ -290,10 +287,10 @@ void decode_kernel(DecodeParams p)
     const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
     const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
 
-    // Chunks start at cbeg: the partition's start, or the 32-token boundary
-    // at or below the window start.
-    const int cbeg = __builtin_amdgcn_readfirstlane(max(start, lo - lo % kChunk));
-    const int boff = (cbeg - start) / kBlockSize;   // table entries before cbeg
+    // Chunks start at cbeg: the 32-token boundary at or below the window
+    // start (0 without a window).
+    const int cbeg = __builtin_amdgcn_readfirstlane(lo - lo % kChunk);
+    const int boff = cbeg / kBlockSize;             // table entries before cbeg
     const int head = lo - cbeg;                      // masked leading positions of chunk 0
 
     // Issue the loads of chunk ci (tokens cbeg + 32ci ...); its second block
@@ -333,23 +330,11 @@ void decode_kernel(DecodeParams p)
     if (!live)
         return;
     // acc[c] holds O^T[16c + 4quad + i][col], i = 0..3.
-    if (!kSplit) {
-        const float inv = p.out_scale / l;
-        float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
+    const float inv = p.out_scale / l;
+    float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
 #pragma unroll
-        for (int c = 0; c < H / 16; ++c)
-            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
-    } else {
-        const int64_t slot = ((int64_t)b * p.num_heads + n) * p.num_parts + part_idx;
-        float *o = p.part_o + slot * H;
-#pragma unroll
-        for (int c = 0; c < H / 16; ++c)
-            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * p.out_scale;
-        if (quad == 0) {
-            p.part_ml[2 * slot] = m;
-            p.part_ml[2 * slot + 1] = l;
-        }
-    }
+    for (int c = 0; c < H / 16; ++c)
+        *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
 }
 
 struct MergeParams {

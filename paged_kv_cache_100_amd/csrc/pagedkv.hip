@@ -396,8 +396,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.num_parts = (int32_t)parts;
     if (!split) {
         const dim3 grid(1u, (unsigned)num_kv_heads, (unsigned)num_seqs);
-        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, false>
-                                           : (const void *)pkv::decode_kernel<Fmt, 64, false>;
+        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128>
+                                           : (const void *)pkv::decode_kernel<Fmt, 64>;
         return launch(kern, grid, dim3(pkv::kWave), &p, stream);
     }
     int rc = persistent_launch<Fmt, false>(p, head_dim, num_seqs, num_heads, num_kv_heads,
@@ -523,8 +523,8 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     const bool split = parts > 1;
     if (!split) {
         p.num_parts = 1;
-        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128, false>
-                                           : (const void *)pkv::decode_kernel<Fmt, 64, false>;
+        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128>
+                                           : (const void *)pkv::decode_kernel<Fmt, 64>;
         return launch(kern, dim3(1u, (unsigned)num_kv_heads, (unsigned)num_seqs),
                       dim3(pkv::kWave), &p, stream);
     }
