@@ -291,6 +291,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
         return PKV_ERR_SHAPE;
+    if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
+        return PKV_ERR_SHAPE;
     if (num_seqs > 65535 || num_kv_heads > 65535)
         return PKV_ERR_SHAPE;
     if (partition_size != 0 &&
@@ -731,6 +733,8 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
         return PKV_ERR_SHAPE;
+    if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
+        return PKV_ERR_SHAPE;
     if ((int64_t)num_seqs * num_queries > 65535 || num_kv_heads > 65535)
         return PKV_ERR_SHAPE;
     if (partition_size < PKV_PARTITION_GRAIN || partition_size > PKV_MAX_MQ_PARTITION ||
@@ -852,6 +856,8 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     if ((int64_t)max_members * (num_heads / num_kv_heads) > PKV_MAX_PREFIX_ROWS)
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+        return PKV_ERR_SHAPE;
+    if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
         return PKV_ERR_SHAPE;
     if (num_seqs > 65535 || num_kv_heads > 65535)
         return PKV_ERR_SHAPE;

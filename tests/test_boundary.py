@@ -148,6 +148,8 @@ def test_decode_mq_checks(L):
     assert decode_mq(L, part=0) == SHAPE                   # fixed partitions only
     assert decode_mq(L, part=48) == SHAPE
     assert decode_mq(L, part=(1 << 20) + 32) == SHAPE       # past PKV_MAX_MQ_PARTITION
+    # the last partition's end must fit in 32 bits
+    assert decode_mq(L, part=1 << 20, maxblk=1 << 27, maxctx=(1 << 31) - 1000) == SHAPE
     assert decode_mq(L, part=4096, maxblk=512, maxctx=8192) != SHAPE   # > 1024: allowed here
     assert decode_mq(L, H=96) == UNSUP
     assert decode_mq(L, maxctx=257) == SHAPE
