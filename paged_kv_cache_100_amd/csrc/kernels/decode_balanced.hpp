@@ -1,14 +1,16 @@
 // Token-balanced decode attention for ragged batches (continuous batching).
 //
-// The fixed-partition launch of decode.hpp gives every (partition, KV head,
-// sequence) its own wave.  With ragged contexts -- the continuous-batching mix
-// of "CS336 Lecture 10: Inference", part 6 -- that leaves a tail of unequal
-// waves and pays the start-up latency of every wave (context length, block
-// ids, first loads) once per partition.  Here the grid is exactly the number
-// of waves the chip holds at once, and the work is cut by tokens instead:
+// A launch of one wave per (partition, KV head, sequence) leaves, on ragged
+// contexts -- the continuous-batching mix of "CS336 Lecture 10: Inference",
+// part 6 -- a tail of unequal waves and pays the start-up latency of every
+// wave (context length, block ids, first loads) once per partition.  Here the
+// grid is exactly the number of waves the chip holds at once, and the work is
+// cut by tokens instead:
 //
 //   * segments s = (sequence b, KV head kvh), in order b-major; segment s has
-//     nc_b = ceil(ctx_b / 32) chunks of 32 tokens;
+//     nc_b = ceil(ctx_b / 32) chunks of 32 tokens (counted from the sliding
+//     window's first chunk, or, for kPrefix, after the partitions that b's
+//     prefix group computes);
 //   * the flattened chunk list [0, T), T = K * sum_b nc_b, is split evenly:
 //     wave w gets chunks [floor(w T / W), floor((w+1) T / W));
 //   * a wave walks its chunks in order, crossing segment boundaries without
@@ -20,9 +22,12 @@
 // flattened list every wave or segment boundary starts a new piece) and the
 // merge kernel combines them with the log-sum-exp rule.
 //
-// A one-workgroup schedule kernel runs first: it scans the context lengths
-// into chunk offsets cs[b] (exclusive prefix sum of nc_b) and writes each
-// wave's starting (b, kvh, chunk) so that a wave needs one load to begin.
+// For more than 256 sequences a one-workgroup schedule kernel runs first: it
+// scans the context lengths into chunk offsets cs[b] (exclusive prefix sum of
+// nc_b) and writes each wave's starting (b, kvh, chunk) so that a wave needs
+// one load to begin; smaller batches are scanned inside every wave.
+// Finished pieces wait in LDS until the wave's loads are done (see the
+// kernel).
 //
 // Fixed partitions (kFixed, part_chunks chunks each) run on the same
 // schedule: both ends of every wave's range move down to a partition
@@ -44,7 +49,7 @@ constexpr int kScheduleThreads = 1024;
 constexpr int kMaxBalancedWaves = 4096;
 
 struct BalancedParams {
-    DecodeParams d;               // shapes, pointers, scale (part/num_parts unused)
+    DecodeParams d;               // shapes, pointers, scale (part / num_parts: kFixed only)
     int32_t *chunk_start;         // [B + 1]: exclusive prefix sum of nc_b (schedule output)
     int32_t *total_chunks;        // [1]: T = K * chunk_start[B]
     int4 *wave_start;             // [W]: (b, kvh, chunk in segment, ctx of b)
