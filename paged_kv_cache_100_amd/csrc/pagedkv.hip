@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <atomic>
 
 #include "pagedkv.h"
 #include "kernels/append.hpp"
@@ -109,13 +110,16 @@ constexpr int kWavesPerCU = 4;
 
 int device_waves(int *log2_waves)
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];   // zero-initialised; written once per device
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return PKV_ERR_DEVICE;
-    if (dev < 64 && cached[dev] > 0) {
-        *log2_waves = cached[dev];
-        return PKV_OK;
+    if (dev < 64) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *log2_waves = c;
+            return PKV_OK;
+        }
     }
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -125,7 +129,7 @@ int device_waves(int *log2_waves)
     while ((2 << lg) <= cus * kWavesPerCU && (2 << lg) <= pkv::kMaxBalancedWaves)
         ++lg;
     if (dev < 64)
-        cached[dev] = lg;
+        cached[dev].store(lg, std::memory_order_relaxed);
     *log2_waves = lg;
     return PKV_OK;
 }
@@ -439,13 +443,13 @@ const void *multi_kernel(int tiles, bool split)
 }
 
 // Tiles per wave of the shared-prefix group kernel: the fewest (most waves,
-// shortest kernel) that still fit one wave per SIMD of the chip; the waves
-// that split an item's columns re-read its blocks from their XCD's L2.
-int prefix_tiles_per_wave(int64_t items, int tiles)
+// shortest kernel) that still fit one wave per SIMD of the chip (wave_slots);
+// the waves that split an item's columns re-read its blocks from their XCD's
+// L2.
+int prefix_tiles_per_wave(int64_t items, int tiles, int64_t wave_slots)
 {
-    constexpr int64_t kWaveSlots = 256 * 4;   // MI355X: 256 CUs x 4 SIMDs
     for (int pw = 1; pw < pkv::kTilesPerWave && pw < tiles; ++pw)
-        if (items * ceil_div(tiles, pw) <= kWaveSlots)
+        if (items * ceil_div(tiles, pw) <= wave_slots)
             return pw;
     return tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
 }
@@ -548,7 +552,11 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     if (prefix_parts > 0 && p.num_groups > 0) {
         const int tiles = (int)ceil_div((int64_t)p.max_members * (num_heads / num_kv_heads), 16);
         const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
-        const int per_wave = prefix_tiles_per_wave(items, tiles);
+        int log2_waves = 0;
+        rc = device_waves(&log2_waves);
+        if (rc != PKV_OK)
+            return rc;
+        const int per_wave = prefix_tiles_per_wave(items, tiles, (int64_t)1 << log2_waves);
         pkv::PrefixParams pp;
         pp.d = p;
         pp.d.col_groups = (int32_t)ceil_div(tiles, per_wave);
