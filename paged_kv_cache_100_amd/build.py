@@ -31,6 +31,11 @@ def command(out: str = LIB, extra=()) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-result",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # Matrix-instruction accumulators in ordinary vector registers: the
+            # online softmax rescales the output accumulators with vector
+            # multiplies, and accumulation registers would need a copy of them
+            # kept in vector registers on every chunk.
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
             *extra, "-o", out, SRC]
 
