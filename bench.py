@@ -173,7 +173,8 @@ def main() -> int:
                          "(default: the workload's own, else 0)")
     ap.add_argument("--mode", choices=["plain", "prefix"], default="plain",
                     help="prefix: read each shared prefix once for its sharers "
-                         "(fixed partitions; workloads with shared prefixes)")
+                         "(--partition: its pieces, default 256; workloads with shared "
+                         "prefixes)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend each sequence's last W positions (0 = all)")
     ap.add_argument("--cold", action="store_true",
@@ -268,7 +269,7 @@ def main() -> int:
         prefix_tokens = torch.tensor([shared_tokens], dtype=torch.int32)
         seq_group, members, prefix_tokens = (seq_group.to(dev), members.to(dev),
                                              prefix_tokens.to(dev))
-        ws_bytes = pkv.workspace_size(s.B, s.N, s.K, s.H, mcl, part)
+        ws_bytes = pkv.prefix_workspace_size(s.B, s.N, s.K, s.H, mcl, part, shared_tokens)
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
         def attend():

@@ -311,33 +311,46 @@ int paged_decode_attention_window(float *out, const void *q,
  *   result is then unspecified).  src_blocks, dst_blocks: [num_pairs] int32
  *   device arrays, num_pairs <= 65535.  Checks as for paged_kv_append.
  *
- * paged_decode_attention_prefix -- paged_decode_attention with fixed
- *   partitions (partition_size P: a multiple of 32 in [32, 1024]) that reads
- *   each shared prefix once per partition for all of its sharers instead of
- *   once per sharer.  The result is plain attention over each sequence's
- *   context, exactly (bit for bit) what paged_decode_attention gives with the
- *   same partition size; only the reading changes.
+ * paged_decode_attention_prefix -- paged_decode_attention that reads each
+ *   shared prefix once for all of its sharers instead of once per sharer
+ *   ("CS336 Lecture 10: Inference", part 6: shared prefix blocks).  The
+ *   result is plain attention over each sequence's context (paging and
+ *   sharing only change where blocks are read from), up to rounding.
  *   seq_group      [num_seqs] int32: the prefix group of each sequence, -1 for
  *                  none.
  *   group_members  [num_groups][max_members] int32: the sequences of each
- *                  group, -1 padded; the first is the group's lead.
+ *                  group, -1 padded; the first is the group's lead.  Every
+ *                  sequence b with seq_group[b] = g must be listed in row g.
  *   prefix_tokens  [num_groups] int32: positions 0 .. prefix_tokens - 1 of
  *                  every member map to the same physical blocks as the lead's.
  *   max_prefix_tokens  host-known bound of prefix_tokens.
- *   For a member b of group g, partitions p with (p + 1) * P <=
- *   min(prefix_tokens[g], ctx_b, ctx_lead) are read once for the group; the
- *   rest of its context is read on its own.  max_members * (N / K) <=
- *   PKV_MAX_PREFIX_ROWS.  A member whose table disagrees with the lead's over
- *   that span gets attention over the lead's blocks there.  Workspace as
- *   paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
- *   max_context_len, partition_size); kv_dtype, k_scale, v_scale as for
- *   paged_decode_attention_mq; other arguments as for paged_decode_attention.
+ *   Member b of group g shares positions 0 .. S_b - 1, S_b = min(
+ *   prefix_tokens[g], ctx_b, ctx_lead) rounded down to a multiple of 32: one
+ *   group kernel reads them for all members, in partitions of partition_size
+ *   P tokens (a multiple of 32 in [32, 1024]: smaller partitions spread the
+ *   shared span over more waves, each adding one partial per member row to
+ *   merge); the rest of every context runs on the token-balanced schedule
+ *   of paged_decode_attention with partition_size 0, and one merge joins
+ *   both.  max_members * (N / K) <= PKV_MAX_PREFIX_ROWS.  A member whose
+ *   table disagrees with the lead's over its shared span gets attention over
+ *   the lead's blocks there.  Workspace: paged_decode_prefix_workspace_size
+ *   bytes; kv_dtype, k_scale, v_scale as for paged_decode_attention_mq; other
+ *   arguments as for paged_decode_attention.
  */
 int paged_kv_copy_blocks(void *key_cache, void *value_cache,
                          const int32_t *src_blocks, const int32_t *dst_blocks,
                          int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int64_t num_blocks, int32_t kv_dtype,
                          void *stream);
+
+/* Workspace bytes paged_decode_attention_prefix needs for these sizes (0 if
+ * they are invalid): the token-balanced workspace plus the group kernel's
+ * partials, ceil(min(max_prefix_tokens, max_context_len) rounded down to 32,
+ * over partition_size) per (sequence, query head) row. */
+size_t paged_decode_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          int32_t max_prefix_tokens);
 
 int paged_decode_attention_prefix(float *out, const void *q,
                                   const void *key_cache, const void *value_cache,

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_attention_fp8.restype = ctypes.c_int
     L.paged_decode_mq_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.paged_decode_mq_workspace_size.restype = sz
+    L.paged_decode_prefix_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.paged_decode_prefix_workspace_size.restype = sz
     L.paged_decode_attention_mq.argtypes = [P, P, P, P, P, P, f32, i32, f32, f32, i32, i32, i32,
                                             i32, i32, i32, i32, i32, i64, i32, P, sz, P]
     L.paged_decode_attention_mq.restype = ctypes.c_int
@@ -249,6 +251,13 @@ def paged_decode_attention_fp8(out: torch.Tensor, q: torch.Tensor, key_cache: to
 KV_BF16, KV_FP8_E4M3 = 0, 1
 
 
+def prefix_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                          max_context_len: int, partition: int, max_prefix_tokens: int) -> int:
+    return int(lib().paged_decode_prefix_workspace_size(num_seqs, num_heads, num_kv_heads,
+                                                        head_dim, max_context_len, partition,
+                                                        max_prefix_tokens))
+
+
 def mq_workspace_size(num_seqs: int, num_queries: int, num_heads: int, head_dim: int,
                       max_context_len: int, partition: int) -> int:
     return int(lib().paged_decode_mq_workspace_size(num_seqs, num_queries, num_heads, head_dim,
@@ -309,11 +318,20 @@ def paged_decode_attention_prefix(out: torch.Tensor, q: torch.Tensor, key_cache:
                                   k_scale: float = 1.0, v_scale: float = 1.0,
                                   max_context_len: Optional[int] = None,
                                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """``paged_decode_attention`` with fixed ``partition``-token splits that
-    reads each shared prefix once for all its sharers.  seq_group [B] int32
-    (-1 = none), group_members [num_groups, max_members] int32 (-1 padded, lead
-    first), prefix_tokens [num_groups] int32; ``max_prefix_tokens`` is a host
-    bound of prefix_tokens (default: the block-table capacity)."""
+    """``paged_decode_attention`` that reads each shared prefix once for all
+    its sharers (in ``partition``-token pieces) and the rest of every context
+    on the token-balanced schedule.  seq_group [B] int32 (-1 = none),
+    group_members [num_groups, max_members] int32 (-1 padded, lead first),
+    prefix_tokens [num_groups] int32; ``max_prefix_tokens`` is a host bound of
+    prefix_tokens (default: the block-table capacity)."""
+    if max_prefix_tokens is None:
+        max_prefix_tokens = block_tables.shape[1] * block_size
+    if workspace is None and q.shape[0]:
+        mcl = block_tables.shape[1] * block_size if max_context_len is None else max_context_len
+        need = prefix_workspace_size(q.shape[0], q.shape[1], num_kv_heads, q.shape[2], mcl,
+                                     partition, max_prefix_tokens)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
                               num_kv_heads, block_size, max_context_len, partition, workspace,
                               FP8_DTYPES if key_cache.dtype in FP8_DTYPES else torch.bfloat16)
@@ -327,8 +345,6 @@ def paged_decode_attention_prefix(out: torch.Tensor, q: torch.Tensor, key_cache:
     if seq_group.shape != (q.shape[0],):
         raise ValueError("seq_group must be [B]")
     num_groups, max_members = group_members.shape
-    if max_prefix_tokens is None:
-        max_prefix_tokens = block_tables.shape[1] * block_size
     K, bs, B, N, H, max_blocks, mcl, nb, part, pw, wbytes, stream = tail
     _check(lib().paged_decode_attention_prefix(
         *head, float(scale), KV_FP8_E4M3 if fp8 else KV_BF16, float(k_scale), float(v_scale),

@@ -82,6 +82,8 @@ struct DecodeParams {
     const int32_t *prefix_tokens; // [num_groups]: shared positions 0 .. prefix_tokens - 1
     int32_t num_groups;
     int32_t max_members;
+    int32_t max_prefix;           // cap on every shared span (whole partitions the
+                                  // workspace holds partials for)
     int32_t window;               // sliding window: attend the last `window` positions; 0 = all
 };
 
@@ -91,12 +93,13 @@ __device__ __forceinline__ int window_start(const DecodeParams &d, int ctx)
     return d.window > 0 ? max(ctx - d.window, 0) : 0;
 }
 
-// Prefix-aware decode: the leading fixed partitions of sequence b that its
-// prefix group computes once for all sharers (0 when b shares nothing).
-// Partition p qualifies when (p + 1) * part <= min(prefix_tokens[g], ctx_b,
-// ctx_lead), lead being the group's first sharer, whose block table holds
-// the shared block ids.
-__device__ __forceinline__ int prefix_shared_parts(const DecodeParams &d, int b)
+// Shared-prefix decode: sequence b's positions 0 .. S_b - 1 are read by its
+// prefix group's kernel (once for all members), the rest by b's own waves.
+// S_b = min(prefix_tokens[g], ctx_b, ctx_lead, max_prefix) rounded down to a
+// whole chunk, lead being the group's first member, whose block table holds
+// the shared block ids; 0 when b belongs to no group.  Both sides compute it
+// here.
+__device__ __forceinline__ int prefix_shared_tokens(const DecodeParams &d, int b)
 {
     const int g = d.seq_group[b];
     if (g < 0 || g >= d.num_groups)
@@ -106,8 +109,8 @@ __device__ __forceinline__ int prefix_shared_parts(const DecodeParams &d, int b)
         return 0;
     const int ctx_b = min(max(d.context_lens[b], 0), d.max_ctx);
     const int ctx_lead = min(max(d.context_lens[lead], 0), d.max_ctx);
-    const int span = min(min(d.prefix_tokens[g], ctx_b), ctx_lead);
-    return max(span, 0) / d.part;
+    const int span = min(min(min(d.prefix_tokens[g], ctx_b), ctx_lead), d.max_prefix);
+    return max(span, 0) / kChunk * kChunk;
 }
 
 __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)

@@ -9,8 +9,8 @@
 //
 //   * segments s = (sequence b, KV head kvh), in order b-major; segment s has
 //     nc_b = ceil(ctx_b / 32) chunks of 32 tokens (counted from the sliding
-//     window's first chunk, or, for kPrefix, after the partitions that b's
-//     prefix group computes);
+//     window's first chunk, or, for kPrefix, from the end of the positions
+//     that b's prefix group reads for it);
 //   * the flattened chunk list [0, T), T = K * sum_b nc_b, is split evenly:
 //     wave w gets chunks [floor(w T / W), floor((w+1) T / W));
 //   * a wave walks its chunks in order, crossing segment boundaries without
@@ -20,7 +20,10 @@
 // A piece that is a whole segment is normalised and written to `out` by its
 // wave.  Other pieces go to the workspace at slot w + s (unique: along the
 // flattened list every wave or segment boundary starts a new piece) and the
-// merge kernel combines them with the log-sum-exp rule.
+// merge kernel combines them with the log-sum-exp rule.  With kPrefix, a
+// sequence that shares positions with its prefix group never writes `out`
+// from the decode wave: its pieces are merged with the group kernel's
+// partials.
 //
 // For more than 256 sequences a one-workgroup schedule kernel runs first: it
 // scans the context lengths into chunk offsets cs[b] (exclusive prefix sum of
@@ -61,6 +64,8 @@ struct BalancedParams {
     int32_t inline_schedule;      // 1: small batch, waves scan the context lengths themselves
     int32_t part_chunks;          // kFixed: chunks per partition (partials to d.part_o /
                                   // d.part_ml); else unused
+    int32_t prefix_parts;         // kPrefix: prefix partials per member row (d.part_o /
+                                  // d.part_ml, d.part tokens each); else unused
 };
 
 constexpr int kInlineScheduleSeqs = 256;   // largest B scanned inside every wave
@@ -69,13 +74,13 @@ __device__ __forceinline__ int chunks_of(int ctx) { return (ctx + kChunk - 1) / 
 
 // A segment's chunks run from the 32-token boundary at or below the sliding
 // window's start (0 without a window) to the end of the context of sequence
-// b.  kPrefix (shared-prefix decode, fixed partitions, no window): from the
-// end of the partitions that b's prefix group computes for it.
+// b.  kPrefix (shared-prefix decode, no window): from the end of the
+// positions that b's prefix group reads for it (a chunk boundary).
 template <bool kPrefix = false>
 __device__ __forceinline__ int first_chunk(const DecodeParams &d, int b, int ctx)
 {
     if constexpr (kPrefix)
-        return ctx > 0 ? prefix_shared_parts(d, b) * (d.part / kChunk) : 0;
+        return ctx > 0 ? prefix_shared_tokens(d, b) / kChunk : 0;
     else
         return window_start(d, ctx) / kChunk;
 }
@@ -524,7 +529,8 @@ void decode_balanced_kernel(BalancedParams p)
             if (kFixed) {                               // a partition's split-K partial
                 kind = kStagePartial;
                 row = ((int64_t)ap.b * d.num_heads + n) * d.num_parts + pidx;
-            } else if (piece_from_start && seg_end) {   // the whole segment: final output
+            } else if (piece_from_start && seg_end && !(kPrefix && ap.fc > 0)) {
+                // the whole segment (and no prefix partials to join): final output
                 kind = kStageFinal;
                 row = (int64_t)ap.b * d.num_heads + n;
                 scl = d.out_scale / lt;
@@ -571,7 +577,10 @@ void decode_balanced_kernel(BalancedParams p)
 // Lane layout: heads padded to Gp (a power of two >= G), 64/Gp lanes per
 // head, each lane VPL = H*Gp/64 consecutive values of its head's row; a
 // piece's G rows are contiguous, so each piece is one coalesced read.
-template <int H, int Gp>
+// kPrefix: the row of a sequence with shared positions also joins its prefix
+// group's partials (ceil(S_b / P) of them, ahead of its pieces), also when
+// one wave holds the whole segment or the context has no chunk of its own.
+template <int H, int Gp, bool kPrefix = false>
 __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 {
     constexpr int kLanesPerHead = kWave / Gp;
@@ -597,7 +606,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             const int bb = t * kWave + lane;
-            c[t] = bb < B ? seg_chunks(d, bb, seq_ctx(d, bb)) : 0;
+            c[t] = bb < B ? seg_chunks<kPrefix>(d, bb, seq_ctx(d, bb)) : 0;
         }
         int total = 0, before = 0, mine = 0;
 #pragma unroll
@@ -613,29 +622,40 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
         T = (int64_t)total * K;
         seq_first = before;
     } else {
-        nc = seg_chunks(d, b, seq_ctx_uniform(d, b));
+        nc = seg_chunks<kPrefix>(d, b, seq_ctx_uniform(d, b));
         T = scalar_load(p.total_chunks);
         seq_first = scalar_load(p.chunk_start + b);
     }
+    int n_pre = 0;                        // prefix partials of this row
+    if constexpr (kPrefix)
+        n_pre = uniform((prefix_shared_tokens(d, b) + d.part - 1) / d.part);
     float *o = d.out + ((int64_t)b * d.num_heads + kvh * d.group + g) * H + h0;
-    if (nc == 0) {
+    if (nc == 0 && n_pre == 0) {
         if (live)
 #pragma unroll
             for (int v = 0; v < kVals; v += 4)
                 *reinterpret_cast<f32x4 *>(o + v) = f32x4{0.f, 0.f, 0.f, 0.f};
         return;
     }
-    const int64_t first = seq_first * K + (int64_t)kvh * nc;
-    const int w_first = wave_of(first, T, lg);
-    const int w_last = wave_of(first + nc - 1, T, lg);
-    if (w_first == w_last)
-        return;
+    int w_first = 0, count = 0;
+    if (nc > 0) {
+        const int64_t first = seq_first * K + (int64_t)kvh * nc;
+        w_first = wave_of(first, T, lg);
+        const int w_last = wave_of(first + nc - 1, T, lg);
+        if (w_first == w_last && n_pre == 0)
+            return;
+        count = w_last - w_first + 1;
+    }
     const int64_t seg = (int64_t)b * K + kvh;
-    const int count = w_last - w_first + 1;
+    const int total = n_pre + count;      // inputs: prefix partials, then pieces
     const int gg = live ? g : 0;
     auto empty = [&](int w) { return wave_begin(w, T, lg) == wave_begin(w + 1, T, lg); };
-    // piece (w, seg): rows (w + seg) * G + g' for the group's heads g'
-    auto row_of = [&](int w) { return ((int64_t)min(w, w_last) + seg) * d.group + gg; };
+    // Input i: prefix partial i (rows ((b K + kvh) prefix_parts + i) G + g'),
+    // else piece (w_first + i - n_pre, seg) (rows (w + seg) G + g').
+    auto row_of = [&](int i) {
+        return i < n_pre ? ((seg * p.prefix_parts + i) * d.group + gg)
+                         : (((int64_t)w_first + i - n_pre + seg) * d.group + gg);
+    };
 
     // Pieces are combined kBatch at a time: every load of a batch in one
     // memory round trip, then the batch joins the running log-sum-exp state
@@ -646,27 +666,33 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
     for (int v = 0; v < kVals / 4; ++v)
         num[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < count; i0 += kBatch) {
+    for (int i0 = 0; i0 < total; i0 += kBatch) {
         float mv[kBatch], lv[kBatch];
         f32x4 ov[kBatch][kVals / 4];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int64_t r = row_of(w_first + i0 + u);
-            mv[u] = p.piece_ml[2 * r];
-            lv[u] = p.piece_ml[2 * r + 1];
+            const int i = min(i0 + u, total - 1);
+            const bool pre = kPrefix && i < n_pre;
+            const int64_t r = row_of(i);
+            const float *mlp = pre ? d.part_ml : p.piece_ml;
+            const float *op = pre ? d.part_o : p.piece_o;
+            mv[u] = mlp[2 * r];
+            lv[u] = mlp[2 * r + 1];
 #pragma unroll
             for (int v = 0; v < kVals / 4; ++v)
-                ov[u][v] = *reinterpret_cast<const f32x4 *>(p.piece_o + r * H + h0 + 4 * v);
+                ov[u][v] = *reinterpret_cast<const f32x4 *>(op + r * H + h0 + 4 * v);
         }
         bool use[kBatch];
         float nb = big;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            use[u] = i0 + u < count && !empty(w_first + i0 + u);
+            const int i = i0 + u;
+            use[u] = i < total && (i < n_pre || !empty(w_first + i - n_pre));
             nb = use[u] ? fmaxf(nb, mv[u]) : nb;
         }
-        // The first batch holds the segment's first piece, so nb is finite from
-        // then on; a later batch of empty waves leaves it unchanged (sc = 1).
+        // The first batch holds the first prefix partial or the segment's
+        // first piece (each covers at least one position), so nb is finite
+        // from then on; a later batch of empty waves leaves it unchanged.
         const float sc = big == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(big - nb);
         den *= sc;
 #pragma unroll

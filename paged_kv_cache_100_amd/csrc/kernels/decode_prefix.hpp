@@ -3,22 +3,23 @@
 // Sequences that share a prompt prefix point their block tables at the same
 // physical blocks ("CS336 Lecture 10: Inference", part 6: shared prefix
 // blocks, copied on write).  Plain decode reads those blocks once per sharer.
-// Here a prefix group -- its sharers listed by the caller -- is processed
-// once per fixed partition of the shared region: the columns of the
-// matrix-core tiles are the (sharer, query head) pairs of a KV head's group,
-// so every load of a shared key or value serves all the sharers a wave
-// carries (up to four tiles, 64 pairs, per wave; more sharers take more waves,
-// placed on one XCD at consecutive slots so their repeated reads meet in
-// its L2).  Each sharer gets the partition's partial (m, l, o) in its own
-// split-K slot, exactly as the per-sequence kernel would have written it; the
-// per-sequence kernel skips those partitions, and the log-sum-exp merge is
-// unchanged.  The result is plain attention: paging and sharing only change
-// where the blocks are read from.
+// Here a prefix group -- its members listed by the caller -- reads its shared
+// span once: the span is cut into partitions of P tokens, and for each one a
+// wave's matrix-core tiles take as columns the (member, query head) pairs of
+// a KV head's group, so every load of a shared key or value serves all the
+// members the wave carries (up to four tiles, 64 pairs, per wave; more
+// members take more waves, placed on one XCD at consecutive slots so their
+// repeated reads meet in its L2).  Each member gets the partition's partial
+// (m, l, o) over its own shared positions; the token-balanced per-sequence
+// waves take the rest of every context, and their merge folds the prefix
+// partials in with the log-sum-exp rule.  The result is plain attention:
+// paging and sharing only change where the blocks are read from.
 //
-// Partition p of sequence b comes from the group kernel when b belongs to a
-// group g and (p + 1) * P <= min(prefix_tokens[g], ctx_b, ctx_lead), where
-// lead is the group's first sharer, whose block table supplies the shared
-// block ids; both kernels compute this bound the same way.
+// Member b of group g shares positions 0 .. S_b - 1 (prefix_shared_tokens:
+// the group's prefix, b's and the lead's contexts, rounded down to a chunk);
+// the group's partitions cover the lead's span, and b's columns are masked
+// from S_b on.  Partials go to row ((b * K + kvh) * prefix_parts + p) * G + g'
+// of d.part_o / d.part_ml, so a partition's G rows are contiguous.
 #pragma once
 
 #include "decode_multi.hpp"
@@ -26,9 +27,9 @@
 namespace pkv {
 
 struct PrefixParams {
-    DecodeParams d;                // split-K partials in d.part_o / d.part_ml, d.part = P,
+    DecodeParams d;                // prefix partials in d.part_o / d.part_ml, d.part = P,
                                    // groups in d.seq_group / d.group_members / d.prefix_tokens
-    int32_t prefix_parts;          // grid bound: max over groups of prefix_tokens / P
+    int32_t prefix_parts;          // partitions per member row: ceil(max shared span / P)
 };
 
 // Grid (one dimension, XCD-aware as in decode_multi_kernel): items =
@@ -57,32 +58,43 @@ void decode_prefix_kernel(PrefixParams p)
     const int lead = members[0];
     if (lead < 0 || lead >= d.num_seqs)
         return;
+    // The partition's positions within the lead's shared span.
+    const int span = min(min(max(d.prefix_tokens[grp], 0), d.max_prefix),
+                         min(max(d.context_lens[lead], 0), d.max_ctx)) / kChunk * kChunk;
     const int start = part_idx * d.part;
-    const int end = start + d.part;
-    // The shared span as the lead sees it; sharers shorter than this
-    // partition's end get nothing here (their own kernel covers it).
-    if (end > min(d.prefix_tokens[grp], min(max(d.context_lens[lead], 0), d.max_ctx)))
+    if (start >= span)
         return;
+    const int end = min(start + d.part, span);
+    const int n_blocks = (end - start) / kBlockSize;
 
-    const int first_block = start / kBlockSize;
-    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + first_block;
+    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + start / kBlockSize;
     int my_id = 0;
-    if (lane < d.part / kBlockSize)
+    if (lane < n_blocks)
         my_id = clamp_block(table[lane], d.num_blocks);
-    const int n_blocks = d.part / kBlockSize;
 
-    // Column t of this lane: sharer m, head g.
+    // Column t of this lane: member m, head g; lim: the end of the member's
+    // shared positions (a multiple of the chunk).
     bool live[kTiles];
+    int lim[kTiles];
     int64_t qrow[kTiles];
+    int64_t prow[kTiles];
+    bool short_col = false;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const int c = 16 * (kTiles * cg + t) + col;
         const int m = c / G;
         const int mb = m < d.max_members ? members[m] : -1;
-        live[t] = mb >= 0 && mb < d.num_seqs && d.seq_group[mb] == grp &&
-                  prefix_shared_parts(d, mb) > part_idx;
-        qrow[t] = (int64_t)(live[t] ? mb : lead) * d.num_heads + kvh * G + (c - m * G);
+        const bool in_group = mb >= 0 && mb < d.num_seqs && d.seq_group[mb] == grp;
+        const int own = in_group ? prefix_shared_tokens(d, mb) : 0;
+        live[t] = own > start;
+        lim[t] = live[t] ? min(own, end) : end;
+        short_col |= live[t] && own < end;
+        const int gh = c - m * G;
+        qrow[t] = (int64_t)(live[t] ? mb : lead) * d.num_heads + kvh * G + gh;
+        prow[t] = (((int64_t)(live[t] ? mb : 0) * d.num_kv_heads + kvh) * p.prefix_parts +
+                   part_idx) * G + gh;
     }
+    const bool mask = __builtin_amdgcn_ballot_w64(short_col) != 0;
 
     __shared__ u32x4 q_lds[kTiles * (H / 32) * kWave];
 #pragma unroll
@@ -112,45 +124,44 @@ void decode_prefix_kernel(PrefixParams p)
     };
 
     float m[kTiles], l[kTiles];
-    int lim[kTiles];
     f32x4 acc[kTiles][H / 16];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         m[t] = -INFINITY;
         l[t] = 0.f;
-        lim[t] = end;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
             acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Every position of the partition is valid for every live sharer.
+    // Every position of the partition is a cached token; a member whose
+    // shared span ends inside the partition has its later positions masked
+    // (whole chunks: spans are multiples of the chunk).
     auto attend = [&](Regs &r, int ci) {
         int opaque = lane;
         asm volatile("" : "+v"(opaque));
         auto qfrag = [&](int t, int s) {
             return as_bf16x8(q_lds[(t * (H / 32) + s) * kWave + opaque]);
         };
-        attend_chunk_multi<Fmt, H, kTiles, false>(r, qfrag, start + kChunk * ci + 8 * quad, lim,
-                                                  end - start - kChunk * ci, quad, d.scale_log2,
-                                                  m, l, acc);
+        attend_chunk_multi<Fmt, H, kTiles, true>(r, qfrag, start + kChunk * ci + 8 * quad, lim,
+                                                 end - start - kChunk * ci, quad, d.scale_log2,
+                                                 m, l, acc, mask);
     };
     constexpr int kRing = multi_ring_depth<Fmt, kTiles>();
     Regs ring[kRing];
-    run_ring<kRing>(d.part / kChunk, ring, issue, attend);
+    run_ring<kRing>((end - start) / kChunk, ring, issue, attend);
 
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const float lt = sum_over_rows(l[t]);
         if (!live[t])
             continue;
-        const int64_t slot = qrow[t] * d.num_parts + part_idx;
-        float *o = d.part_o + slot * H;
+        float *o = d.part_o + prow[t] * H;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
             *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * d.out_scale;
         if (quad == 0) {
-            d.part_ml[2 * slot] = m[t];
-            d.part_ml[2 * slot + 1] = lt;
+            d.part_ml[2 * prow[t]] = m[t];
+            d.part_ml[2 * prow[t] + 1] = lt;
         }
     }
 }

@@ -18,7 +18,7 @@
 namespace {
 
 constexpr int kVersionMajor = 1;
-constexpr int kVersionMinor = 5;
+constexpr int kVersionMinor = 6;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
@@ -64,8 +64,8 @@ size_t fixed_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_d
     return fixed_layout(num_seqs, num_heads, head_dim, max_ctx, part).total;
 }
 
-// The partials alone (the multi-query and prefix-group paths, which run one
-// wave per partition and need no schedule).
+// The partials alone (the multi-query path, which runs one wave per
+// partition and needs no schedule).
 size_t partials_bytes(int32_t num_rows, int32_t num_heads, int32_t head_dim, int32_t max_ctx,
                       int32_t part)
 {
@@ -99,6 +99,40 @@ BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_
     off = align256(off + (size_t)(pieces * group * 2 * 4));
     L.piece_o = off;
     off = align256(off + (size_t)(pieces * group * head_dim * 4));
+    L.total = off;
+    return L;
+}
+
+// Shared-prefix decode: the token-balanced layout, then the prefix group
+// kernel's partials, prefix_parts per (sequence, query head) row: [B][K]
+// [prefix_parts][G] rows of head_dim values, and their (m, l) pairs.
+struct PrefixLayout {
+    BalancedLayout bal;
+    size_t pre_o, pre_ml, total;
+};
+
+// Partitions of the longest shared span: its positions are a whole number of
+// chunks (the bound rounded down), cut into partitions of `part` tokens.
+int64_t prefix_parts_of(int32_t max_context_len, int32_t part, int32_t max_prefix_tokens)
+{
+    const int64_t span = (int64_t)(max_prefix_tokens < max_context_len ? max_prefix_tokens
+                                                                        : max_context_len);
+    if (span <= 0 || part <= 0)
+        return 0;
+    return ceil_div(span / pkv::kChunk * pkv::kChunk, part);
+}
+
+PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t prefix_parts)
+{
+    PrefixLayout L;
+    L.bal = balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim);
+    const int64_t rows = (int64_t)num_seqs * num_heads * prefix_parts;
+    size_t off = L.bal.total;
+    L.pre_o = off;
+    off = align256(off + (size_t)(rows * head_dim * 4));
+    L.pre_ml = off;
+    off = align256(off + (size_t)(rows * 2 * 4));
     L.total = off;
     return L;
 }
@@ -137,22 +171,24 @@ int device_waves(int *log2_waves)
 // Merge kernel of the balanced schedule for a head dim and group size: the
 // group is padded to a power of two, and to at least 256/H so that every
 // lane owns a whole 16-byte slice of a row.
-template <int H>
+template <int H, bool kPrefix>
 const void *merge_pieces_h(int group)
 {
     constexpr int kMin = 256 / H;
     const int gp = group <= kMin ? kMin : group <= 4 ? 4 : group <= 8 ? 8 : 16;
     switch (gp) {
-    case 2: return (const void *)pkv::merge_pieces_kernel<H, (kMin > 2 ? kMin : 2)>;
-    case 4: return (const void *)pkv::merge_pieces_kernel<H, 4>;
-    case 8: return (const void *)pkv::merge_pieces_kernel<H, 8>;
-    default: return (const void *)pkv::merge_pieces_kernel<H, 16>;
+    case 2: return (const void *)pkv::merge_pieces_kernel<H, (kMin > 2 ? kMin : 2), kPrefix>;
+    case 4: return (const void *)pkv::merge_pieces_kernel<H, 4, kPrefix>;
+    case 8: return (const void *)pkv::merge_pieces_kernel<H, 8, kPrefix>;
+    default: return (const void *)pkv::merge_pieces_kernel<H, 16, kPrefix>;
     }
 }
 
+template <bool kPrefix>
 const void *merge_pieces_for(int head_dim, int group)
 {
-    return head_dim == 128 ? merge_pieces_h<128>(group) : merge_pieces_h<64>(group);
+    return head_dim == 128 ? merge_pieces_h<128, kPrefix>(group)
+                           : merge_pieces_h<64, kPrefix>(group);
 }
 
 int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream)
@@ -229,8 +265,7 @@ int launch_merge(pkv::MergeParams &mp, int head_dim, int32_t num_kv_heads, int64
 // Fixed partitions (several) on persistent waves: schedule (large batches),
 // then the balanced kernel in partition mode writing every partition's
 // partial to the workspace's split-K slots; the caller launches the merge.
-// kPrefix: sequences skip the partitions their prefix group computes.
-template <class Fmt, bool kPrefix>
+template <class Fmt>
 int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
                       int32_t num_kv_heads, int32_t max_context_len, void *workspace,
                       size_t workspace_bytes, void *stream)
@@ -264,15 +299,58 @@ int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int3
     bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
     bp.part_chunks = part / pkv::kChunk;
     if (!bp.inline_schedule) {
+        rc = launch((const void *)pkv::schedule_kernel<false>, dim3(1),
+                    dim3(pkv::kScheduleThreads), &bp, stream);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    const void *dk = head_dim == 128
+                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, false>
+                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, false>;
+    return launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+}
+
+// Token-balanced decode: schedule (large batches), persistent decode, merge
+// of the split segments.  kPrefix: segments start after the positions each
+// sequence's prefix group reads (its prefix_parts partials per row are in
+// p.part_o / p.part_ml), and the merge joins those partials.
+template <class Fmt, bool kPrefix>
+int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_kv_heads,
+                    const BalancedLayout &L, char *ws, int64_t prefix_parts, void *stream)
+{
+    int log2_waves = 0;
+    int rc = device_waves(&log2_waves);
+    if (rc != PKV_OK)
+        return rc;
+    const int waves = 1 << log2_waves;
+    pkv::BalancedParams bp;
+    bp.d = p;
+    bp.total_chunks = reinterpret_cast<int32_t *>(ws + L.total_chunks);
+    bp.chunk_start = reinterpret_cast<int32_t *>(ws + L.chunk_start);
+    bp.wave_start = reinterpret_cast<int4 *>(ws + L.wave_start);
+    bp.piece_ml = reinterpret_cast<float *>(ws + L.piece_ml);
+    bp.piece_o = reinterpret_cast<float *>(ws + L.piece_o);
+    bp.num_waves = waves;
+    bp.log2_waves = log2_waves;
+    bp.num_seqs = num_seqs;
+    bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
+    bp.part_chunks = 0;
+    bp.prefix_parts = (int32_t)prefix_parts;
+    if (!bp.inline_schedule) {
         rc = launch((const void *)pkv::schedule_kernel<kPrefix>, dim3(1),
                     dim3(pkv::kScheduleThreads), &bp, stream);
         if (rc != PKV_OK)
             return rc;
     }
     const void *dk = head_dim == 128
-                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, kPrefix>
-                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, kPrefix>;
-    return launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, kPrefix>
+                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, kPrefix>;
+    rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
+    if (rc != PKV_OK)
+        return rc;
+    const void *mk = merge_pieces_for<kPrefix>(head_dim, p.group);
+    return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)num_seqs), dim3(pkv::kWave), &bp,
+                  stream);
 }
 
 template <class Fmt>
@@ -346,6 +424,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.prefix_tokens = nullptr;
     p.num_groups = 0;
     p.max_members = 0;
+    p.max_prefix = 0;
     p.window = window;
 
     if (partition_size == 0) {
@@ -357,39 +436,8 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
             return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace))
             return PKV_ERR_ALIGN;
-        int log2_waves = 0;
-        int rc = device_waves(&log2_waves);
-        if (rc != PKV_OK)
-            return rc;
-        const int waves = 1 << log2_waves;
-        char *ws = static_cast<char *>(workspace);
-        pkv::BalancedParams bp;
-        bp.d = p;
-        bp.total_chunks = reinterpret_cast<int32_t *>(ws + L.total_chunks);
-        bp.chunk_start = reinterpret_cast<int32_t *>(ws + L.chunk_start);
-        bp.wave_start = reinterpret_cast<int4 *>(ws + L.wave_start);
-        bp.piece_ml = reinterpret_cast<float *>(ws + L.piece_ml);
-        bp.piece_o = reinterpret_cast<float *>(ws + L.piece_o);
-        bp.num_waves = waves;
-        bp.log2_waves = log2_waves;
-        bp.num_seqs = num_seqs;
-        bp.inline_schedule = num_seqs <= pkv::kInlineScheduleSeqs;
-        bp.part_chunks = 0;
-        if (!bp.inline_schedule) {
-            rc = launch((const void *)pkv::schedule_kernel<false>, dim3(1),
-                        dim3(pkv::kScheduleThreads),
-                        &bp, stream);
-            if (rc != PKV_OK)
-                return rc;
-        }
-        const void *dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128>
-                                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64>;
-        rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
-        if (rc != PKV_OK)
-            return rc;
-        const void *mk = merge_pieces_for(head_dim, num_heads / num_kv_heads);
-        return launch(mk, dim3((unsigned)num_kv_heads, (unsigned)num_seqs), dim3(pkv::kWave), &bp,
-                      stream);
+        return balanced_launch<Fmt, false>(p, head_dim, num_seqs, num_kv_heads, L,
+                                           static_cast<char *>(workspace), 0, stream);
     }
 
     // Fixed partitions of partition_size tokens.  One partition: one wave per
@@ -406,7 +454,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
                                            : (const void *)pkv::decode_kernel<Fmt, 64>;
         return launch(kern, grid, dim3(pkv::kWave), &p, stream);
     }
-    int rc = persistent_launch<Fmt, false>(p, head_dim, num_seqs, num_heads, num_kv_heads,
+    int rc = persistent_launch<Fmt>(p, head_dim, num_seqs, num_heads, num_kv_heads,
                                            max_context_len, workspace, workspace_bytes, stream);
     if (rc != PKV_OK)
         return rc;
@@ -515,45 +563,38 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     return launch_merge(mp, head_dim, num_kv_heads, (int64_t)num_seqs * num_queries, stream);
 }
 
-// Prefix-aware decode: group kernel (shared partitions), persistent waves for
-// the rest of every sequence, merge.  With a single partition no partition
-// can lie wholly inside a shared prefix (which ends before the context does),
-// so that case is the plain kernel.
+// Prefix-aware decode: the group kernel reads every shared span once (its
+// partitions' partials per member), the token-balanced waves the rest of
+// every context, and their merge joins the two.
 template <class Fmt>
 int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
                          int32_t num_kv_heads, int32_t max_context_len, int32_t max_prefix_tokens,
                          void *workspace, size_t workspace_bytes, void *stream)
 {
-    const int32_t part = p.part;
-    const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
-    const bool split = parts > 1;
-    if (!split) {
-        p.num_parts = 1;
-        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128>
-                                           : (const void *)pkv::decode_kernel<Fmt, 64>;
-        return launch(kern, dim3(1u, (unsigned)num_kv_heads, (unsigned)num_seqs),
-                      dim3(pkv::kWave), &p, stream);
-    }
-    // Everything the persistent launch checks, before the group kernel runs.
-    const FixedLayout FL = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, part);
-    if (!workspace || workspace_bytes < FL.total)
+    const int64_t prefix_parts = prefix_parts_of(max_context_len, p.part, max_prefix_tokens);
+    const PrefixLayout L = prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim,
+                                         prefix_parts);
+    if (!workspace || workspace_bytes < L.total)
         return PKV_ERR_WORKSPACE;
     if (!aligned16(workspace))
         return PKV_ERR_ALIGN;
     if ((int64_t)num_seqs * num_kv_heads * ceil_div(max_context_len, pkv::kChunk) >= INT32_MAX)
         return PKV_ERR_SHAPE;
-    p.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + FL.part_o);
-    p.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + FL.part_ml);
-    p.num_parts = (int32_t)parts;
+    char *ws = static_cast<char *>(workspace);
+    p.part_o = reinterpret_cast<float *>(ws + L.pre_o);
+    p.part_ml = reinterpret_cast<float *>(ws + L.pre_ml);
+    p.num_parts = 1;
+    // No shared span outgrows the partials the workspace holds (a group whose
+    // prefix_tokens exceeds the stated bound shares only this much).
+    p.max_prefix = (int32_t)(prefix_parts * p.part);
 
-    const int64_t prefix_parts =
-        (int64_t)(max_prefix_tokens < max_context_len ? max_prefix_tokens : max_context_len) / part;
-    int rc = PKV_OK;
+    // The group kernel first: its partials must be complete when the merge
+    // of the per-sequence pieces (same stream, later) reads them.
     if (prefix_parts > 0 && p.num_groups > 0) {
         const int tiles = (int)ceil_div((int64_t)p.max_members * (num_heads / num_kv_heads), 16);
         const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
         int log2_waves = 0;
-        rc = device_waves(&log2_waves);
+        int rc = device_waves(&log2_waves);
         if (rc != PKV_OK)
             return rc;
         const int per_wave = prefix_tiles_per_wave(items, tiles, (int64_t)1 << log2_waves);
@@ -570,23 +611,8 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
         if (rc != PKV_OK)
             return rc;
     }
-    rc = persistent_launch<Fmt, true>(p, head_dim, num_seqs, num_heads, num_kv_heads,
-                                      max_context_len, workspace, workspace_bytes, stream);
-    if (rc != PKV_OK)
-        return rc;
-    pkv::MergeParams mp;
-    mp.out = p.out;
-    mp.part_o = p.part_o;
-    mp.part_ml = p.part_ml;
-    mp.context_lens = p.context_lens;
-    mp.num_queries = 1;
-    mp.window = p.window;
-    mp.num_heads = num_heads;
-    mp.max_ctx = max_context_len;
-    mp.part = part;
-    mp.num_parts = (int32_t)parts;
-    mp.group = num_heads / num_kv_heads;
-    return launch_merge(mp, head_dim, num_kv_heads, num_seqs, stream);
+    return balanced_launch<Fmt, true>(p, head_dim, num_seqs, num_kv_heads, L.bal, ws,
+                                      prefix_parts, stream);
 }
 
 }  // namespace
@@ -671,6 +697,20 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
     if (partition_size == 0)
         return balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim).total;
     return fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+}
+
+size_t paged_decode_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t max_context_len, int32_t partition_size,
+                                          int32_t max_prefix_tokens)
+{
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || partition_size <= 0 || max_prefix_tokens < 0 ||
+        num_heads % num_kv_heads != 0)
+        return 0;
+    return prefix_layout(num_seqs, num_heads, num_kv_heads, head_dim,
+                         prefix_parts_of(max_context_len, partition_size, max_prefix_tokens))
+        .total;
 }
 
 int paged_decode_attention(float *out, const void *q, const void *key_cache,
@@ -797,6 +837,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.prefix_tokens = nullptr;
     p.num_groups = 0;
     p.max_members = 0;
+    p.max_prefix = 0;
     p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_mq_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_queries, num_heads,
@@ -926,6 +967,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     p.prefix_tokens = prefix_tokens;
     p.num_groups = num_groups;
     p.max_members = max_members;
+    p.max_prefix = 0;
     p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_prefix_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_heads, num_kv_heads,

@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(L):
     assert {"paged_kv_append", "paged_decode_attention", "paged_decode_workspace_size",
             "paged_kv_append_fp8", "paged_decode_attention_fp8",
             "paged_decode_attention_mq", "paged_decode_mq_workspace_size",
-            "paged_decode_attention_prefix", "paged_kv_copy_blocks",
+            "paged_decode_attention_prefix", "paged_decode_prefix_workspace_size",
+            "paged_kv_copy_blocks",
             "paged_decode_attention_window",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
@@ -47,7 +48,7 @@ def test_status_strings(L):
     for code in range(-7, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
-    assert pkv.version() == "1.5"
+    assert pkv.version() == "1.6"
 
 
 def append(L, k=A, v=A, slots=A, kc=A, vc=A, T=4, K=2, H=64, bs=16, nb=8):
@@ -177,11 +178,34 @@ def test_decode_prefix_checks(L):
     assert decode_prefix(L, sg=0) == NULL
     assert decode_prefix(L, gm=0) == NULL
     assert decode_prefix(L, gm=0, ng=0) != NULL            # no groups: members not needed
-    assert decode_prefix(L, part=0) == SHAPE               # fixed partitions only
+    assert decode_prefix(L, part=0) == SHAPE               # prefix pieces need a length
+    assert decode_prefix(L, part=1056) == SHAPE            # at most 1024
+    assert decode_prefix(L, part=48) == SHAPE              # a multiple of 32
     assert decode_prefix(L, mm=300, N=8, K=2) == UNSUP     # 300 * 4 pairs > 1024
     assert decode_prefix(L, ng=-1) == SHAPE
     assert decode_prefix(L, pt=A + 2) == ALIGN
     assert decode_prefix(L, ws=0) == WS
+
+
+def test_prefix_workspace_size(L):
+    a256 = lambda x: (x + 255) // 256 * 256
+    bal = pkv.workspace_size(4, 8, 2, 64, 256, 0)
+    # shared span bound 100 -> 96 positions (whole chunks) -> two 64-token pieces
+    rows = 4 * 8 * 2
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 100) == (
+        bal + a256(rows * 64 * 4) + a256(rows * 2 * 4))
+    # no shared span: the token-balanced workspace alone
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 0) == bal
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 31) == bal
+    # the bound is clipped to the context bound
+    assert (pkv.prefix_workspace_size(4, 8, 2, 64, 128, 64, 5000) ==
+            pkv.prefix_workspace_size(4, 8, 2, 64, 128, 64, 128))
+    # the llama3-70B ragged mix: 992 shared positions in 256-token pieces
+    rows = 100 * 64 * 4
+    assert pkv.prefix_workspace_size(100, 64, 8, 128, 8192, 256, 992) == (
+        pkv.workspace_size(100, 64, 8, 128, 8192, 0) + a256(rows * 128 * 4) + a256(rows * 8))
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 0, 100) == 0
+    assert pkv.prefix_workspace_size(4, 8, 3, 64, 256, 64, 100) == 0
 
 
 def copy_blocks(L, kc=A, vc=A, src=A, dst=A, n=3, K=2, H=64, bs=16, nb=8, dt=0):

@@ -74,3 +74,42 @@ def test_full_size(name):
     with H.Timer(f"oracle on {len(rb)} sampled rows"):
         ref = H.oracle_decode_rows(w, inp, rb, rn)
     H.assert_parity(out.numpy()[rb, rn], ref, f"{name} sampled rows")
+
+
+@pytest.mark.parametrize("name", ["llama3_70b_ragged_b100", "llama3_70b_ragged_b100_fp8"])
+def test_full_size_shared_prefix(name):
+    """The ragged mix through the shared-prefix call as the benchmark's
+    prefix mode runs it (its 20 sharers' 62 shared blocks read once, in
+    256-token pieces): sampled rows -- the first and last sharer among them --
+    against the oracle, every row against plain decode of the same pools."""
+    import paged_kv_cache_100_amd as pkv
+    H.log(f"case {name} shared prefix (full size)")
+    with H.Timer("generate"):
+        w = W.make(name)
+    s = w.spec
+    dev = "cuda:0"
+    out, g = H.gpu_step(w)           # append, then plain decode
+    shared = len(w.shared_blocks) * s.bs
+    seq_group = torch.full((s.B,), -1, dtype=torch.int32)
+    seq_group[w.sharer_ids] = 0
+    members = torch.tensor([w.sharer_ids], dtype=torch.int32)
+    tokens = torch.tensor([shared], dtype=torch.int32)
+    got = torch.full((s.B, s.N, s.H), float("nan"), dtype=torch.float32, device=dev)
+    with H.Timer("gpu prefix decode"):
+        pkv.paged_decode_attention_prefix(got, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                          g.context_lens, w.scale, s.K, s.bs, 256,
+                                          seq_group.to(dev), members.to(dev), tokens.to(dev),
+                                          max_prefix_tokens=shared, k_scale=w.k_scale,
+                                          v_scale=w.v_scale, max_context_len=w.max_context_len)
+        torch.cuda.synchronize()
+    got = got.cpu()
+    assert torch.isfinite(got).all(), "non-finite output"
+    H.assert_parity(got.numpy(), out.numpy().astype(np.float64), f"{name} prefix vs plain")
+    inp = oracle_inputs(w)
+    H.oracle_append(w, inp)
+    del g
+    torch.cuda.empty_cache()
+    rb, rn = sample_rows(w, seed=1)
+    with H.Timer(f"oracle on {len(rb)} sampled rows"):
+        ref = H.oracle_decode_rows(w, inp, rb, rn)
+    H.assert_parity(got.numpy()[rb, rn], ref, f"{name} prefix sampled rows")

@@ -1,13 +1,18 @@
 """GPU: shared-prefix-aware decode and the copy-on-write block copy.
 
-``paged_decode_attention_prefix`` reads each shared prefix once per partition
-for all of its sharers.  What it computes is plain attention, so it is
-checked against the oracle's decode (``oracle.decode``) and, bit for bit,
-against ``paged_decode_attention`` with the same partition size: one group
-(the reduced ragged workload and its 20-sharer full size), several groups
-built by re-pointing block tables, more sharers than one wave carries,
+``paged_decode_attention_prefix`` reads each shared prefix once for all of
+its sharers (a group kernel over the shared span, in partition-sized pieces)
+and the rest of every context on the token-balanced schedule, then merges
+both.  What it computes is plain attention, so it is checked against the
+oracle's decode (``oracle.decode``) and, to the same tolerance, against plain
+``paged_decode_attention``: one group (the reduced ragged workload), several
+groups built by re-pointing block tables, more sharers than one wave carries,
 every tiles-per-wave choice of the group kernel, members shorter than the
-shared span, and FP8 pools.
+shared span, spans that end inside a partition, sequences wholly inside
+their shared span or with one chunk of their own, partition sizes, FP8
+pools.  A member whose table disagrees with the lead's over its shared span
+must get attention over the lead's blocks there: that pins that the shared
+positions really come from the group kernel.
 
 ``paged_kv_copy_blocks`` is bit-exact against ``oracle.copy_blocks`` for
 bf16 and FP8 pools, and a copy-on-write divergence (copy a shared block,
@@ -45,14 +50,7 @@ def groups_from(B, groups):
     return seq_group.to(DEV), members.to(DEV), tokens.to(DEV)
 
 
-def run_prefix(w, groups, partition, what):
-    """Append, then prefix-aware and plain decode on copies of the same pools;
-    compare with the oracle and with each other."""
-    H.log(f"case {what}: B={w.spec.B} N={w.spec.N} K={w.spec.K} {w.kv_dtype} part {partition} "
-          f"groups={[(len(m), t) for m, t in groups]}")
-    ref, inp = H.oracle_step(w)
-    g = w.to(DEV)
-    H.gpu_append(g, w)
+def prefix_decode(g, w, groups, partition):
     sg, gm, pt = groups_from(w.spec.B, groups)
     out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=DEV)
     pkv.paged_decode_attention_prefix(out, g.q, g.key_cache, g.value_cache, g.block_tables,
@@ -60,19 +58,38 @@ def run_prefix(w, groups, partition, what):
                                       sg, gm, pt, max_prefix_tokens=int(pt.max()),
                                       k_scale=w.k_scale, v_scale=w.v_scale,
                                       max_context_len=w.max_context_len)
+    return out
+
+
+def run_prefix(w, groups, partition, what, ref_tables=None):
+    """Append, then prefix-aware and plain decode on the same pools; compare
+    with the oracle (over ``ref_tables`` when given) and with each other."""
+    H.log(f"case {what}: B={w.spec.B} N={w.spec.N} K={w.spec.K} {w.kv_dtype} part {partition} "
+          f"groups={[(len(m), t) for m, t in groups]}")
+    inp = oracle_inputs(w)
+    H.oracle_append(w, inp)
+    if ref_tables is not None:
+        inp["block_tables"] = ref_tables
+    ref = H.oracle_decode(w, inp)
+    g = w.to(DEV)
+    H.gpu_append(g, w)
+    out = prefix_decode(g, w, groups, partition)
     plain = torch.full_like(out, float("nan"))
-    H.gpu_decode(plain, g, w, partition=partition)
+    H.gpu_decode(plain, g, w, partition=0)
     torch.cuda.synchronize()
     H.assert_append_exact(g, inp, what)
     H.assert_parity(out.cpu().numpy(), ref, what)
-    assert torch.equal(out, plain), f"{what}: differs from plain decode with the same partitions"
+    if ref_tables is None:
+        H.assert_parity(out.cpu().numpy(), plain.cpu().numpy().astype(np.float64),
+                        what + " vs plain decode")
+    return out
 
 
 def workload_groups(w):
     return [(w.sharer_ids, len(w.shared_blocks) * w.spec.bs)]
 
 
-@pytest.mark.parametrize("partition", [32, 64, 128])
+@pytest.mark.parametrize("partition", [32, 96, 256, 1024])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_ragged_small(kv, partition):
     spec = dataclasses.replace(W.small("llama3_70b_ragged_b100"), kv_dtype=kv)
@@ -113,15 +130,48 @@ def test_many_sharers(sharers):
     run_prefix(w, groups, 64, f"{sharers} sharers")
 
 
+@pytest.mark.parametrize("partition", [32, 96])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_sharers_wholly_shared(kv):
-    # sequences 1 and 2 (64 tokens) lie wholly in their group's partitions:
-    # no chunk of their own is left for the per-sequence waves
+def test_sharers_wholly_shared(kv, partition):
+    # sequences 1 and 2 (64 tokens) lie wholly in their shared span: no chunk
+    # of their own is left for the per-sequence waves (rows made of prefix
+    # partials alone); 5 (96 tokens) has one chunk of its own
     spec = W.Spec("whole", B=6, N=32, K=8, H=128, ctx=[700, 64, 64, 300, 33, 96], seed=97,
                   kv_dtype=kv)
     w = W.make(spec)
     groups = repoint(w, [(0, [1, 2, 5], 10)])
-    run_prefix(w, groups, 32, f"wholly shared {kv}")
+    run_prefix(w, groups, partition, f"wholly shared {kv} part {partition}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_members_read_the_leads_blocks(kv):
+    """Members whose own tables point elsewhere over the shared span get
+    attention over the lead's blocks there (and their own blocks after it):
+    the shared positions come from the group kernel, not from each member's
+    table."""
+    spec = W.Spec("lead", B=5, N=32, K=8, H=128, ctx=[500, 430, 300, 70, 520], seed=103,
+                  kv_dtype=kv, max_blocks=40)
+    w = W.make(spec)
+    members, tokens = [0, 1, 2, 3], 200
+    tables = w.block_tables.numpy().astype(np.int32).copy()
+    ctx = w.context_lens.numpy()
+    for b in members[1:]:
+        span = min(tokens, ctx[b], ctx[0]) // 32 * 32
+        tables[b, :span // 16] = tables[0, :span // 16]
+    run_prefix(w, [(members, tokens)], 64, f"lead's blocks {kv}", ref_tables=tables)
+
+
+@pytest.mark.parametrize("partition", [32, 64, 160, 1024])
+def test_span_ends_inside_a_partition(partition):
+    # spans of 1000 positions (992 shared: whole chunks) and of members
+    # shorter than that: 300 (-> 288), 150 (-> 128), 40 (-> 32), 20 (-> 0);
+    # the group kernel masks each member's columns past its own span
+    spec = W.Spec("spans", B=7, N=16, K=4, H=128, ctx=[1300, 1100, 300, 150, 40, 20, 1000],
+                  seed=107, max_blocks=90)
+    w = W.make(spec)
+    groups = repoint(w, [(0, [1, 2, 3, 4, 5, 6], 63)])
+    groups = [(groups[0][0], 1000)]
+    run_prefix(w, groups, partition, f"spans, part {partition}")
 
 
 def test_large_batch():
