@@ -346,7 +346,8 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache,
 /* Workspace bytes paged_decode_attention_prefix needs for these sizes (0 if
  * they are invalid): the token-balanced workspace plus the group kernel's
  * partials, ceil(min(max_prefix_tokens, max_context_len) rounded down to 32,
- * over partition_size) per (sequence, query head) row. */
+ * over partition_size) per (sequence, query head) row, plus one int32 per
+ * sequence. */
 size_t paged_decode_prefix_workspace_size(int32_t num_seqs, int32_t num_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
                                           int32_t max_context_len, int32_t partition_size,

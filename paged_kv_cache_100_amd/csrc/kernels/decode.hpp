@@ -84,6 +84,7 @@ struct DecodeParams {
     int32_t max_members;
     int32_t max_prefix;           // cap on every shared span (whole partitions the
                                   // workspace holds partials for)
+    int32_t *shared_tokens;       // [B]: S_b, written by the group kernel; null = none
     int32_t window;               // sliding window: attend the last `window` positions; 0 = all
 };
 
@@ -97,8 +98,16 @@ __device__ __forceinline__ int window_start(const DecodeParams &d, int ctx)
 // prefix group's kernel (once for all members), the rest by b's own waves.
 // S_b = min(prefix_tokens[g], ctx_b, ctx_lead, max_prefix) rounded down to a
 // whole chunk, lead being the group's first member, whose block table holds
-// the shared block ids; 0 when b belongs to no group.  Both sides compute it
-// here.
+// the shared block ids; 0 when b belongs to no group.  The group kernel
+// computes it (shared_span, from its group's values) and stores it in
+// d.shared_tokens for the per-sequence waves and the merge.
+__device__ __forceinline__ int shared_span(const DecodeParams &d, int prefix_tokens, int ctx_b,
+                                           int ctx_lead)
+{
+    const int span = min(min(min(prefix_tokens, ctx_b), ctx_lead), d.max_prefix);
+    return max(span, 0) / kChunk * kChunk;
+}
+
 __device__ __forceinline__ int prefix_shared_tokens(const DecodeParams &d, int b)
 {
     const int g = d.seq_group[b];
@@ -107,10 +116,16 @@ __device__ __forceinline__ int prefix_shared_tokens(const DecodeParams &d, int b
     const int lead = d.group_members[(int64_t)g * d.max_members];
     if (lead < 0 || lead >= d.num_seqs)
         return 0;
-    const int ctx_b = min(max(d.context_lens[b], 0), d.max_ctx);
-    const int ctx_lead = min(max(d.context_lens[lead], 0), d.max_ctx);
-    const int span = min(min(min(d.prefix_tokens[g], ctx_b), ctx_lead), d.max_prefix);
-    return max(span, 0) / kChunk * kChunk;
+    return shared_span(d, d.prefix_tokens[g], min(max(d.context_lens[b], 0), d.max_ctx),
+                       min(max(d.context_lens[lead], 0), d.max_ctx));
+}
+
+// S_b as the per-sequence side reads it (0 when no group kernel ran, and for
+// indices past the batch).  The load depends on nothing loaded before it, so
+// it shares a memory round trip with the context length.
+__device__ __forceinline__ int stored_shared_tokens(const DecodeParams &d, int b)
+{
+    return (d.shared_tokens && b < d.num_seqs) ? d.shared_tokens[b] : 0;
 }
 
 __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)

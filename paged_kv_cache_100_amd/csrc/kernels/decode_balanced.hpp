@@ -79,8 +79,10 @@ __device__ __forceinline__ int chunks_of(int ctx) { return (ctx + kChunk - 1) / 
 template <bool kPrefix = false>
 __device__ __forceinline__ int first_chunk(const DecodeParams &d, int b, int ctx)
 {
-    if constexpr (kPrefix)
-        return ctx > 0 ? prefix_shared_tokens(d, b) / kChunk : 0;
+    if constexpr (kPrefix) {
+        const int shared = stored_shared_tokens(d, b);
+        return ctx > 0 ? shared / kChunk : 0;
+    }
     else
         return window_start(d, ctx) / kChunk;
 }
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     }
     int n_pre = 0;                        // prefix partials of this row
     if constexpr (kPrefix)
-        n_pre = uniform((prefix_shared_tokens(d, b) + d.part - 1) / d.part);
+        n_pre = uniform((stored_shared_tokens(d, b) + d.part - 1) / d.part);
     float *o = d.out + ((int64_t)b * d.num_heads + kvh * d.group + g) * H + h0;
     if (nc == 0 && n_pre == 0) {
         if (live)

@@ -15,11 +15,13 @@
 // partials in with the log-sum-exp rule.  The result is plain attention:
 // paging and sharing only change where the blocks are read from.
 //
-// Member b of group g shares positions 0 .. S_b - 1 (prefix_shared_tokens:
-// the group's prefix, b's and the lead's contexts, rounded down to a chunk);
-// the group's partitions cover the lead's span, and b's columns are masked
-// from S_b on.  Partials go to row ((b * K + kvh) * prefix_parts + p) * G + g'
-// of d.part_o / d.part_ml, so a partition's G rows are contiguous.
+// Member b of group g shares positions 0 .. S_b - 1 (shared_span: the
+// group's prefix, b's and the lead's contexts, rounded down to a chunk); the
+// group's partitions cover the lead's span, and b's columns are masked from
+// S_b on.  Partials go to row ((b * K + kvh) * prefix_parts + p) * G + g' of
+// d.part_o / d.part_ml, so a partition's G rows are contiguous.  The first
+// ceil(B / 64) waves also store every S_b in d.shared_tokens (0 outside a
+// group), which the per-sequence waves and the merge read.
 #pragma once
 
 #include "decode_multi.hpp"
@@ -40,6 +42,11 @@ void decode_prefix_kernel(PrefixParams p)
 {
     const DecodeParams &d = p.d;
     const int L = blockIdx.x;
+    if ((int64_t)L * kWave < d.num_seqs) {
+        const int b = L * kWave + (int)threadIdx.x;
+        if (b < d.num_seqs)
+            d.shared_tokens[b] = prefix_shared_tokens(d, b);
+    }
     const int xcd = L % kXcds;
     const int j = L / kXcds;
     const int cg = j % d.col_groups;
@@ -58,19 +65,21 @@ void decode_prefix_kernel(PrefixParams p)
     const int lead = members[0];
     if (lead < 0 || lead >= d.num_seqs)
         return;
-    // The partition's positions within the lead's shared span.
-    const int span = min(min(max(d.prefix_tokens[grp], 0), d.max_prefix),
-                         min(max(d.context_lens[lead], 0), d.max_ctx)) / kChunk * kChunk;
+    // The partition's block ids (read before its length is known: as many as
+    // a partition holds, within the table row), then the partition's
+    // positions within the lead's shared span.
     const int start = part_idx * d.part;
+    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + start / kBlockSize;
+    int my_id = 0;
+    if (lane < d.part / kBlockSize && start / kBlockSize + lane < d.max_blocks)
+        my_id = clamp_block(table[lane], d.num_blocks);
+    const int prefix = d.prefix_tokens[grp];
+    const int ctx_lead = min(max(d.context_lens[lead], 0), d.max_ctx);
+    const int span = shared_span(d, prefix, ctx_lead, ctx_lead);
     if (start >= span)
         return;
     const int end = min(start + d.part, span);
     const int n_blocks = (end - start) / kBlockSize;
-
-    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + start / kBlockSize;
-    int my_id = 0;
-    if (lane < n_blocks)
-        my_id = clamp_block(table[lane], d.num_blocks);
 
     // Column t of this lane: member m, head g; lim: the end of the member's
     // shared positions (a multiple of the chunk).
@@ -85,7 +94,9 @@ void decode_prefix_kernel(PrefixParams p)
         const int m = c / G;
         const int mb = m < d.max_members ? members[m] : -1;
         const bool in_group = mb >= 0 && mb < d.num_seqs && d.seq_group[mb] == grp;
-        const int own = in_group ? prefix_shared_tokens(d, mb) : 0;
+        const int own =
+            in_group ? shared_span(d, prefix, min(max(d.context_lens[mb], 0), d.max_ctx), ctx_lead)
+                     : 0;
         live[t] = own > start;
         lim[t] = live[t] ? min(own, end) : end;
         short_col |= live[t] && own < end;

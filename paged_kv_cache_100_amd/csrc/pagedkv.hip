@@ -105,10 +105,11 @@ BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_
 
 // Shared-prefix decode: the token-balanced layout, then the prefix group
 // kernel's partials, prefix_parts per (sequence, query head) row: [B][K]
-// [prefix_parts][G] rows of head_dim values, and their (m, l) pairs.
+// [prefix_parts][G] rows of head_dim values, and their (m, l) pairs; then
+// every sequence's shared span S_b (int32).
 struct PrefixLayout {
     BalancedLayout bal;
-    size_t pre_o, pre_ml, total;
+    size_t pre_o, pre_ml, shared, total;
 };
 
 // Partitions of the longest shared span: its positions are a whole number of
@@ -133,6 +134,8 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     off = align256(off + (size_t)(rows * head_dim * 4));
     L.pre_ml = off;
     off = align256(off + (size_t)(rows * 2 * 4));
+    L.shared = off;
+    off = align256(off + (size_t)num_seqs * 4);
     L.total = off;
     return L;
 }
@@ -425,6 +428,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.num_groups = 0;
     p.max_members = 0;
     p.max_prefix = 0;
+    p.shared_tokens = nullptr;
     p.window = window;
 
     if (partition_size == 0) {
@@ -587,6 +591,7 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     // No shared span outgrows the partials the workspace holds (a group whose
     // prefix_tokens exceeds the stated bound shares only this much).
     p.max_prefix = (int32_t)(prefix_parts * p.part);
+    p.shared_tokens = nullptr;      // no group kernel: nothing is shared
 
     // The group kernel first: its partials must be complete when the merge
     // of the per-sequence pieces (same stream, later) reads them.
@@ -598,11 +603,15 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
         if (rc != PKV_OK)
             return rc;
         const int per_wave = prefix_tiles_per_wave(items, tiles, (int64_t)1 << log2_waves);
+        p.shared_tokens = reinterpret_cast<int32_t *>(ws + L.shared);
         pkv::PrefixParams pp;
         pp.d = p;
         pp.d.col_groups = (int32_t)ceil_div(tiles, per_wave);
         pp.prefix_parts = (int32_t)prefix_parts;
-        const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * pp.d.col_groups;
+        // At least one wave per 64 sequences: those store the shared spans.
+        int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * pp.d.col_groups;
+        if (waves < ceil_div(num_seqs, pkv::kWave))
+            waves = ceil_div(num_seqs, pkv::kWave);
         if (waves > INT32_MAX)
             return PKV_ERR_SHAPE;
         const void *gk = head_dim == 128 ? prefix_kernel<Fmt, 128>(per_wave)
@@ -838,6 +847,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.num_groups = 0;
     p.max_members = 0;
     p.max_prefix = 0;
+    p.shared_tokens = nullptr;
     p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_mq_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_queries, num_heads,
@@ -968,6 +978,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     p.num_groups = num_groups;
     p.max_members = max_members;
     p.max_prefix = 0;
+    p.shared_tokens = nullptr;
     p.window = 0;
     if (kv_dtype == PKV_KV_FP8_E4M3)
         return decode_prefix_launch<pkv::KvFp8>(p, head_dim, num_seqs, num_heads, num_kv_heads,

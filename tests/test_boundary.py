@@ -193,17 +193,18 @@ def test_prefix_workspace_size(L):
     # shared span bound 100 -> 96 positions (whole chunks) -> two 64-token pieces
     rows = 4 * 8 * 2
     assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 100) == (
-        bal + a256(rows * 64 * 4) + a256(rows * 2 * 4))
-    # no shared span: the token-balanced workspace alone
-    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 0) == bal
-    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 31) == bal
+        bal + a256(rows * 64 * 4) + a256(rows * 2 * 4) + a256(4 * 4))
+    # no shared span: the token-balanced workspace and the spans
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 0) == bal + 256
+    assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 64, 31) == bal + 256
     # the bound is clipped to the context bound
     assert (pkv.prefix_workspace_size(4, 8, 2, 64, 128, 64, 5000) ==
             pkv.prefix_workspace_size(4, 8, 2, 64, 128, 64, 128))
     # the llama3-70B ragged mix: 992 shared positions in 256-token pieces
     rows = 100 * 64 * 4
     assert pkv.prefix_workspace_size(100, 64, 8, 128, 8192, 256, 992) == (
-        pkv.workspace_size(100, 64, 8, 128, 8192, 0) + a256(rows * 128 * 4) + a256(rows * 8))
+        pkv.workspace_size(100, 64, 8, 128, 8192, 0) + a256(rows * 128 * 4) + a256(rows * 8) +
+        a256(100 * 4))
     assert pkv.prefix_workspace_size(4, 8, 2, 64, 256, 0, 100) == 0
     assert pkv.prefix_workspace_size(4, 8, 3, 64, 256, 64, 100) == 0
 
