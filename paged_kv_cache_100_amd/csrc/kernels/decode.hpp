@@ -393,17 +393,22 @@ __device__ __forceinline__ float block_reduce(float v, float *scratch)
 }
 
 // Log-sum-exp merge of the partitions of one (sequence, query token, query
-// head) row, one workgroup each: the partition maxima and weighted sums are
-// reduced across the threads, then kMergeThreads / H groups of H threads each
-// accumulate a strided subset of the partitions' o vectors, combined through
-// LDS.  Partition maxima are in log2 units; a row that saw no position in any
-// partition (maximum -inf, sums 0) gets zeros.
+// head) row, one workgroup each.  The partition maxima and weighted sums are
+// reduced across the threads; then kGroups groups of H/4 threads, each
+// thread four consecutive values of the row, accumulate every kGroups-th
+// partition's o with 16-byte loads, kUnroll partitions in flight per thread
+// (a row of hundreds of partitions is then a few memory round trips, not one
+// per partition), combined through LDS.  Partition maxima are in log2 units;
+// a row that saw no position in any partition (maximum -inf, sums 0) gets
+// zeros.
 template <int H>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
 {
-    constexpr int kGroups = kMergeThreads / H;
+    constexpr int kLanes = H / 4;                      // threads per partition row
+    constexpr int kGroups = kMergeThreads / kLanes;
+    constexpr int kUnroll = 8;
     __shared__ float red[kMergeThreads / kWave];
-    __shared__ float part_sum[kGroups][H];
+    __shared__ f32x4 part_sum[kGroups][kLanes];
 
     const int n = blockIdx.x;
     const int bq = blockIdx.y;                     // b * Q + query token
@@ -425,20 +430,36 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeParams p)
         den += __builtin_amdgcn_exp2f(ml[2 * j] - big) * ml[2 * j + 1];
     den = block_reduce<false>(den, red);
 
-    const int h = tid % H;
-    const int grp = tid / H;
-    float num = 0.f;
-#pragma unroll 4
-    for (int j = first + grp; j < parts; j += kGroups)
-        num += __builtin_amdgcn_exp2f(ml[2 * j] - big) * po[(int64_t)j * H + h];
-    part_sum[grp][h] = num;
+    const int h4 = tid % kLanes;
+    const int grp = tid / kLanes;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    int j = first + grp;
+    for (; j + (kUnroll - 1) * kGroups < parts; j += kUnroll * kGroups) {
+        f32x4 v[kUnroll];
+        float m[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int jj = j + u * kGroups;
+            v[u] = *reinterpret_cast<const f32x4 *>(po + (int64_t)jj * H + 4 * h4);
+            m[u] = ml[2 * jj];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            num += __builtin_amdgcn_exp2f(m[u] - big) * v[u];
+    }
+    for (; j < parts; j += kGroups)
+        num += __builtin_amdgcn_exp2f(ml[2 * j] - big) *
+               *reinterpret_cast<const f32x4 *>(po + (int64_t)j * H + 4 * h4);
+    part_sum[grp][h4] = num;
     __syncthreads();
     if (grp == 0) {
-        float total = 0.f;
+        f32x4 total = part_sum[0][h4];
 #pragma unroll
-        for (int g2 = 0; g2 < kGroups; ++g2)
-            total += part_sum[g2][h];
-        p.out[row * H + h] = (parts && den > 0.f) ? total / den : 0.f;
+        for (int g2 = 1; g2 < kGroups; ++g2)
+            total += part_sum[g2][h4];
+        // A row with no position has big = -inf and NaN weights: select zeros.
+        *reinterpret_cast<f32x4 *>(p.out + row * H + 4 * h4) =
+            (parts && den > 0.f) ? total * (1.0f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 }
 
