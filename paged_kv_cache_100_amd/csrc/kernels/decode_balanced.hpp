@@ -52,7 +52,8 @@ constexpr int kScheduleThreads = 1024;
 constexpr int kMaxBalancedWaves = 4096;
 
 struct BalancedParams {
-    DecodeParams d;               // shapes, pointers, scale (part / num_parts: kFixed only)
+    DecodeParams d;               // shapes, pointers, scale (part: kFixed partitions or
+                                  // kPrefix pieces; num_parts: kFixed only)
     int32_t *chunk_start;         // [B + 1]: exclusive prefix sum of nc_b (schedule output)
     int32_t *total_chunks;        // [1]: T = K * chunk_start[B]
     int4 *wave_start;             // [W]: (b, kvh, chunk in segment, ctx of b)
