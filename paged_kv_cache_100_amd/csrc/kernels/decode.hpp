@@ -56,8 +56,9 @@ constexpr int kChunk = 32;   // tokens per inner step (two cache blocks)
 
 struct DecodeParams {
     float *out;                   // [B][N][H]
-    float *part_o;                // [B][N][P][H]   (split only)
-    float *part_ml;               // [B][N][P][2]   (split only)
+    float *part_o;                // [B][N][P][H]   (split only; prefix pieces:
+                                  //                 [B][K][pieces][G][H])
+    float *part_ml;               // [B][N][P][2]   (likewise, pairs (m, l))
     const uint16_t *q;            // [B][N][H] bf16
     const void *key_cache;        // [num_blocks][K][16][H]  (Fmt::Elem)
     const void *value_cache;      // [num_blocks][K][H][16]  (Fmt::Elem)
