@@ -113,3 +113,27 @@ def test_full_size_shared_prefix(name):
     with H.Timer(f"oracle on {len(rb)} sampled rows"):
         ref = H.oracle_decode_rows(w, inp, rb, rn)
     H.assert_parity(got.numpy()[rb, rn], ref, f"{name} prefix sampled rows")
+
+
+def test_full_size_window():
+    """Llama-3-8B, B 64 x 8k, with a 4,096-token sliding window, as the
+    benchmark's `--window 4096` runs it (token-balanced schedule): every row
+    against the oracle's windowed decode."""
+    name, window = "llama3_8b_b64_ctx8k", 4096
+    H.log(f"case {name} window {window} (full size)")
+    with H.Timer("generate"):
+        w = W.make(name)
+    g = w.to("cuda:0")
+    H.gpu_append(g, w)
+    out = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device="cuda:0")
+    with H.Timer("gpu window decode"):
+        H.gpu_decode_window(out, g, w, window, partition=0)
+        torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del g
+    torch.cuda.empty_cache()
+    inp = oracle_inputs(w)
+    H.oracle_append(w, inp)
+    with H.Timer("oracle windowed decode, all rows"):
+        ref = H.oracle_decode_window(w, inp, window)
+    H.assert_parity(got, ref, f"{name} window {window}")
