@@ -16,8 +16,16 @@ import gpu_harness as H
 pytestmark = pytest.mark.gpu
 
 
+class spec_w:
+    """A made workload passed to run_case in place of its Spec."""
+    def __init__(self, workload):
+        self.workload = workload
+
+
 def run_case(spec, partition=0, what=None):
-    w = W.make(spec)
+    """spec: a workload Spec, or an already made Workload (spec_w)."""
+    w = spec.workload if isinstance(spec, spec_w) else W.make(spec)
+    spec = w.spec
     what = what or spec.name
     H.log(f"case {what}: B={spec.B} N={spec.N} K={spec.K} H={spec.H} partition={partition} "
           f"ctx={w.context_lens.tolist()[:12]}")
@@ -94,3 +102,26 @@ def test_one_long_sequence_among_short_ones():
     # one segment spread over many waves, the others each inside one wave
     spec = W.Spec("skew", B=9, N=64, K=8, H=128, ctx=[6000] + [40] * 8, seed=41)
     run_case(spec, partition=0, what="skewed")
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+def test_zero_scale_is_the_mean_of_the_values(partition):
+    # scale 0: every position weighs the same, so each output row is the plain
+    # mean of its sequence's value rows (the appended token included) -- a
+    # closed form, gathered here through the block table with numpy
+    spec = W.Spec("mean", B=5, N=16, K=4, H=128, ctx=[1, 17, 100, 333, 1024], seed=139)
+    w = W.make(spec)
+    w.scale = 0.0
+    _, out, _ = run_case(spec_w(w), partition=partition, what=f"scale 0, partition {partition}")
+    from _util import bits_to_f64, oracle_inputs
+    inp = oracle_inputs(w)
+    H.oracle_append(w, inp)
+    vc = bits_to_f64(inp["value_cache"])                     # [nb][K][H][16]
+    G = spec.N // spec.K
+    expect = np.zeros((spec.B, spec.N, spec.H))
+    for b, c in enumerate(w.context_lens.tolist()):
+        t = np.arange(c)
+        blocks = inp["block_tables"][b, t // 16]
+        vals = vc[blocks, :, :, t % 16]                         # [c][K][H]
+        expect[b] = np.repeat(vals.mean(axis=0), G, axis=0)
+    H.assert_parity(out.numpy(), expect, f"scale 0, partition {partition}, closed form")
