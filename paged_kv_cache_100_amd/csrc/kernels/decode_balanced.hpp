@@ -575,8 +575,11 @@ void decode_balanced_kernel(BalancedParams p)
 // One wave per segment (sequence, KV head): combines the pieces of the
 // segment for all G query heads of its group, or writes zeros for an empty
 // sequence.  Segments held whole by one wave were written by that wave and
-// are skipped.  Waves between the segment's first and last may own no chunk
-// at all (when the batch has fewer chunks than waves); they wrote no piece.
+// are skipped.  The segment's pieces are the waves that hold its chunks:
+// with at least as many chunks as waves (T >= W) every wave holds one or
+// more, so they are the waves w_first .. w_last; with fewer (T < W) every
+// wave holds at most one, so they are the waves of its nc chunks, and the
+// empty waves between them are never read.
 // Lane layout: heads padded to Gp (a power of two >= G), 64/Gp lanes per
 // head, each lane VPL = H*Gp/64 consecutive values of its head's row; a
 // piece's G rows are contiguous, so each piece is one coalesced read.
@@ -640,24 +643,28 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
                 *reinterpret_cast<f32x4 *>(o + v) = f32x4{0.f, 0.f, 0.f, 0.f};
         return;
     }
+    const bool sparse = T < ((int64_t)1 << lg);   // fewer chunks than waves
+    const int64_t first = seq_first * K + (int64_t)kvh * nc;
     int w_first = 0, count = 0;
     if (nc > 0) {
-        const int64_t first = seq_first * K + (int64_t)kvh * nc;
         w_first = wave_of(first, T, lg);
         const int w_last = wave_of(first + nc - 1, T, lg);
         if (w_first == w_last && n_pre == 0)
             return;
-        count = w_last - w_first + 1;
+        count = sparse ? nc : w_last - w_first + 1;
     }
     const int64_t seg = (int64_t)b * K + kvh;
     const int total = n_pre + count;      // inputs: prefix partials, then pieces
     const int gg = live ? g : 0;
-    auto empty = [&](int w) { return wave_begin(w, T, lg) == wave_begin(w + 1, T, lg); };
     // Input i: prefix partial i (rows ((b K + kvh) prefix_parts + i) G + g'),
-    // else piece (w_first + i - n_pre, seg) (rows (w + seg) G + g').
-    auto row_of = [&](int i) {
-        return i < n_pre ? ((seg * p.prefix_parts + i) * d.group + gg)
-                         : (((int64_t)w_first + i - n_pre + seg) * d.group + gg);
+    // else piece j = i - n_pre, written by wave w_first + j (or, sparse, by
+    // the wave of chunk first + j) at rows (w + seg) G + g'.
+    auto row_of = [&](int i) -> int64_t {
+        if (i < n_pre)
+            return (seg * p.prefix_parts + i) * d.group + gg;
+        const int j = i - n_pre;          // a piece exists, so nc > 0 and T > 0
+        const int64_t w = sparse ? wave_of(first + j, T, lg) : (int64_t)w_first + j;
+        return (w + seg) * d.group + gg;
     };
 
     // Pieces are combined kBatch at a time: every load of a batch in one
@@ -690,12 +697,11 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int i = i0 + u;
-            use[u] = i < total && (i < n_pre || !empty(w_first + i - n_pre));
+            use[u] = i < total;
             nb = use[u] ? fmaxf(nb, mv[u]) : nb;
         }
-        // The first batch holds the first prefix partial or the segment's
-        // first piece (each covers at least one position), so nb is finite
-        // from then on; a later batch of empty waves leaves it unchanged.
+        // Every input covers at least one position, so nb is finite from the
+        // first batch on.
         const float sc = big == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(big - nb);
         den *= sc;
 #pragma unroll

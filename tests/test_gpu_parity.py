@@ -104,6 +104,36 @@ def test_one_long_sequence_among_short_ones():
     run_case(spec, partition=0, what="skewed")
 
 
+def resident_waves():
+    """Waves of the token-balanced schedule: four per compute unit (one per
+    SIMD), rounded down to a power of two, at most 4096."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = 1
+    while 2 * w <= min(4 * cus, 4096):
+        w *= 2
+    return w
+
+
+@pytest.mark.parametrize("delta", [-1, 0, 2], ids=["below", "equal", "above"])
+def test_chunk_count_around_the_wave_count(delta):
+    # one sequence over eight KV heads: T = 8 * chunks 32-token chunks against
+    # W waves.  Below W every wave holds at most one chunk and the merge finds
+    # each piece by its chunk; from W on every wave holds at least one and the
+    # pieces are consecutive waves.
+    chunks = resident_waves() // 8 + delta
+    spec = W.Spec("around", B=1, N=32, K=8, H=128, ctx=[32 * chunks - 5], seed=151)
+    run_case(spec, partition=0, what=f"T = W {delta * 8:+d}")
+
+
+def test_several_chunk_segments_with_fewer_chunks_than_waves():
+    # T = 8 * (10 + 1 + 22 + 3) = 288 chunks, far below the wave count: the
+    # longer segments are split into one-chunk pieces in waves that lie
+    # between empty ones
+    spec = W.Spec("sparse", B=4, N=32, K=8, H=128, ctx=[300, 1, 700, 70], seed=157)
+    run_case(spec, partition=0, what="sparse pieces")
+
+
 @pytest.mark.parametrize("partition", [0, 64])
 def test_zero_scale_is_the_mean_of_the_values(partition):
     # scale 0: every position weighs the same, so each output row is the plain
