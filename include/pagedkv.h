@@ -325,13 +325,13 @@ int paged_decode_attention_window(float *out, const void *q,
  *                  every member map to the same physical blocks as the lead's.
  *   max_prefix_tokens  host-known bound of prefix_tokens.
  *   Member b of group g shares positions 0 .. S_b - 1, S_b = min(
- *   prefix_tokens[g], ctx_b, ctx_lead) rounded down to a multiple of 32: one
- *   group kernel reads them for all members, in partitions of partition_size
- *   P tokens (a multiple of 32 in [32, 1024]: smaller partitions spread the
- *   shared span over more waves, each adding one partial per member row to
- *   merge); the rest of every context runs on the token-balanced schedule
- *   of paged_decode_attention with partition_size 0, and one merge joins
- *   both.  max_members * (N / K) <= PKV_MAX_PREFIX_ROWS.  A member whose
+ *   prefix_tokens[g], ctx_b, ctx_lead) rounded down to a multiple of 32:
+ *   the group's waves read them once for all members, in partitions of
+ *   partition_size P tokens (a multiple of 32 in [32, 1024]: smaller
+ *   partitions spread the shared span over more waves, each adding one
+ *   partial per member row to merge); the rest of every context runs on the
+ *   token-balanced schedule of paged_decode_attention with partition_size 0,
+ *   in the same grid ahead of the group waves, and one merge joins both.  max_members * (N / K) <= PKV_MAX_PREFIX_ROWS.  A member whose
  *   table disagrees with the lead's over its shared span gets attention over
  *   the lead's blocks there.  Workspace: paged_decode_prefix_workspace_size
  *   bytes; kv_dtype, k_scale, v_scale as for paged_decode_attention_mq; other
@@ -344,7 +344,7 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache,
                          void *stream);
 
 /* Workspace bytes paged_decode_attention_prefix needs for these sizes (0 if
- * they are invalid): the token-balanced workspace plus the group kernel's
+ * they are invalid): the token-balanced workspace plus the group waves'
  * partials, ceil(min(max_prefix_tokens, max_context_len) rounded down to 32,
  * over partition_size) per (sequence, query head) row, plus one int32 per
  * sequence. */

@@ -43,7 +43,7 @@
 // across partitions instead of paying a start-up per partition.
 #pragma once
 
-#include "decode.hpp"
+#include "decode_prefix.hpp"
 #include "pagedkv.h"
 
 namespace pkv {
@@ -254,13 +254,30 @@ struct BalancedBuf {
     u32x4 q[H / 32];
 };
 
-template <class Fmt, int H, bool kFixed = false, bool kPrefix = false>
+// kGroupTiles > 0 (with kPrefix): the grid also holds the prefix groups'
+// waves (prefix_group_wave, kGroupTiles tiles each) after the W persistent
+// ones; they share the stage's LDS.  For small batches they also store the
+// shared spans for the merge, which the persistent waves compute for
+// themselves.
+template <class Fmt, int H, bool kFixed = false, bool kPrefix = false, int kGroupTiles = 0>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
     using Elem = typename Fmt::Elem;
     using Buf = BalancedBuf<Fmt, H>;
     const DecodeParams &d = p.d;
+    __shared__ f32x4 stage_o[kStageBytes / 16];    // staged pieces (see below)
+    if constexpr (kGroupTiles > 0) {
+        static_assert(kPrefix && kGroupTiles * (H / 32) * kWave * 16 <= kStageBytes,
+                      "group queries fit the stage");
+        if ((int)blockIdx.x >= p.num_waves) {
+            prefix_group_wave<Fmt, H, kGroupTiles>(d, p.prefix_parts,
+                                                   (int)blockIdx.x - p.num_waves,
+                                                   reinterpret_cast<u32x4 *>(stage_o),
+                                                   p.inline_schedule != 0);
+            return;
+        }
+    }
     const int wv = blockIdx.x;
     const int lane = threadIdx.x;
     const int col = lane & 15;
@@ -277,19 +294,46 @@ void decode_balanced_kernel(BalancedParams p)
     int4 st = make_int4(0, 0, 0, 0);
     int4 st_end = make_int4(0, 0, 0, 0);   // kFixed: the position of c_end (x, z, w used)
     int c_begin, c_end;
+    // kPrefix, small batches: S_b of sequence t * 64 + lane, computed here
+    // from the groups (larger batches read d.shared_tokens, which a kernel
+    // before this one stores).
+    constexpr int kTiles = kInlineScheduleSeqs / kWave;
+    int shv[kTiles];
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+        shv[t] = 0;
+    // kPrefix: first chunk of sequence b's segments (b the same in every
+    // lane); the other instances call first_chunk / seg_chunks directly.
+    auto fc_at = [&](int b, int ctx) {
+        if (!p.inline_schedule)
+            return first_chunk<kPrefix>(d, b, ctx);
+        int span = 0;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t)
+            span = (b >> 6) == t ? __builtin_amdgcn_readlane(shv[t], b & 63) : span;
+        return ctx > 0 ? span / kChunk : 0;
+    };
+    auto nc_at = [&](int b, int ctx) { return chunks_of(ctx) - fc_at(b, ctx); };
     if (p.inline_schedule) {
-        constexpr int kTiles = kInlineScheduleSeqs / kWave;
         int cx[kTiles];
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
             const int b = t * kWave + lane;
             cx[t] = b < B ? seq_ctx(d, b) : 0;
+            if constexpr (kPrefix)
+                shv[t] = b < B && d.shared_tokens ? prefix_shared_tokens(d, b) : 0;
         }
+        // kPrefix: chunks of the lane's sequence in tile t.
+        auto nc_lane = [&](int t) { return chunks_of(cx[t]) - (cx[t] > 0 ? shv[t] / kChunk : 0); };
         int total_seq = 0;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t)
-            if (t * kWave < B)             // tiles past the batch hold zeros
-                total_seq += wave_sum(seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]));
+            if (t * kWave < B) {           // tiles past the batch hold zeros
+                if constexpr (kPrefix)
+                    total_seq += wave_sum(nc_lane(t));
+                else
+                    total_seq += wave_sum(seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]));
+            }
         T = (int64_t)uniform(total_seq) * K;
         if (T == 0)
             return;
@@ -304,7 +348,11 @@ void decode_balanced_kernel(BalancedParams p)
         bool found = false, found_end = !kFixed || c_end >= T;
 #pragma unroll
         for (int t = 0; t < kTiles; ++t) {
-            const int nc = seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]);
+            int nc;
+            if constexpr (kPrefix)
+                nc = nc_lane(t);
+            else
+                nc = seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]);
             const int incl = wave_inclusive_scan(nc, lane);
             const int tile_total = __shfl(incl, kWave - 1);
             if (!found && (int64_t)(carry + tile_total) * K > c_begin) {
@@ -368,8 +416,13 @@ void decode_balanced_kernel(BalancedParams p)
     start.kvh = uniform(st.y);
     start.j = uniform(st.z);
     start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
-    start.nc = seg_chunks<kPrefix>(d, start.b, start.ctx);
-    start.fc = first_chunk<kPrefix>(d, start.b, start.ctx);
+    if constexpr (kPrefix) {
+        start.nc = nc_at(start.b, start.ctx);
+        start.fc = fc_at(start.b, start.ctx);
+    } else {
+        start.nc = seg_chunks<kPrefix>(d, start.b, start.ctx);
+        start.fc = first_chunk<kPrefix>(d, start.b, start.ctx);
+    }
     if (start.j >= start.nc)          // cannot happen for a consistent schedule
         return;
 
@@ -379,9 +432,16 @@ void decode_balanced_kernel(BalancedParams p)
         int ctx = nb < B ? seq_ctx_uniform(d, nb) : 0;
         // Without kPrefix only an empty context has no chunks; with it, so has
         // a sharer whose context lies wholly in its group's partitions.
-        while ((kPrefix ? seg_chunks<kPrefix>(d, nb, ctx) == 0 : ctx == 0) && nb + 1 < B) {
-            ++nb;
-            ctx = seq_ctx_uniform(d, nb);
+        if constexpr (kPrefix) {
+            while (nc_at(nb, ctx) == 0 && nb + 1 < B) {
+                ++nb;
+                ctx = seq_ctx_uniform(d, nb);
+            }
+        } else {
+            while (ctx == 0 && nb + 1 < B) {
+                ++nb;
+                ctx = seq_ctx_uniform(d, nb);
+            }
         }
         return make_int2(nb, ctx);
     };
@@ -395,8 +455,13 @@ void decode_balanced_kernel(BalancedParams p)
         const int2 nx = next_seq(q.b);
         q.b = nx.x;
         q.ctx = nx.y;
-        q.nc = seg_chunks<kPrefix>(d, q.b, q.ctx);
-        q.fc = first_chunk<kPrefix>(d, q.b, q.ctx);
+        if constexpr (kPrefix) {
+            q.nc = nc_at(q.b, q.ctx);
+            q.fc = fc_at(q.b, q.ctx);
+        } else {
+            q.nc = seg_chunks<kPrefix>(d, q.b, q.ctx);
+            q.fc = first_chunk<kPrefix>(d, q.b, q.ctx);
+        }
     };
 
     const int64_t tile_elems = (int64_t)kBlockSize * H;
@@ -454,7 +519,6 @@ void decode_balanced_kernel(BalancedParams p)
     // of order), which stalls the wave for a full memory latency.
     // Only the G live columns are kept: a piece takes G * H * 4 bytes, so
     // the stage holds more pieces for smaller groups (up to kStageMax).
-    __shared__ f32x4 stage_o[kStageBytes / 16];
     __shared__ int64_t stage_row[kStageMax][16];   // destination row of each column
     __shared__ float stage_m[kStageMax][16];
     __shared__ float stage_l[kStageMax][16];

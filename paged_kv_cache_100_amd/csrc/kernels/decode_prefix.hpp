@@ -19,30 +19,37 @@
 // group's prefix, b's and the lead's contexts, rounded down to a chunk); the
 // group's partitions cover the lead's span, and b's columns are masked from
 // S_b on.  Partials go to row ((b * K + kvh) * prefix_parts + p) * G + g' of
-// d.part_o / d.part_ml, so a partition's G rows are contiguous.  The first
-// ceil(B / 64) waves also store every S_b in d.shared_tokens (0 outside a
-// group), which the per-sequence waves and the merge read.
+// d.part_o / d.part_ml, so a partition's G rows are contiguous.  Every S_b
+// is stored in d.shared_tokens (0 outside a group) for the merge: by the first
+// ceil(B / 64) group waves for batches the per-sequence waves scan themselves
+// (they compute S_b too), else by a small kernel before the per-sequence ones,
+// which read it.  The group waves run in the token-balanced kernel's grid,
+// after its persistent waves: the dispatcher places them as those finish, so
+// they fill the idle SIMDs of its tail.
 #pragma once
 
 #include "decode_multi.hpp"
 
 namespace pkv {
 
-struct PrefixParams {
-    DecodeParams d;                // prefix partials in d.part_o / d.part_ml, d.part = P,
-                                   // groups in d.seq_group / d.group_members / d.prefix_tokens
-    int32_t prefix_parts;          // partitions per member row: ceil(max shared span / P)
-};
-
-// Grid (one dimension, XCD-aware as in decode_multi_kernel): items =
-// (group * K + kvh) * prefix_parts + partition, col_groups waves each.
-template <class Fmt, int H, int kTiles>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_prefix_kernel(PrefixParams p)
+// One thread per sequence: d.shared_tokens[b] = S_b.
+__global__ __launch_bounds__(kWave) void prefix_spans_kernel(DecodeParams d)
 {
-    const DecodeParams &d = p.d;
-    const int L = blockIdx.x;
-    if ((int64_t)L * kWave < d.num_seqs) {
+    const int b = (int)blockIdx.x * kWave + (int)threadIdx.x;
+    if (b < d.num_seqs)
+        d.shared_tokens[b] = prefix_shared_tokens(d, b);
+}
+
+// Group wave L (XCD-aware as in decode_multi_kernel): items =
+// (group * K + kvh) * prefix_parts + partition, d.col_groups waves each.
+// prefix_parts: partitions per member row, ceil(max shared span / P), with
+// d.part = P.  q_lds: kTiles * (H / 32) * 64 16-byte slots of LDS.
+// store_spans: waves L < ceil(B / 64) store S_b of sequences 64 L + lane.
+template <class Fmt, int H, int kTiles>
+__device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int prefix_parts, int L,
+                                                  u32x4 *q_lds, bool store_spans)
+{
+    if (store_spans && (int64_t)L * kWave < d.num_seqs) {
         const int b = L * kWave + (int)threadIdx.x;
         if (b < d.num_seqs)
             d.shared_tokens[b] = prefix_shared_tokens(d, b);
@@ -51,11 +58,11 @@ void decode_prefix_kernel(PrefixParams p)
     const int j = L / kXcds;
     const int cg = j % d.col_groups;
     const int64_t item = (int64_t)(j / d.col_groups) * kXcds + xcd;
-    if (item >= (int64_t)d.num_groups * d.num_kv_heads * p.prefix_parts)
+    if (item >= (int64_t)d.num_groups * d.num_kv_heads * prefix_parts)
         return;
-    const int part_idx = (int)(item % p.prefix_parts);
-    const int kvh = (int)((item / p.prefix_parts) % d.num_kv_heads);
-    const int grp = (int)(item / ((int64_t)p.prefix_parts * d.num_kv_heads));
+    const int part_idx = (int)(item % prefix_parts);
+    const int kvh = (int)((item / prefix_parts) % d.num_kv_heads);
+    const int grp = (int)(item / ((int64_t)prefix_parts * d.num_kv_heads));
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int quad = lane >> 4;
@@ -102,12 +109,11 @@ void decode_prefix_kernel(PrefixParams p)
         short_col |= live[t] && own < end;
         const int gh = c - m * G;
         qrow[t] = (int64_t)(live[t] ? mb : lead) * d.num_heads + kvh * G + gh;
-        prow[t] = (((int64_t)(live[t] ? mb : 0) * d.num_kv_heads + kvh) * p.prefix_parts +
+        prow[t] = (((int64_t)(live[t] ? mb : 0) * d.num_kv_heads + kvh) * prefix_parts +
                    part_idx) * G + gh;
     }
     const bool mask = __builtin_amdgcn_ballot_w64(short_col) != 0;
 
-    __shared__ u32x4 q_lds[kTiles * (H / 32) * kWave];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const uint16_t *qr = d.q + qrow[t] * H;

@@ -313,13 +313,30 @@ int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int3
     return launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
 }
 
+// Token-balanced kernel of the shared-prefix path for a head dim and the
+// group waves' tiles (0: no group waves in the grid; else 1 to 4).
+template <class Fmt, int H>
+const void *balanced_prefix_kernel(int tiles)
+{
+    switch (tiles) {
+    case 0: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 0>;
+    case 1: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 1>;
+    case 2: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 2>;
+    case 3: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 3>;
+    default: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 4>;
+    }
+}
+
 // Token-balanced decode: schedule (large batches), persistent decode, merge
 // of the split segments.  kPrefix: segments start after the positions each
 // sequence's prefix group reads (its prefix_parts partials per row are in
-// p.part_o / p.part_ml), and the merge joins those partials.
+// p.part_o / p.part_ml), and the merge joins those partials; group_waves
+// waves of group_tiles tiles that compute them follow the persistent ones
+// in the grid.
 template <class Fmt, bool kPrefix>
 int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_kv_heads,
-                    const BalancedLayout &L, char *ws, int64_t prefix_parts, void *stream)
+                    const BalancedLayout &L, char *ws, int64_t prefix_parts, void *stream,
+                    int group_tiles = 0, int64_t group_waves = 0)
 {
     int log2_waves = 0;
     int rc = device_waves(&log2_waves);
@@ -345,10 +362,14 @@ int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_
         if (rc != PKV_OK)
             return rc;
     }
-    const void *dk = head_dim == 128
-                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, kPrefix>
-                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, kPrefix>;
-    rc = launch(dk, dim3((unsigned)waves), dim3(pkv::kWave), &bp, stream);
+    const void *dk;
+    if constexpr (kPrefix)
+        dk = head_dim == 128 ? balanced_prefix_kernel<Fmt, 128>(group_tiles)
+                             : balanced_prefix_kernel<Fmt, 64>(group_tiles);
+    else
+        dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, false>
+                             : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, false>;
+    rc = launch(dk, dim3((unsigned)(waves + group_waves)), dim3(pkv::kWave), &bp, stream);
     if (rc != PKV_OK)
         return rc;
     const void *mk = merge_pieces_for<kPrefix>(head_dim, p.group);
@@ -494,7 +515,7 @@ const void *multi_kernel(int tiles, bool split)
     }
 }
 
-// Tiles per wave of the shared-prefix group kernel: the fewest (most waves,
+// Tiles per wave of the shared-prefix group waves: the fewest (most waves,
 // shortest kernel) that still fit one wave per SIMD of the chip (wave_slots);
 // the waves that split an item's columns re-read its blocks from their XCD's
 // L2.
@@ -506,17 +527,7 @@ int prefix_tiles_per_wave(int64_t items, int tiles, int64_t wave_slots)
     return tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
 }
 
-// Shared-prefix group kernel for a head dim and tiles per wave (1 to 4).
-template <class Fmt, int H>
-const void *prefix_kernel(int tiles)
-{
-    switch (tiles) {
-    case 1: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 1>;
-    case 2: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 2>;
-    case 3: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 3>;
-    default: return (const void *)pkv::decode_prefix_kernel<Fmt, H, 4>;
-    }
-}
+
 
 template <class Fmt>
 int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_queries,
@@ -567,9 +578,11 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     return launch_merge(mp, head_dim, num_kv_heads, (int64_t)num_seqs * num_queries, stream);
 }
 
-// Prefix-aware decode: the group kernel reads every shared span once (its
-// partitions' partials per member), the token-balanced waves the rest of
-// every context, and their merge joins the two.
+// Prefix-aware decode: one grid of the token-balanced waves (the rest of
+// every context) followed by the group waves (every shared span once, its
+// partitions' partials per member), then the merge that joins the two.  For
+// more sequences than the waves scan themselves, a spans kernel first stores
+// every S_b, which the schedule and the per-sequence waves read.
 template <class Fmt>
 int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_t num_heads,
                          int32_t num_kv_heads, int32_t max_context_len, int32_t max_prefix_tokens,
@@ -591,10 +604,13 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
     // No shared span outgrows the partials the workspace holds (a group whose
     // prefix_tokens exceeds the stated bound shares only this much).
     p.max_prefix = (int32_t)(prefix_parts * p.part);
-    p.shared_tokens = nullptr;      // no group kernel: nothing is shared
+    p.shared_tokens = nullptr;      // no group: nothing is shared
 
-    // The group kernel first: its partials must be complete when the merge
-    // of the per-sequence pieces (same stream, later) reads them.
+    // The group waves' partials (and, for small batches, the spans they
+    // store) are complete when the merge, a later kernel on the same stream,
+    // reads them.
+    int group_tiles = 0;
+    int64_t group_waves = 0;
     if (prefix_parts > 0 && p.num_groups > 0) {
         const int tiles = (int)ceil_div((int64_t)p.max_members * (num_heads / num_kv_heads), 16);
         const int64_t items = (int64_t)p.num_groups * num_kv_heads * prefix_parts;
@@ -602,26 +618,26 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
         int rc = device_waves(&log2_waves);
         if (rc != PKV_OK)
             return rc;
-        const int per_wave = prefix_tiles_per_wave(items, tiles, (int64_t)1 << log2_waves);
-        p.shared_tokens = reinterpret_cast<int32_t *>(ws + L.shared);
-        pkv::PrefixParams pp;
-        pp.d = p;
-        pp.d.col_groups = (int32_t)ceil_div(tiles, per_wave);
-        pp.prefix_parts = (int32_t)prefix_parts;
-        // At least one wave per 64 sequences: those store the shared spans.
-        int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * pp.d.col_groups;
-        if (waves < ceil_div(num_seqs, pkv::kWave))
-            waves = ceil_div(num_seqs, pkv::kWave);
-        if (waves > INT32_MAX)
+        group_tiles = prefix_tiles_per_wave(items, tiles, (int64_t)1 << log2_waves);
+        p.col_groups = (int32_t)ceil_div(tiles, group_tiles);
+        group_waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * p.col_groups;
+        // Small batches: at least one group wave per 64 sequences stores the spans.
+        const bool inline_spans = num_seqs <= pkv::kInlineScheduleSeqs;
+        if (inline_spans && group_waves < ceil_div(num_seqs, pkv::kWave))
+            group_waves = ceil_div(num_seqs, pkv::kWave);
+        if (group_waves > INT32_MAX - ((int64_t)1 << log2_waves))
             return PKV_ERR_SHAPE;
-        const void *gk = head_dim == 128 ? prefix_kernel<Fmt, 128>(per_wave)
-                                         : prefix_kernel<Fmt, 64>(per_wave);
-        rc = launch(gk, dim3((unsigned)waves), dim3(pkv::kWave), &pp, stream);
-        if (rc != PKV_OK)
-            return rc;
+        p.shared_tokens = reinterpret_cast<int32_t *>(ws + L.shared);
+        if (!inline_spans) {
+            rc = launch((const void *)pkv::prefix_spans_kernel,
+                        dim3((unsigned)ceil_div(num_seqs, pkv::kWave)), dim3(pkv::kWave), &p,
+                        stream);
+            if (rc != PKV_OK)
+                return rc;
+        }
     }
     return balanced_launch<Fmt, true>(p, head_dim, num_seqs, num_kv_heads, L.bal, ws,
-                                      prefix_parts, stream);
+                                      prefix_parts, stream, group_tiles, group_waves);
 }
 
 }  // namespace
