@@ -173,7 +173,7 @@ def main() -> int:
                          "(default: the workload's own, else 0)")
     ap.add_argument("--mode", choices=["plain", "prefix"], default="plain",
                     help="prefix: read each shared prefix once for its sharers "
-                         "(--partition: its pieces, default 256; workloads with shared "
+                         "(--partition: its pieces, default 128; workloads with shared "
                          "prefixes)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend each sequence's last W positions (0 = all)")
@@ -261,7 +261,7 @@ def main() -> int:
                   file=sys.stderr)
             return 2
         if part == 0:
-            part = 256
+            part = 128
         seq_group = torch.full((s.B,), -1, dtype=torch.int32)
         seq_group[w.sharer_ids] = 0
         members = torch.tensor([w.sharer_ids], dtype=torch.int32)

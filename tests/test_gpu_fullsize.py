@@ -76,14 +76,16 @@ def test_full_size(name):
     H.assert_parity(out.numpy()[rb, rn], ref, f"{name} sampled rows")
 
 
+@pytest.mark.parametrize("piece", [128, 256])
 @pytest.mark.parametrize("name", ["llama3_70b_ragged_b100", "llama3_70b_ragged_b100_fp8"])
-def test_full_size_shared_prefix(name):
+def test_full_size_shared_prefix(name, piece):
     """The ragged mix through the shared-prefix call as the benchmark's
     prefix mode runs it (its 20 sharers' 62 shared blocks read once, in
-    256-token pieces): sampled rows -- the first and last sharer among them --
-    against the oracle, every row against plain decode of the same pools."""
+    128-token pieces; also 256): sampled rows -- the first and last sharer
+    among them -- against the oracle, every row against plain decode of the
+    same pools."""
     import paged_kv_cache_100_amd as pkv
-    H.log(f"case {name} shared prefix (full size)")
+    H.log(f"case {name} shared prefix (full size), {piece}-token pieces")
     with H.Timer("generate"):
         w = W.make(name)
     s = w.spec
@@ -97,7 +99,7 @@ def test_full_size_shared_prefix(name):
     got = torch.full((s.B, s.N, s.H), float("nan"), dtype=torch.float32, device=dev)
     with H.Timer("gpu prefix decode"):
         pkv.paged_decode_attention_prefix(got, g.q, g.key_cache, g.value_cache, g.block_tables,
-                                          g.context_lens, w.scale, s.K, s.bs, 256,
+                                          g.context_lens, w.scale, s.K, s.bs, piece,
                                           seq_group.to(dev), members.to(dev), tokens.to(dev),
                                           max_prefix_tokens=shared, k_scale=w.k_scale,
                                           v_scale=w.v_scale, max_context_len=w.max_context_len)
