@@ -743,9 +743,7 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     for (int i0 = 0; i0 < total; i0 += kBatch) {
         float mv[kBatch], lv[kBatch];
         f32x4 ov[kBatch][kVals / 4];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = min(i0 + u, total - 1);
+        auto load_input = [&](int u, int i) {
             const bool pre = kPrefix && i < n_pre;
             const int64_t r = row_of(i);
             const float *mlp = pre ? d.part_ml : p.piece_ml;
@@ -755,6 +753,24 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 #pragma unroll
             for (int v = 0; v < kVals / 4; ++v)
                 ov[u][v] = *reinterpret_cast<const f32x4 *>(op + r * H + h0 + 4 * v);
+        };
+        // A full batch loads straight through; the last, partial one loads
+        // only its live inputs (most segments have two or three pieces).
+        if (i0 + kBatch <= total) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                load_input(u, i0 + u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                mv[u] = -INFINITY;
+                lv[u] = 0.f;
+#pragma unroll
+                for (int v = 0; v < kVals / 4; ++v)
+                    ov[u][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i0 + u < total)
+                    load_input(u, i0 + u);
+            }
         }
         bool use[kBatch];
         float nb = big;
