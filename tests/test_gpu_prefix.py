@@ -174,6 +174,27 @@ def test_span_ends_inside_a_partition(partition):
     run_prefix(w, groups, partition, f"spans, part {partition}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_nothing_shared_below_one_chunk(kv):
+    # every group's prefix under one 32-token chunk: no span, no group waves,
+    # and the result is plain decode's
+    spec = W.Spec("nochunk", B=6, N=32, K=8, H=128, ctx=[300, 200, 90, 45, 33, 120], seed=163,
+                  kv_dtype=kv)
+    w = W.make(spec)
+    groups = repoint(w, [(0, [1, 2, 3], 2), (4, [5], 2)])   # 32 positions mapped alike
+    groups = [(groups[0][0], 20), (groups[1][0], 31)]
+    run_prefix(w, groups, 64, f"prefixes under a chunk {kv}")
+
+
+def test_group_with_an_empty_span_beside_a_shared_one():
+    # group 0's lead holds 20 tokens, so its span is empty and its waves find
+    # nothing to read; group 1 shares 160 positions
+    spec = W.Spec("emptyspan", B=6, N=32, K=8, H=128, ctx=[20, 300, 45, 500, 400, 161], seed=167)
+    w = W.make(spec)
+    groups = repoint(w, [(0, [1, 2], 1), (3, [4, 5], 10)])
+    run_prefix(w, groups, 64, "empty span beside a shared one")
+
+
 def test_large_batch():
     # more than 256 sequences: the schedule kernel's table, with shared
     # partitions skipped
