@@ -35,8 +35,12 @@ constexpr int kMaxQueryTiles = 4;   // Q * G <= 64
 constexpr int kTilesPerWave = 4;
 constexpr int kXcds = 8;            // MI355X: workgroups are dealt to 8 XCDs in turn
 
-// Chunk buffers per wave for kTiles tiles (spill-free on gfx950): bf16 4, 3,
-// 3, 2; FP8 5, 4, 3, 2.
+// Chunk buffers per wave for kTiles tiles: bf16 4, 3, 3, 2; FP8 5, 4, 3, 2.
+// These fit gfx950's 256 vector registers without spilling only because the
+// per-column output rows are recomputed after the chunk loop and, from four
+// tiles on, FP8 value codes are widened anew for every tile
+// (KvFp8::value_fresh): holding the widened values of all eight value tiles
+// across the tile loop takes 32 more registers than the kernel has.
 template <class Fmt, int kTiles>
 constexpr int multi_ring_depth()
 {
@@ -112,7 +116,7 @@ __device__ __forceinline__ void attend_chunk_multi(typename Fmt::template Regs<H
         }
 #pragma unroll
         for (int c = 0; c < H / 16; ++c) {
-            const bf16x8 vv = as_bf16x8(Fmt::value(r, c));
+            const bf16x8 vv = as_bf16x8(kTiles >= 4 ? Fmt::value_fresh(r, c) : Fmt::value(r, c));
             acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_hi, acc[t][c], 0, 0, 0);
             acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, p_lo, acc[t][c], 0, 0, 0);
         }
@@ -149,18 +153,28 @@ void decode_multi_kernel(DecodeParams p)
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
 
     // Column t of this lane: query token i, head g; its output row in
-    // [B][Q][N] and the positions it sees.
+    // [B][Q][N] and the positions it sees.  The rows are recomputed where
+    // they are used (from an index the compiler cannot see through), so
+    // that they hold no registers across the chunk loop.
+    auto out_row = [&](int t, int lane_id) -> int64_t {
+        const int c = 16 * (kTiles * cg + t) + (lane_id & 15);
+        const bool lv = c < Q * G;
+        const int i = lv ? c / G : 0;
+        const int g = lv ? c - i * G : 0;
+        return ((int64_t)b * Q + i) * p.num_heads + kvh * G + g;
+    };
+    auto opaque_lane = [&]() {
+        int v = lane;
+        asm volatile("" : "+v"(v));
+        return v;
+    };
     bool live[kTiles];
     int lim[kTiles];
-    int64_t orow[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const int c = 16 * (kTiles * cg + t) + col;
         live[t] = c < Q * G;
-        const int i = live[t] ? c / G : 0;
-        const int g = live[t] ? c - (c / G) * G : 0;
-        orow[t] = ((int64_t)b * Q + i) * p.num_heads + kvh * G + g;
-        lim[t] = live[t] ? ctx - Q + i + 1 : ctx;
+        lim[t] = live[t] ? ctx - Q + c / G + 1 : ctx;
     }
 
     if (start >= ctx) {
@@ -169,7 +183,7 @@ void decode_multi_kernel(DecodeParams p)
             for (int t = 0; t < kTiles; ++t) {
                 if (!live[t])
                     continue;
-                float *o = p.out + orow[t] * H;
+                float *o = p.out + out_row(t, lane) * H;
 #pragma unroll
                 for (int c = 0; c < H / 16; ++c)
                     *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -186,7 +200,7 @@ void decode_multi_kernel(DecodeParams p)
     __shared__ u32x4 q_lds[kTiles * (H / 32) * kWave];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-        const uint16_t *qrow = p.q + orow[t] * H;
+        const uint16_t *qrow = p.q + out_row(t, lane) * H;
 #pragma unroll
         for (int s = 0; s < H / 32; ++s) {
             u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
@@ -258,12 +272,12 @@ void decode_multi_kernel(DecodeParams p)
             continue;
         if (!kSplit) {
             const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
-            float *o = p.out + orow[t] * H;
+            float *o = p.out + out_row(t, opaque_lane()) * H;
 #pragma unroll
             for (int c = 0; c < H / 16; ++c)
                 *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * inv;
         } else {
-            const int64_t slot = orow[t] * p.num_parts + part_idx;
+            const int64_t slot = out_row(t, opaque_lane()) * p.num_parts + part_idx;
             float *o = p.part_o + slot * H;
 #pragma unroll
             for (int c = 0; c < H / 16; ++c)

@@ -89,11 +89,15 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
     const int n_blocks = (end - start) / kBlockSize;
 
     // Column t of this lane: member m, head g; lim: the end of the member's
-    // shared positions (a multiple of the chunk).
-    bool live[kTiles];
+    // shared positions (a multiple of the chunk).  Only the member's sequence
+    // (-1 for a column with nothing to attend) stays live across the chunk
+    // loop; the head within the group is recomputed where it is needed.
+    auto head_of = [&](int t, int lane_id) {
+        const int c = 16 * (kTiles * cg + t) + (lane_id & 15);
+        return c - (c / G) * G;
+    };
+    int mcol[kTiles];
     int lim[kTiles];
-    int64_t qrow[kTiles];
-    int64_t prow[kTiles];
     bool short_col = false;
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
@@ -104,23 +108,22 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
         const int own =
             in_group ? shared_span(d, prefix, min(max(d.context_lens[mb], 0), d.max_ctx), ctx_lead)
                      : 0;
-        live[t] = own > start;
-        lim[t] = live[t] ? min(own, end) : end;
-        short_col |= live[t] && own < end;
-        const int gh = c - m * G;
-        qrow[t] = (int64_t)(live[t] ? mb : lead) * d.num_heads + kvh * G + gh;
-        prow[t] = (((int64_t)(live[t] ? mb : 0) * d.num_kv_heads + kvh) * prefix_parts +
-                   part_idx) * G + gh;
+        const bool live = own > start;
+        mcol[t] = live ? mb : -1;
+        lim[t] = live ? min(own, end) : end;
+        short_col |= live && own < end;
     }
     const bool mask = __builtin_amdgcn_ballot_w64(short_col) != 0;
 
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
-        const uint16_t *qr = d.q + qrow[t] * H;
+        const int64_t qrow =
+            (int64_t)(mcol[t] >= 0 ? mcol[t] : lead) * d.num_heads + kvh * G + head_of(t, lane);
+        const uint16_t *qr = d.q + qrow * H;
 #pragma unroll
         for (int s = 0; s < H / 32; ++s) {
             u32x4 raw = load16(qr + Fmt::dim_offset(s, quad));
-            if (!live[t])
+            if (mcol[t] < 0)
                 raw = u32x4{0u, 0u, 0u, 0u};
             q_lds[(t * (H / 32) + s) * kWave + lane] = raw;
         }
@@ -167,18 +170,23 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
     Regs ring[kRing];
     run_ring<kRing>((end - start) / kChunk, ring, issue, attend);
 
+    int opaque = lane;
+    asm volatile("" : "+v"(opaque));
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const float lt = sum_over_rows(l[t]);
-        if (!live[t])
+        if (mcol[t] < 0)
             continue;
-        float *o = d.part_o + prow[t] * H;
+        const int64_t prow =
+            (((int64_t)mcol[t] * d.num_kv_heads + kvh) * prefix_parts + part_idx) * G +
+            head_of(t, opaque);
+        float *o = d.part_o + prow * H;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
             *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * d.out_scale;
         if (quad == 0) {
-            d.part_ml[2 * prow[t]] = m[t];
-            d.part_ml[2 * prow[t] + 1] = lt;
+            d.part_ml[2 * prow] = m[t];
+            d.part_ml[2 * prow + 1] = lt;
         }
     }
 }

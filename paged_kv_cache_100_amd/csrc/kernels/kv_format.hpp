@@ -84,6 +84,13 @@ struct KvBf16 {
     {
         return r.v[c];
     }
+    // value() for a kernel that consumes the operand in several places: the
+    // loaded bits need no widening, so it is value() itself.
+    template <int H>
+    __device__ static __forceinline__ u32x4 value_fresh(const Regs<H> &r, int c)
+    {
+        return r.v[c];
+    }
     // Zeroes the lane's value elements from token `valid` (0..8) on, in place.
     template <int H>
     __device__ static __forceinline__ void zero_values(Regs<H> &r, int valid)
@@ -169,6 +176,16 @@ struct KvFp8 {
     __device__ static __forceinline__ u32x4 value(const Regs<H> &r, int c)
     {
         return __builtin_bit_cast(u32x4, widen8(r.v[c][0], r.v[c][1]));
+    }
+    // value() widened anew at each call: the compiler cannot reuse the widened
+    // operand of an earlier call, so a kernel that takes the same value tile
+    // for several query tiles keeps 8 widened registers live instead of 32.
+    template <int H>
+    __device__ static __forceinline__ u32x4 value_fresh(const Regs<H> &r, int c)
+    {
+        u32x2 w = r.v[c];
+        asm volatile("" : "+v"(w));
+        return __builtin_bit_cast(u32x4, widen8(w[0], w[1]));
     }
     // Zeroes the lane's value codes from token `valid` (0..8) on, in place
     // (code 0 is +0).

@@ -48,17 +48,25 @@ LAYOUTS = [  # (Q, N, K): Q * N / K (query, head) pairs per KV head
     (8, 32, 8),    # 32: two full tiles
     (6, 64, 8),    # 48: three tiles
     (7, 64, 8),    # 56: four tiles, the last half used
+    (8, 64, 8),    # 64: four full tiles (G = 8)
     (12, 40, 8),   # 60 (G = 5): four tiles
     (16, 32, 8),   # 64: four full tiles
     (4, 16, 1),    # MQA: 64
 ]
 
 
+@pytest.mark.parametrize("partition", [64, 1024])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
 @pytest.mark.parametrize("Hd", [64, 128])
 @pytest.mark.parametrize("Q,N,K", LAYOUTS, ids=[f"q{q}n{n}k{k}" for q, n, k in LAYOUTS])
-def test_column_layouts(Q, N, K, Hd):
-    spec = W.Spec("layouts", B=3, N=N, K=K, H=Hd, ctx=[300, 47, 129], queries=Q, seed=51)
-    run_case(spec, 64, f"Q={Q} N={N} K={K} H={Hd}")
+def test_column_layouts(Q, N, K, Hd, kv, partition):
+    """Every tile count (one to four) in both pool formats, with several
+    partitions per sequence (64 tokens: partials and the merge) and with one
+    partition covering every context (1,024 tokens: the wave writes the
+    output)."""
+    spec = W.Spec("layouts", B=3, N=N, K=K, H=Hd, ctx=[300, 47, 129], queries=Q, seed=51,
+                  kv_dtype=kv)
+    run_case(spec, partition, f"Q={Q} N={N} K={K} H={Hd} {kv} part {partition}")
 
 
 EDGE_CTX = [0, 1, 2, 4, 5, 6, 31, 32, 33, 36, 37, 63, 64, 65, 511, 512, 513]
