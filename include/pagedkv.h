@@ -368,10 +368,15 @@ int paged_decode_attention_prefix(float *out, const void *q,
 
 /*
  * pagedkv_stream_read -- measurement helper, not part of the method: reads
- * `bytes` (a multiple of 16) from `src` with 16-byte loads and writes one
- * 16-byte value per workgroup into `sink` ([gridDim] x 16 bytes; the size is
- * returned by pagedkv_stream_read_sink_bytes).  Used to calibrate HBM byte
- * counters and the achievable read bandwidth against the decode kernel.
+ * `bytes` (a multiple of 16, 16-byte aligned) from `src` in the decode
+ * kernels' access pattern -- one wave per SIMD, each reading a contiguous
+ * share with non-temporal 16-byte loads, 16 KiB per step, two steps in
+ * flight -- and may write one 16-byte value per wave into `sink` (at most
+ * 4,096 waves; pagedkv_stream_read_sink_bytes returns the size to
+ * allocate).  The rate it reaches is the achievable-bandwidth ceiling the
+ * decode kernels are compared with; a launch of known size also calibrates
+ * HBM read counters.  Returns PKV_ERR_NULL / _SHAPE / _ALIGN / _DEVICE /
+ * _LAUNCH as the other calls do.
  */
 size_t pagedkv_stream_read_sink_bytes(size_t bytes);
 int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream);

@@ -1042,13 +1042,8 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *src_
 
 size_t pagedkv_stream_read_sink_bytes(size_t bytes)
 {
-    const int64_t n16 = (int64_t)(bytes / 16);
-    int64_t blocks = ceil_div(n16, pkv::kStreamThreads * 4);
-    if (blocks > pkv::kStreamBlocksMax)
-        blocks = pkv::kStreamBlocksMax;
-    if (blocks < 1)
-        blocks = 1;
-    return (size_t)blocks * 16;
+    (void)bytes;
+    return (size_t)pkv::kMaxBalancedWaves * 16;    // one slot per wave, any device
 }
 
 int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream)
@@ -1061,16 +1056,19 @@ int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream)
         return PKV_ERR_SHAPE;
     if (!aligned16(src) || !aligned16(sink))
         return PKV_ERR_ALIGN;
+    int log2_waves = 0;
+    const int rc = device_waves(&log2_waves);     // one wave per SIMD, as the decode runs
+    if (rc != PKV_OK)
+        return rc;
     const int64_t n16 = (int64_t)(bytes / 16);
-    const unsigned blocks = (unsigned)(pagedkv_stream_read_sink_bytes(bytes) / 16);
     struct {
         const pkv::u32x4 *src;
         int64_t n16;
         pkv::u32x4 *sink;
     } a = {static_cast<const pkv::u32x4 *>(src), n16, static_cast<pkv::u32x4 *>(sink)};
     void *args[] = {&a.src, &a.n16, &a.sink};
-    hipError_t err = hipLaunchKernel((const void *)pkv::stream_read_kernel, dim3(blocks),
-                                     dim3(pkv::kStreamThreads), args, 0,
+    hipError_t err = hipLaunchKernel((const void *)pkv::stream_read_kernel,
+                                     dim3(1u << log2_waves), dim3(pkv::kWave), args, 0,
                                      reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
