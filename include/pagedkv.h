@@ -31,7 +31,8 @@
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer (HIP global memory) unless
  *     stated otherwise.  The caller owns all memory; the library allocates
- *     nothing and keeps no state except a per-device attribute cache.
+ *     nothing and keeps no state except a per-device attribute cache (and
+ *     the static scratch array of paged_decode_attention_noalloc).
  *   - bf16 data is passed as raw 16-bit patterns (type-erased `void*`).
  *   - `stream` is a hipStream_t passed as `void*` (NULL = the null stream).
  *     Calls only enqueue work on that stream; they never synchronise, so
@@ -70,7 +71,9 @@ typedef enum pkv_status {
     PKV_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                   */
     PKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required         */
     PKV_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch                 */
-    PKV_ERR_DEVICE = -7       /* no HIP device / device query failed                */
+    PKV_ERR_DEVICE = -7,      /* no HIP device / device query failed                */
+    PKV_ERR_SCRATCH = -8      /* paged_decode_attention_noalloc: the problem needs
+                                 more than PKV_NOALLOC_SCRATCH_BYTES of scratch     */
 } pkv_status;
 
 /* Supported shapes (compile-time kernel variants). */
@@ -388,6 +391,39 @@ int pagedkv_stream_read(const void *src, size_t bytes, void *sink, void *stream)
  * known number of bytes, for scaling HBM read/write counters.
  */
 int pagedkv_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+/*
+ * paged_decode_attention_noalloc -- paged_decode_attention without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It allocates nothing (no hipMalloc, hipFree or allocating
+ * library call): the scratch that paged_decode_attention keeps in the
+ * caller's workspace (split partials, the token-balanced schedule and its
+ * pieces) lives in a static device array of PKV_NOALLOC_SCRATCH_BYTES that
+ * every device the library runs on holds from first use until the process
+ * ends.
+ *
+ * Arguments, layouts, results and checks are those of paged_decode_attention
+ * (same kernels, bit-identical output).  PKV_ERR_SCRATCH: the shape needs
+ * more scratch than the array holds, i.e. paged_decode_workspace_size(...)
+ * > PKV_NOALLOC_SCRATCH_BYTES (64 MiB covers, e.g., 2,048 sequences of 32
+ * query and 8 KV heads at head_dim 128 in the token-balanced mode, or 4
+ * sequences of 64 heads at 131,072 tokens in 512-token partitions).
+ * Nothing in the array needs clearing between calls (every value is written
+ * before it is read).  All calls on one device share its array: calls that
+ * can overlap on one device (on different streams, or from several host
+ * threads without ordering) race and give undefined results; calls ordered
+ * on one stream are safe.  PKV_ERR_DEVICE if the array's device address
+ * cannot be obtained.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_decode_attention_noalloc(float *out, const void *q, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, float scale,
+                                   int32_t num_kv_heads, int32_t block_size, int32_t num_seqs,
+                                   int32_t num_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   int64_t num_blocks, int32_t partition_size, void *stream);
 
 /* Human-readable name of a pkv_status value (static string, never NULL). */
 const char *pagedkv_status_string(int status);

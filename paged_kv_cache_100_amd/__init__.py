@@ -21,6 +21,8 @@ computation runs in the library's HIP kernels.  The library must be built
     paged_kv_copy_blocks(key_cache, value_cache, src_blocks, dst_blocks)
     paged_decode_attention_window(out, q, key_cache, value_cache, block_tables,
                                   context_lens, scale, num_kv_heads, block_size, window)
+    paged_decode_attention_noalloc(out, q, key_cache, value_cache, block_tables,
+                                   context_lens, scale, num_kv_heads, block_size)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
 [num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
@@ -41,7 +43,8 @@ LIB_PATH = os.path.join(_PKG, "libpagedkv.so")
 
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_UNSUPPORTED",
           -4: "PKV_ERR_ALIGN", -5: "PKV_ERR_WORKSPACE", -6: "PKV_ERR_LAUNCH",
-          -7: "PKV_ERR_DEVICE"}
+          -7: "PKV_ERR_DEVICE", -8: "PKV_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20     # PKV_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -70,6 +73,9 @@ def lib() -> ctypes.CDLL:
     L.paged_decode_attention.argtypes = [P, P, P, P, P, P, f32, i32, i32, i32, i32, i32, i32,
                                          i32, i64, i32, P, sz, P]
     L.paged_decode_attention.restype = ctypes.c_int
+    L.paged_decode_attention_noalloc.argtypes = [P, P, P, P, P, P, f32, i32, i32, i32, i32, i32,
+                                                 i32, i32, i64, i32, P]
+    L.paged_decode_attention_noalloc.restype = ctypes.c_int
     L.paged_kv_append_fp8.argtypes = [P, P, P, P, P, f32, f32, i32, i32, i32, i32, i64, P]
     L.paged_kv_append_fp8.restype = ctypes.c_int
     L.paged_decode_attention_fp8.argtypes = [P, P, P, P, P, P, f32, f32, f32, i32, i32, i32, i32,
@@ -178,7 +184,8 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
 
 
 def _decode_args(out, q, key_cache, value_cache, block_tables, context_lens, num_kv_heads,
-                 block_size, max_context_len, partition, workspace, cache_dtype):
+                 block_size, max_context_len, partition, workspace, cache_dtype,
+                 allocate=True):
     po = _dev(out, "out", torch.float32)
     pq = _dev(q, "q", torch.bfloat16)
     pkc = _dev(key_cache, "key_cache", cache_dtype)
@@ -198,7 +205,7 @@ def _decode_args(out, q, key_cache, value_cache, block_tables, context_lens, num
     max_blocks = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = max_blocks * block_size
-    need = workspace_size(B, N, K, H, max_context_len, partition) if B else 0
+    need = workspace_size(B, N, K, H, max_context_len, partition) if B and allocate else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     pw, wbytes = 0, 0
@@ -229,6 +236,23 @@ def paged_decode_attention(out: torch.Tensor, q: torch.Tensor, key_cache: torch.
                               num_kv_heads, block_size, max_context_len, partition, workspace,
                               torch.bfloat16)
     _check(lib().paged_decode_attention(*head, float(scale), *tail), "paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_noalloc(out: torch.Tensor, q: torch.Tensor, key_cache: torch.Tensor,
+                                   value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   context_lens: torch.Tensor, scale: float, num_kv_heads: int,
+                                   block_size: int, max_context_len: Optional[int] = None,
+                                   partition: int = 0) -> torch.Tensor:
+    """``paged_decode_attention`` with no workspace: the library's static
+    per-device scratch array serves instead, so neither the library nor this
+    wrapper allocates device memory (for graph capture and callers that
+    cannot allocate).  Calls that may overlap on one device race."""
+    head, tail = _decode_args(out, q, key_cache, value_cache, block_tables, context_lens,
+                              num_kv_heads, block_size, max_context_len, partition, None,
+                              torch.bfloat16, allocate=False)
+    _check(lib().paged_decode_attention_noalloc(*head, float(scale), *tail[:-3], tail[-1]),
+           "paged_decode_attention_noalloc")
     return out
 
 

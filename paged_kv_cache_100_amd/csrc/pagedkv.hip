@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <atomic>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "kernels/append.hpp"
@@ -377,14 +378,14 @@ int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_
                   stream);
 }
 
-template <class Fmt>
-int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
-                const int32_t *block_tables, const int32_t *context_lens, float scale,
-                float k_scale, float v_scale, int32_t window, int32_t num_kv_heads,
-                int32_t block_size,
-                int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
-                int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream)
+// Host-side checks of the single-query decode calls, in the order the
+// statuses are documented (no device is touched).
+int check_decode(float *out, const void *q, const void *key_cache, const void *value_cache,
+                 const int32_t *block_tables, const int32_t *context_lens, float scale,
+                 float k_scale, int32_t window, int32_t num_kv_heads, int32_t block_size,
+                 int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                 int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                 int32_t partition_size)
 {
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         max_context_len < 0 || num_blocks < 0 || window < 0)
@@ -420,6 +421,24 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
         (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
         (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return PKV_ERR_ALIGN;
+    return PKV_OK;
+}
+
+template <class Fmt>
+int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
+                const int32_t *block_tables, const int32_t *context_lens, float scale,
+                float k_scale, float v_scale, int32_t window, int32_t num_kv_heads,
+                int32_t block_size,
+                int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                int32_t partition_size, void *workspace, size_t workspace_bytes, void *stream)
+{
+    const int rc0 = check_decode(out, q, key_cache, value_cache, block_tables, context_lens,
+                                 scale, k_scale, window, num_kv_heads, block_size, num_seqs,
+                                 num_heads, head_dim, max_blocks_per_seq, max_context_len,
+                                 num_blocks, partition_size);
+    if (rc0 != PKV_OK || num_seqs == 0)
+        return rc0;
 
     pkv::DecodeParams p;
     p.out = out;
@@ -640,6 +659,35 @@ int decode_prefix_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, i
                                       prefix_parts, stream, group_tiles, group_waves);
 }
 
+// Scratch of the allocation-free entry point (paged_decode_attention_noalloc):
+// a static device array, so every device the library runs on holds its own
+// copy of PKV_NOALLOC_SCRATCH_BYTES until the process ends.  On the host,
+// `scratch` names a host-side stand-in, not device memory: host code uses
+// only the device address hipGetSymbolAddress returns for it (per device).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_address[kMaxDevices];   // per device, set on the first call there
+
+// Device address of the current device's scratch array (looked up once per
+// device, with that device current).
+int device_scratch(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return PKV_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_address[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return PKV_ERR_DEVICE;
+        scratch_address[dev] = p;
+    }
+    *ptr = scratch_address[dev];
+    return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -657,6 +705,9 @@ const char *pagedkv_status_string(int status)
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_DEVICE: return "no usable HIP device";
+    case PKV_ERR_SCRATCH:
+        return "problem needs more scratch than the allocation-free call holds "
+               "(PKV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -751,6 +802,40 @@ int paged_decode_attention(float *out, const void *q, const void *key_cache,
                                     num_heads, head_dim, max_blocks_per_seq, max_context_len,
                                     num_blocks, partition_size, workspace, workspace_bytes,
                                     stream);
+}
+
+int paged_decode_attention_noalloc(float *out, const void *q, const void *key_cache,
+                                   const void *value_cache, const int32_t *block_tables,
+                                   const int32_t *context_lens, float scale,
+                                   int32_t num_kv_heads, int32_t block_size, int32_t num_seqs,
+                                   int32_t num_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len,
+                                   int64_t num_blocks, int32_t partition_size, void *stream)
+{
+    int rc = check_decode(out, q, key_cache, value_cache, block_tables, context_lens, scale,
+                          1.0f, 0, num_kv_heads, block_size, num_seqs, num_heads, head_dim,
+                          max_blocks_per_seq, max_context_len, num_blocks, partition_size);
+    if (rc != PKV_OK || num_seqs == 0)
+        return rc;
+    // The workspace paged_decode_attention would need for this shape.
+    const size_t need =
+        partition_size == 0
+            ? balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim).total
+            : fixed_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len,
+                                    partition_size);
+    if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+        return PKV_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need > 0) {
+        rc = device_scratch(&ws);
+        if (rc != PKV_OK)
+            return rc;
+    }
+    return decode_impl<pkv::KvBf16>(out, q, key_cache, value_cache, block_tables, context_lens,
+                                    scale, 1.0f, 1.0f, 0, num_kv_heads, block_size, num_seqs,
+                                    num_heads, head_dim, max_blocks_per_seq, max_context_len,
+                                    num_blocks, partition_size, ws,
+                                    need > 0 ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int paged_decode_attention_fp8(float *out, const void *q, const void *key_cache,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(L):
             "paged_decode_attention_mq", "paged_decode_mq_workspace_size",
             "paged_decode_attention_prefix", "paged_decode_prefix_workspace_size",
             "paged_kv_copy_blocks",
-            "paged_decode_attention_window",
+            "paged_decode_attention_window", "paged_decode_attention_noalloc",
             "pagedkv_status_string", "pagedkv_version",
             "pagedkv_stream_read", "pagedkv_stream_read_sink_bytes",
             "pagedkv_stream_copy"} <= set(names)
@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert pkv.status_string(code)
     assert pkv.status_string(-99) == "unknown status"
     assert pkv.version() == "1.6"
@@ -263,3 +263,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pkv, "LIB_PATH", str(tmp_path / "libpagedkv.so"))
     with pytest.raises(RuntimeError, match="missing"):
         pkv.lib()
+
+
+def noalloc(L, out=A, q=A, kc=A, vc=A, bt=A, cl=A, scale=0.125, K=2, bs=16, B=4, N=8, H=64,
+            maxblk=16, maxctx=256, nb=128, part=0):
+    return L.paged_decode_attention_noalloc(out, q, kc, vc, bt, cl, scale, K, bs, B, N, H,
+                                            maxblk, maxctx, nb, part, None)
+
+
+def test_noalloc_checks(L):
+    """The allocation-free call makes paged_decode_attention's checks first,
+    then refuses shapes whose scratch exceeds its static array -- all on the
+    host, before the device is touched."""
+    assert noalloc(L, B=0) == OK
+    assert noalloc(L, out=0) == NULL
+    assert noalloc(L, K=0) == SHAPE
+    assert noalloc(L, N=6, K=4) == SHAPE
+    assert noalloc(L, H=96) == UNSUP
+    assert noalloc(L, bs=32) == UNSUP
+    assert noalloc(L, part=48) == SHAPE
+    assert noalloc(L, q=MIS) == ALIGN
+    # 65,535 sequences of 64 heads, token-balanced: far more than 64 MiB of pieces.
+    assert noalloc(L, B=65535, N=64, K=8, H=128, maxblk=512, maxctx=8192, nb=1 << 20) == -8
+    need = L.paged_decode_workspace_size(65535, 64, 8, 128, 8192, 0)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    # Fixed 32-token partitions of a 131,072-token context for 64 sequences of 64 heads.
+    assert noalloc(L, B=64, N=64, K=8, H=128, maxblk=8192, maxctx=131072, nb=1 << 20,
+                   part=32) == -8

@@ -1,0 +1,64 @@
+"""The allocation-free decode call, paged_decode_attention_noalloc, through
+the C ABI: its scratch is the library's static per-device array instead of a
+caller workspace, and its kernels are paged_decode_attention's, so its output
+must equal paged_decode_attention's bit for bit (and the oracle's within the
+parity bar).  Two calls in a row, the second on a smaller input, in the
+token-balanced mode and with fixed partitions: the second call reuses the
+array the first one filled."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_100_amd as pkv
+from paged_kv_cache_100_amd import workloads as W
+
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def run_pair(w, partition):
+    g = w.to(DEV)
+    H.gpu_append(g, w)
+    s = w.spec
+    mcl = w.max_context_len
+    ref = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    got = torch.full(g.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    ws = pkv.workspace_size(s.B, s.N, s.K, s.H, mcl, partition)
+    assert ws <= pkv.NOALLOC_SCRATCH_BYTES
+    pkv.paged_decode_attention(ref, g.q, g.key_cache, g.value_cache, g.block_tables,
+                               g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
+                               partition=partition)
+    pkv.paged_decode_attention_noalloc(got, g.q, g.key_cache, g.value_cache, g.block_tables,
+                                       g.context_lens, w.scale, s.K, s.bs, max_context_len=mcl,
+                                       partition=partition)
+    torch.cuda.synchronize()
+    return got.cpu(), ref.cpu()
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+def test_two_calls_match_workspace_call(partition):
+    big = W.small("llama3_70b_ragged_b100")
+    small = W.Spec("noalloc small", B=5, N=32, K=8, H=128, ctx=[1, 300, 47, 0, 129], seed=71)
+    for spec in (big, small):
+        w = W.make(spec)
+        H.log(f"case noalloc {spec.name} B={spec.B} partition={partition} "
+              f"ctx={w.context_lens.tolist()[:8]}")
+        got, ref = run_pair(w, partition)
+        assert torch.equal(got, ref), "differs from paged_decode_attention"
+        oref, _ = H.oracle_step(w)
+        H.assert_parity(got.numpy(), oref, f"noalloc {spec.name} part {partition}")
+
+
+def test_too_large_is_refused_before_any_launch():
+    # 65,535 sequences of 64 query heads need far more than the array holds;
+    # the host check refuses them (nothing is launched, the pointers are
+    # never read).
+    L = pkv.lib()
+    A = 0x10000
+    rc = L.paged_decode_attention_noalloc(A, A, A, A, A, A, 0.125, 8, 16, 65535, 64, 128, 512,
+                                          8192, 1 << 20, 0, None)
+    assert rc == -8
+    assert "scratch" in pkv.status_string(rc)
