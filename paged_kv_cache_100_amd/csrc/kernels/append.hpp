@@ -8,9 +8,12 @@
 //
 // One thread moves 8 consecutive head-dim values (16 bytes) of one (token,
 // KV head): a single 16-byte store for the key row, and eight 2-byte stores
-// down the value tile's columns (value tiles are stored transposed, [H][16]).
-// The step moves at most a few hundred KiB, so the strided value stores cost
-// nothing measurable next to the attention that follows.
+// down the value tile's columns (value tiles are stored transposed, [H][16]),
+// so a token dirties every 128-byte line of its value tile (32 at H = 128).
+// The decode that follows reads those lines more slowly the more of them the
+// append wrote (its key rows, two lines per token, cost next to nothing);
+// writing the value elements with non-temporal stores sends them toward
+// memory at once and takes part of that cost off the decode.
 #pragma once
 
 #include "common.hpp"
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint32_t word = vv[e >> 1];
-        dst[e * kBlockSize] = (uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+        __builtin_nontemporal_store((uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu)),
+                                    dst + e * kBlockSize);
     }
 }
 
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params p)
     uint8_t *dst = p.value_cache + (tile * H + 8 * c) * kBlockSize + off;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        dst[e * kBlockSize] = (uint8_t)(vq[e >> 2] >> (8 * (e & 3)));
+        __builtin_nontemporal_store((uint8_t)(vq[e >> 2] >> (8 * (e & 3))), dst + e * kBlockSize);
 }
 
 }  // namespace pkv
