@@ -145,6 +145,8 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
 // The balanced schedule uses the largest power of two not above that, so
 // that wave boundaries need no division.
 constexpr int kWavesPerCU = 4;
+constexpr int64_t kMinChunksPerWave = 4;
+constexpr int64_t kPiecesPerMergeBatch = 8;   // merge_pieces_kernel's batch at H = 128
 
 int device_waves(int *log2_waves)
 {
@@ -343,6 +345,20 @@ int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_
     int rc = device_waves(&log2_waves);
     if (rc != PKV_OK)
         return rc;
+    // Small problems: fewer waves when every wave would get fewer than
+    // kMinChunksPerWave chunks (on the bound of T from the host-known
+    // context bound) and the segments would average more pieces than one
+    // merge batch reads (a batch of one 1,024-token sequence of 40 heads
+    // otherwise gives each of 1,024 waves about one chunk and every segment
+    // some 26 pieces to merge).
+    int64_t seg_chunks_bound = ceil_div(p.max_ctx, pkv::kChunk);
+    if (p.window > 0 && ceil_div(p.window, pkv::kChunk) + 1 < seg_chunks_bound)
+        seg_chunks_bound = ceil_div(p.window, pkv::kChunk) + 1;
+    const int64_t segments = (int64_t)num_seqs * num_kv_heads;
+    const int64_t t_bound = segments * seg_chunks_bound;
+    while (log2_waves > 0 && ((int64_t)1 << log2_waves) * kMinChunksPerWave > t_bound &&
+           ((int64_t)1 << log2_waves) > kPiecesPerMergeBatch * segments)
+        --log2_waves;
     const int waves = 1 << log2_waves;
     pkv::BalancedParams bp;
     bp.d = p;

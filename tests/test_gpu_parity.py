@@ -117,21 +117,33 @@ def resident_waves():
 
 @pytest.mark.parametrize("delta", [-1, 0, 2], ids=["below", "equal", "above"])
 def test_chunk_count_around_the_wave_count(delta):
-    # one sequence over eight KV heads: T = 8 * chunks 32-token chunks against
-    # W waves.  Below W every wave holds at most one chunk and the merge finds
-    # each piece by its chunk; from W on every wave holds at least one and the
-    # pieces are consecutive waves.
-    chunks = resident_waves() // 8 + delta
-    spec = W.Spec("around", B=1, N=32, K=8, H=128, ctx=[32 * chunks - 5], seed=151)
+    # T = 8 * (total chunks) 32-token chunks against W waves, one sequence
+    # longer or shorter than the rest.  Below W every wave holds at most one
+    # chunk and the merge finds each piece by its chunk; from W on every wave
+    # holds at least one and the pieces are consecutive waves.  With 8 * 16 =
+    # 128 segments the library keeps all W waves (it only trims the wave
+    # count when it exceeds eight pieces per segment).
+    W_ = resident_waves()
+    per = W_ // 128                            # chunks per sequence for T = W
+    ctx = [32 * per - 5] * 15 + [32 * (per + delta) - 5]
+    spec = W.Spec("around", B=16, N=32, K=8, H=128, ctx=ctx, seed=151)
     run_case(spec, partition=0, what=f"T = W {delta * 8:+d}")
 
 
 def test_several_chunk_segments_with_fewer_chunks_than_waves():
-    # T = 8 * (10 + 1 + 22 + 3) = 288 chunks, far below the wave count: the
-    # longer segments are split into one-chunk pieces in waves that lie
-    # between empty ones
-    spec = W.Spec("sparse", B=4, N=32, K=8, H=128, ctx=[300, 1, 700, 70], seed=157)
+    # T = 8 * (10 + 1 + 22 + 3 + 1 + 1 + 2 + 1) = 328 chunks, below the 512 or
+    # more waves the library keeps for 64 segments: the longer segments are
+    # split into one-chunk pieces in waves that lie between empty ones
+    spec = W.Spec("sparse", B=8, N=32, K=8, H=128, ctx=[300, 1, 700, 70, 1, 1, 33, 5],
+                  seed=157)
     run_case(spec, partition=0, what="sparse pieces")
+
+
+def test_small_problem_uses_fewer_waves():
+    # One 1,024-token sequence over 40 KV heads: the library trims the wave
+    # count (several chunks per wave, few pieces per segment)
+    spec = W.Spec("trimmed", B=1, N=40, K=40, H=128, ctx=[1024], seed=159)
+    run_case(spec, partition=0, what="trimmed wave count")
 
 
 @pytest.mark.parametrize("partition", [0, 64])
