@@ -50,6 +50,12 @@ namespace pkv {
 
 constexpr int kScheduleThreads = 1024;
 constexpr int kMaxBalancedWaves = 4096;
+// Waves per workgroup of the decode kernel, at most: a workgroup of four
+// fills a CU (one wave per SIMD).  Dispatching 256 four-wave workgroups
+// starts the last wave several microseconds sooner than 1,024 one-wave
+// workgroups.  Grids of fewer waves than the chip holds use smaller
+// workgroups (blockDim.x / 64 waves), which spreads them over more CUs.
+constexpr int kGroupWaves = 4;
 
 struct BalancedParams {
     DecodeParams d;               // shapes, pointers, scale (part: kFixed partitions or
@@ -234,8 +240,8 @@ constexpr uint32_t kStagePiece = 2;     // a piece: piece_o / piece_ml row
 constexpr uint32_t kStagePartial = 3;   // a fixed partition: part_o / part_ml row
 
 // LDS a decode wave stages finished pieces in (eight pieces of a group of 8
-// at H = 128): with the per-column records 37 KiB per wave, so four waves
-// per CU fit in its 160 KiB.
+// at H = 128): with the per-column records 37 KiB per wave, so a workgroup
+// of four waves (one CU) takes 148 KiB of its 160 KiB.
 constexpr int kStageBytes = 32 * 1024;
 constexpr int kStageMax = 16;      // pieces staged at most
 
@@ -260,26 +266,33 @@ struct BalancedBuf {
 // shared spans for the merge, which the persistent waves compute for
 // themselves.
 template <class Fmt, int H, bool kFixed = false, bool kPrefix = false, int kGroupTiles = 0>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kWave * kGroupWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
     using Elem = typename Fmt::Elem;
     using Buf = BalancedBuf<Fmt, H>;
     const DecodeParams &d = p.d;
-    __shared__ f32x4 stage_o[kStageBytes / 16];    // staged pieces (see below)
+    // Wave wv of the grid is wave wig of workgroup blockIdx.x; the waves of a
+    // workgroup share nothing but the CU (each has its own LDS slice).
+    // (read from the first lane: the compiler must see the wave index as
+    // uniform, or everything derived from it leaves the scalar unit)
+    const int wig = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wv = (int)blockIdx.x * ((int)blockDim.x / kWave) + wig;
+    const int lane = (int)threadIdx.x % kWave;
+    __shared__ f32x4 stage_all[kGroupWaves][kStageBytes / 16];   // staged pieces (see below)
+    f32x4 *stage_o = stage_all[wig];
     if constexpr (kGroupTiles > 0) {
         static_assert(kPrefix && kGroupTiles * (H / 32) * kWave * 16 <= kStageBytes,
                       "group queries fit the stage");
-        if ((int)blockIdx.x >= p.num_waves) {
-            prefix_group_wave<Fmt, H, kGroupTiles>(d, p.prefix_parts,
-                                                   (int)blockIdx.x - p.num_waves,
+        if (wv >= p.num_waves) {
+            prefix_group_wave<Fmt, H, kGroupTiles>(d, p.prefix_parts, wv - p.num_waves,
                                                    reinterpret_cast<u32x4 *>(stage_o),
                                                    p.inline_schedule != 0);
             return;
         }
     }
-    const int wv = blockIdx.x;
-    const int lane = threadIdx.x;
+    if (wv >= p.num_waves)           // the last workgroup's spare waves
+        return;
     const int col = lane & 15;
     const int quad = lane >> 4;
     const int K = d.num_kv_heads;
@@ -519,10 +532,14 @@ void decode_balanced_kernel(BalancedParams p)
     // of order), which stalls the wave for a full memory latency.
     // Only the G live columns are kept: a piece takes G * H * 4 bytes, so
     // the stage holds more pieces for smaller groups (up to kStageMax).
-    __shared__ int64_t stage_row[kStageMax][16];   // destination row of each column
-    __shared__ float stage_m[kStageMax][16];
-    __shared__ float stage_l[kStageMax][16];
-    __shared__ uint32_t stage_kind[kStageMax][16];
+    __shared__ int64_t stage_row_all[kGroupWaves][kStageMax][16];   // destination row of each column
+    __shared__ float stage_m_all[kGroupWaves][kStageMax][16];
+    __shared__ float stage_l_all[kGroupWaves][kStageMax][16];
+    __shared__ uint32_t stage_kind_all[kGroupWaves][kStageMax][16];
+    auto &stage_row = stage_row_all[wig];
+    auto &stage_m = stage_m_all[wig];
+    auto &stage_l = stage_l_all[wig];
+    auto &stage_kind = stage_kind_all[wig];
     const int G = d.group;
     const int slot_vecs = G * H / 4;                // f32x4 per staged piece
     const int cap = min(kStageMax, (kStageBytes / 16) / slot_vecs);

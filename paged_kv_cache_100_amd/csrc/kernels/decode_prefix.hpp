@@ -49,8 +49,9 @@ template <class Fmt, int H, int kTiles>
 __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int prefix_parts, int L,
                                                   u32x4 *q_lds, bool store_spans)
 {
+    const int lane = (int)threadIdx.x % kWave;
     if (store_spans && (int64_t)L * kWave < d.num_seqs) {
-        const int b = L * kWave + (int)threadIdx.x;
+        const int b = L * kWave + lane;
         if (b < d.num_seqs)
             d.shared_tokens[b] = prefix_shared_tokens(d, b);
     }
@@ -63,7 +64,6 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
     const int part_idx = (int)(item % prefix_parts);
     const int kvh = (int)((item / prefix_parts) % d.num_kv_heads);
     const int grp = (int)(item / ((int64_t)prefix_parts * d.num_kv_heads));
-    const int lane = threadIdx.x;
     const int col = lane & 15;
     const int quad = lane >> 4;
     const int G = d.group;

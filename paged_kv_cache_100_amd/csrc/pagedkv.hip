@@ -313,7 +313,8 @@ int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int3
     const void *dk = head_dim == 128
                          ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, false>
                          : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, false>;
-    return launch(dk, dim3((unsigned)bp.num_waves), dim3(pkv::kWave), &bp, stream);
+    return launch(dk, dim3((unsigned)ceil_div(bp.num_waves, pkv::kGroupWaves)),
+                  dim3(pkv::kWave * pkv::kGroupWaves), &bp, stream);   // the full chip
 }
 
 // Token-balanced kernel of the shared-prefix path for a head dim and the
@@ -386,7 +387,17 @@ int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_
     else
         dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, false>
                              : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, false>;
-    rc = launch(dk, dim3((unsigned)(waves + group_waves)), dim3(pkv::kWave), &bp, stream);
+    // Four-wave workgroups for a full chip of waves; a trimmed grid (small
+    // problems) takes one or two waves per workgroup, so it spreads over the
+    // CUs instead of filling a quarter or half of them.
+    int device_lg = 0;
+    rc = device_waves(&device_lg);
+    if (rc != PKV_OK)
+        return rc;
+    const int per_group = log2_waves >= device_lg ? pkv::kGroupWaves
+                          : log2_waves == device_lg - 1 ? 2 : 1;
+    rc = launch(dk, dim3((unsigned)ceil_div(waves + group_waves, per_group)),
+                dim3(pkv::kWave * per_group), &bp, stream);
     if (rc != PKV_OK)
         return rc;
     const void *mk = merge_pieces_for<kPrefix>(head_dim, p.group);
