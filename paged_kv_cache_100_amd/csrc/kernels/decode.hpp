@@ -134,6 +134,38 @@ __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
     return (id >= 0 && (int64_t)id < num_blocks) ? id : 0;
 }
 
+// The two block ids of one 32-token chunk, as loaded.  Both go out together
+// through the scalar unit, and the kernels clamp and use them only when the
+// chunk's K/V loads are issued, a whole chunk of work later: a use right
+// after the load would stall the wave for the table's round trip.  A chunk
+// of one block loads its first id twice, so the second address stays inside
+// the sequence's blocks.
+struct ChunkIds {
+    int raw0, raw1;
+};
+__device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t *row, int jj, int nblk)
+{
+    const int e = 2 * jj;   // e < nblk
+    return ChunkIds{scalar_load(row + e), scalar_load(row + min(e + 1, nblk - 1))};
+}
+
+// clamp_block's bound as an unsigned 32-bit value: ids are int32, so
+// min(num_blocks, 2^31) admits exactly the same ids, and a negative id, seen
+// unsigned, is at least 2^31.
+__device__ __forceinline__ uint32_t id_bound(int64_t num_blocks)
+{
+    return (uint32_t)min(max(num_blocks, (int64_t)0), (int64_t)1 << 31);
+}
+
+// Element offset of the block with id `raw` (block 0 if raw is outside
+// [0, num_blocks)) in a pool of block_elems = K * 16 * H elements per block.
+// The host keeps K * 16 * H below 2^31, so one 32 x 32-bit product serves.
+__device__ __forceinline__ uint64_t block_offset(int raw, uint32_t bound, uint32_t block_elems)
+{
+    const uint32_t id = (uint32_t)raw < bound ? (uint32_t)raw : 0u;
+    return ((uint64_t)__umulhi(id, block_elems) << 32) | (id * block_elems);
+}
+
 // `qf(s)` yields the lane's query operand for k-step s (from registers or LDS).
 // kTail: a chunk with masked positions -- those at or past `rem` (the end of
 // the context: their values are zeroed too) and those before `head` (the

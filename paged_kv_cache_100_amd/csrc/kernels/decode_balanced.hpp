@@ -250,6 +250,8 @@ constexpr int kStageMax = 16;      // pieces staged at most
 // positions 32 * (fc + j) .. (fc counts the chunks before the sliding window).
 struct Pos {
     int b, kvh, j, nc, ctx, fc;
+    const int32_t *row;   // sequence b's block-table row
+    int nblk;             // its blocks: ceil(ctx / 16)
 };
 
 // One ring slot: the chunk's key/value operands, plus the group's query
@@ -429,6 +431,8 @@ void decode_balanced_kernel(BalancedParams p)
     start.kvh = uniform(st.y);
     start.j = uniform(st.z);
     start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
+    start.row = d.block_tables + (int64_t)start.b * d.max_blocks;
+    start.nblk = (start.ctx + kBlockSize - 1) / kBlockSize;
     if constexpr (kPrefix) {
         start.nc = nc_at(start.b, start.ctx);
         start.fc = fc_at(start.b, start.ctx);
@@ -468,6 +472,8 @@ void decode_balanced_kernel(BalancedParams p)
         const int2 nx = next_seq(q.b);
         q.b = nx.x;
         q.ctx = nx.y;
+        q.row = d.block_tables + (int64_t)q.b * d.max_blocks;
+        q.nblk = (q.ctx + kBlockSize - 1) / kBlockSize;
         if constexpr (kPrefix) {
             q.nc = nc_at(q.b, q.ctx);
             q.fc = fc_at(q.b, q.ctx);
@@ -477,27 +483,23 @@ void decode_balanced_kernel(BalancedParams p)
         }
     };
 
-    const int64_t tile_elems = (int64_t)kBlockSize * H;
-    const int64_t block_elems = (int64_t)K * tile_elems;
+    constexpr uint32_t tile_elems = kBlockSize * H;
+    const uint32_t block_elems = (uint32_t)K * tile_elems;   // < 2^31 (K <= 65535)
+    const uint32_t id_lim = id_bound(d.num_blocks);
+    const Elem *kcache = static_cast<const Elem *>(d.key_cache);
+    const Elem *vcache = static_cast<const Elem *>(d.value_cache);
 
-    // ---- issue side: its own cursor; each chunk's two block ids come from
-    // scalar loads made one chunk ahead ----
+    // ---- issue side: its own cursor; each chunk's two block ids are loaded
+    // one chunk ahead (load_chunk_ids) ----
     Pos ip = start;
-    int id0 = 0, id1 = 0;
-    auto load_ids = [&](const Pos &q) {
-        const int jj = q.fc + q.j;    // chunk index within the sequence
-        const int32_t *row = d.block_tables + (int64_t)q.b * d.max_blocks + 2 * jj;
-        const int nblk = (q.ctx + kBlockSize - 1) / kBlockSize;
-        id0 = clamp_block(scalar_load(row), d.num_blocks);
-        id1 = 2 * jj + 1 < nblk ? clamp_block(scalar_load(row + 1), d.num_blocks) : id0;
-    };
-    load_ids(ip);
+    ChunkIds ids = load_chunk_ids(ip.row, ip.fc + ip.j, ip.nblk);
     auto issue = [&](Buf &r, int k) {
-        // ip is chunk k; (id0, id1) are its blocks
-        const Elem *kb = static_cast<const Elem *>(d.key_cache) + ip.kvh * tile_elems;
-        const Elem *vb = static_cast<const Elem *>(d.value_cache) + ip.kvh * tile_elems;
-        Fmt::template load<H>(r.kv, kb + id0 * block_elems, kb + id1 * block_elems,
-                              vb + id0 * block_elems, vb + id1 * block_elems, col, quad);
+        // ip is chunk k; ids are its blocks
+        const uint64_t head_off = (uint32_t)ip.kvh * tile_elems;
+        const uint64_t o0 = head_off + block_offset(ids.raw0, id_lim, block_elems);
+        const uint64_t o1 = head_off + block_offset(ids.raw1, id_lim, block_elems);
+        Fmt::template load<H>(r.kv, kcache + o0, kcache + o1, vcache + o0, vcache + o1, col,
+                              quad);
         if (k == 0 || ip.j == 0) {    // the chunk opens a segment: bring its queries
             // Columns past the group repeat its last query; their results are
             // never stored.
@@ -509,7 +511,7 @@ void decode_balanced_kernel(BalancedParams p)
         }
         if (k + 1 < total) {          // step to chunk k + 1 and fetch its block ids
             next_pos(ip);
-            load_ids(ip);
+            ids = load_chunk_ids(ip.row, ip.fc + ip.j, ip.nblk);
         }
     };
 

@@ -210,27 +210,23 @@ void decode_multi_kernel(DecodeParams p)
         }
     }
 
-    const int64_t tile_elems = (int64_t)kBlockSize * H;
-    const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
+    constexpr uint32_t tile_elems = kBlockSize * H;
+    const uint32_t block_elems = (uint32_t)p.num_kv_heads * tile_elems;   // < 2^31
+    const uint32_t id_lim = id_bound(p.num_blocks);
     using Elem = typename Fmt::Elem;
     using Regs = typename Fmt::template Regs<H>;
-    const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
-    const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
+    const Elem *kbase = static_cast<const Elem *>(p.key_cache) + (uint64_t)kvh * tile_elems;
+    const Elem *vbase = static_cast<const Elem *>(p.value_cache) + (uint64_t)kvh * tile_elems;
 
-    // A chunk's two block ids come from scalar loads made one chunk ahead,
-    // so a partition may span any number of blocks.
-    int id0 = 0, id1 = 0;
-    auto load_ids = [&](int ci) {
-        id0 = clamp_block(scalar_load(table + 2 * ci), p.num_blocks);
-        id1 = 2 * ci + 1 < n_blocks ? clamp_block(scalar_load(table + 2 * ci + 1), p.num_blocks)
-                                    : id0;
-    };
-    load_ids(0);
+    // A chunk's two block ids are loaded one chunk ahead (load_chunk_ids), so
+    // a partition may span any number of blocks.
+    ChunkIds ids = load_chunk_ids(table, 0, n_blocks);
     auto issue = [&](Regs &r, int ci) {
-        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
-                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+        const uint64_t o0 = block_offset(ids.raw0, id_lim, block_elems);
+        const uint64_t o1 = block_offset(ids.raw1, id_lim, block_elems);
+        Fmt::template load<H>(r, kbase + o0, kbase + o1, vbase + o0, vbase + o1, col, quad);
         if (ci + 1 < n_chunks)
-            load_ids(ci + 1);
+            ids = load_chunk_ids(table, ci + 1, n_blocks);
     };
 
     float m[kTiles], l[kTiles];
