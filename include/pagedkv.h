@@ -255,10 +255,20 @@ int paged_decode_attention_fp8(float *out, const void *q,
  *   workspace      at least paged_decode_mq_workspace_size(num_seqs,
  *                  num_queries, num_heads, head_dim, max_context_len,
  *                  partition_size) bytes (0 when one partition covers
- *                  max_context_len), 16-byte aligned.
+ *                  max_context_len), 16-byte aligned.  Its contents on entry
+ *                  do not matter; calls sharing one workspace must not run
+ *                  concurrently.
  * Other arguments, checks and clamping as for paged_decode_attention.  The
  * Q * G (query token, head) pairs of a KV head's group share each load of
- * its keys and values.
+ * its keys and values.  Several partitions are merged with the log-sum-exp
+ * rule by a second launch, except when max_context_len spans exactly two
+ * partitions and a wave holds at most three column tiles: then of the two
+ * partition waves of a (sequence, KV head), the one that finishes second
+ * merges both partials itself (one launch).  It finds out through an atomic
+ * exchange of a per-call 64-bit tag in the workspace (a process-wide
+ * counter from a random start), so the workspace needs no clearing; the
+ * merge takes the partitions in order with the merge launch's arithmetic, so
+ * the result is the same whichever wave merges.
  */
 size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
                                       int32_t head_dim, int32_t max_context_len,

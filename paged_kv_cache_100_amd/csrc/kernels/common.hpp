@@ -31,6 +31,24 @@ __device__ __forceinline__ void store16(void *p, u32x4 v) { *reinterpret_cast<u3
 typedef __attribute__((address_space(4))) const int32_t const_i32;
 __device__ __forceinline__ int32_t scalar_load(const int32_t *p) { return *(const const_i32 *)p; }
 
+// Device-coherent 32-bit accesses (agent-scope relaxed atomics: written
+// through to, and read from, the level every XCD shares) for data one wave
+// hands to a wave of another XCD inside one launch.
+__device__ __forceinline__ void store_coherent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float *p, f32x4 v)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        store_coherent(p + e, v[e]);
+}
+__device__ __forceinline__ float load_coherent(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Lane-pair reductions across the four 16-lane rows with VALU permutes
 // (no LDS round trip): max / sum of v over lanes l, l^16, l^32, l^48.
 __device__ __forceinline__ float max_over_rows(float v)

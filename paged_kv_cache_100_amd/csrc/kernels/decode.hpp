@@ -87,6 +87,11 @@ struct DecodeParams {
                                   // workspace holds partials for)
     int32_t *shared_tokens;       // [B]: S_b, written by the group kernel; null = none
     int32_t window;               // sliding window: attend the last `window` positions; 0 = all
+    // Multi-query calls of exactly two partitions: per (sequence, KV head)
+    // tags through which the two partition waves find which of them finishes
+    // second (that one merges both partials); null = merge_parts_kernel merges.
+    uint64_t *pair_tags = nullptr;
+    uint64_t epoch = 0;           // this call's tag value (never 0)
 };
 
 // First position a sequence of ctx tokens attends (sliding window), else 0.

@@ -32,6 +32,8 @@
 namespace pkv {
 
 constexpr int kMaxQueryTiles = 4;   // Q * G <= 64
+constexpr int kBufferFlags = 0x00020000;   // word 3 of a raw buffer resource (gfx9)
+constexpr int kCoherentAux = 16;           // cache policy: system-coherence bit (sc1)
 constexpr int kTilesPerWave = 4;
 constexpr int kXcds = 8;            // MI355X: workgroups are dealt to 8 XCDs in turn
 
@@ -177,8 +179,13 @@ void decode_multi_kernel(DecodeParams p)
         lim[t] = live[t] ? ctx - Q + c / G + 1 : ctx;
     }
 
+    // Two partitions merged in this kernel: a sequence whose context fits the
+    // first partition is finished by that partition's wave alone.
+    // (Four tiles keep the merge kernel: their registers leave no room for it.)
+    constexpr bool kPairMerge = kSplit && kTiles < kMaxQueryTiles;
+    const bool pair = kPairMerge && p.pair_tags != nullptr;
     if (start >= ctx) {
-        if (!kSplit && part_idx == 0) {   // empty sequence: zeros
+        if ((!kSplit || pair) && part_idx == 0) {   // empty sequence: zeros
 #pragma unroll
             for (int t = 0; t < kTiles; ++t) {
                 if (!live[t])
@@ -261,18 +268,35 @@ void decode_multi_kernel(DecodeParams p)
     Regs ring[kRing];
     run_ring<kRing>(n_chunks, ring, issue, attend);
 
+    const bool single = !kSplit || (pair && ctx <= p.part);   // this wave finishes its rows
+    // Pair partials of this sequence: a buffer over its Q * N rows of two
+    // partitions, so that 16-byte accesses can carry the coherence bit.
+    const int64_t pair_base = (int64_t)b * Q * p.num_heads * 2 * H;   // in floats
+    const __amdgpu_buffer_rsrc_t pair_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        p.part_o + (pair ? pair_base : 0), 0, Q * p.num_heads * 2 * H * 4, kBufferFlags);
+    float lts[kTiles];
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
         const float lt = sum_over_rows(l[t]);
+        lts[t] = lt;
         if (!live[t])
             continue;
-        if (!kSplit) {
+        if (single && !pair) {
             const float inv = lt > 0.f ? p.out_scale / lt : 0.f;
             float *o = p.out + out_row(t, opaque_lane()) * H;
 #pragma unroll
             for (int c = 0; c < H / 16; ++c)
                 *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[t][c] * inv;
-        } else {
+        } else if (single) {
+            // One partition of a two-partition call: the merge's arithmetic on
+            // a single partial (weight 1), so that the result is the one the
+            // merge kernel would give.
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            float *o = p.out + out_row(t, opaque_lane()) * H;
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = (acc[t][c] * p.out_scale) * inv;
+        } else if (!pair) {
             const int64_t slot = out_row(t, opaque_lane()) * p.num_parts + part_idx;
             float *o = p.part_o + slot * H;
 #pragma unroll
@@ -282,6 +306,82 @@ void decode_multi_kernel(DecodeParams p)
                 p.part_ml[2 * slot] = m[t];
                 p.part_ml[2 * slot + 1] = lt;
             }
+        } else {
+            // Read by the other partition's wave, possibly on another XCD:
+            // device-coherent 16-byte stores (system-coherence bit).
+            const int64_t slot = out_row(t, opaque_lane()) * 2 + part_idx;
+            const int off = (int)((slot * H - pair_base) * 4);
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, acc[t][c] * p.out_scale), pair_rsrc,
+                    off + (16 * c + 4 * quad) * 4, 0, kCoherentAux);
+            if (quad == 0) {
+                store_coherent(p.part_ml + 2 * slot, m[t]);
+                store_coherent(p.part_ml + 2 * slot + 1, lt);
+            }
+        }
+    }
+    if constexpr (!kPairMerge)
+        return;
+    if (!pair || single)
+        return;
+    // Two partitions: once this wave's partial is stored, it swaps the call's
+    // tag into the (sequence, KV head) slot.  Finding the tag already there
+    // means the other wave's partial is stored: this wave merges both, in
+    // partition order with merge_parts_kernel's arithmetic (so the result
+    // does not depend on which wave merges), reading the other partial with
+    // device-coherent loads.  Nothing waits on the other wave, and the tags
+    // need no clearing: every call brings a new value.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint64_t seen = 0;
+    if (lane == 0)
+        seen = __hip_atomic_exchange(p.pair_tags + ((int64_t)b * p.num_kv_heads + kvh) *
+                                                       p.col_groups + cg, p.epoch,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)seen);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(seen >> 32));
+    if ((((uint64_t)hi << 32) | lo) != p.epoch)
+        return;                           // first to finish: the other wave merges
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+        if (!live[t])
+            continue;
+        const int64_t row = out_row(t, opaque_lane());
+        const int64_t other = row * 2 + (1 - part_idx);
+        const float mo = load_coherent(p.part_ml + 2 * other);
+        const float lo_ = load_coherent(p.part_ml + 2 * other + 1);
+        f32x4 oo[H / 16];
+        const int ooff = (int)((other * H - pair_base) * 4);
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c)
+            oo[c] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           pair_rsrc, ooff + (16 * c + 4 * quad) * 4, 0, kCoherentAux));
+        // partition 0 first, as merge_parts_kernel takes them
+        const bool own_first = part_idx == 0;
+        const float m0 = own_first ? m[t] : mo, m1 = own_first ? mo : m[t];
+        const float l0 = own_first ? lts[t] : lo_, l1 = own_first ? lo_ : lts[t];
+        float nb = -INFINITY;
+        const bool u0 = m0 > -INFINITY, u1 = m1 > -INFINITY;
+        nb = u0 ? fmaxf(nb, m0) : nb;
+        nb = u1 ? fmaxf(nb, m1) : nb;
+        const float w0 = u0 ? __builtin_amdgcn_exp2f(m0 - nb) : 0.f;
+        const float w1 = u1 ? __builtin_amdgcn_exp2f(m1 - nb) : 0.f;
+        float den = 0.f;
+        den += u0 ? w0 * l0 : 0.f;
+        den += u1 ? w1 * l1 : 0.f;
+        const float inv = den > 0.f ? 1.0f / den : 0.f;
+        float *o = p.out + row * H;
+#pragma unroll
+        for (int c = 0; c < H / 16; ++c) {
+            const f32x4 own = acc[t][c] * p.out_scale;
+            const f32x4 o0 = own_first ? own : oo[c], o1 = own_first ? oo[c] : own;
+            f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+            num += u0 ? w0 * o0 : f32x4{0.f, 0.f, 0.f, 0.f};
+            num += u1 ? w1 * o1 : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = num * inv;
         }
     }
 }

@@ -7,6 +7,7 @@
 #include <stdint.h>
 #include <atomic>
 #include <mutex>
+#include <random>
 
 #include "pagedkv.h"
 #include "kernels/append.hpp"
@@ -75,6 +76,46 @@ size_t partials_bytes(int32_t num_rows, int32_t num_heads, int32_t head_dim, int
         return 0;
     const int64_t rows = (int64_t)num_rows * num_heads * parts;
     return align256((size_t)(rows * head_dim * 4)) + (size_t)(rows * 2 * 4);
+}
+
+// The multi-query call's workspace: the partials, and for exactly two
+// partitions per context the pair tags after them (one per (sequence, KV
+// head) pair of partition waves; sized by num_seqs * num_heads, a bound of
+// num_seqs * K * column groups).
+size_t mq_pair_tags_offset(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                           int32_t head_dim, int32_t max_ctx, int32_t part)
+{
+    const int64_t rows = (int64_t)num_seqs * num_queries;
+    return align256(partials_bytes((int32_t)(rows > INT32_MAX ? INT32_MAX : rows), num_heads,
+                                   head_dim, max_ctx, part));
+}
+
+size_t mq_workspace_bytes(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
+                          int32_t head_dim, int32_t max_ctx, int32_t part)
+{
+    const size_t base = mq_pair_tags_offset(num_seqs, num_queries, num_heads, head_dim, max_ctx,
+                                            part);
+    if (ceil_div(max_ctx, part) != 2)
+        return partials_bytes((int32_t)((int64_t)num_seqs * num_queries > INT32_MAX
+                                             ? INT32_MAX
+                                             : (int64_t)num_seqs * num_queries),
+                              num_heads, head_dim, max_ctx, part);
+    return base + align256((size_t)num_seqs * num_heads * 8);
+}
+
+// A fresh tag value per two-partition multi-query call: a process-wide
+// counter from a random start, never 0.
+uint64_t next_pair_epoch()
+{
+    static std::atomic<uint64_t> counter{[] {
+        std::random_device rd;
+        return ((uint64_t)rd() << 32) ^ (uint64_t)rd();
+    }()};
+    uint64_t e;
+    do
+        e = counter.fetch_add(1, std::memory_order_relaxed);
+    while (e == 0);
+    return e;
 }
 
 // Token-balanced mode: the layout of its workspace, sized for the largest
@@ -584,8 +625,8 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     const int64_t parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
     const bool split = parts > 1;
     if (split) {
-        const size_t need = partials_bytes(num_seqs * num_queries, num_heads, head_dim,
-                                                  max_context_len, part);
+        const size_t need = mq_workspace_bytes(num_seqs, num_queries, num_heads, head_dim,
+                                               max_context_len, part);
         if (!workspace || workspace_bytes < need)
             return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace))
@@ -606,8 +647,18 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * p.col_groups;
     if (waves > INT32_MAX)
         return PKV_ERR_SHAPE;
+    // Two partitions: the second partition wave of each pair merges (no
+    // merge launch).
+    const bool pair = split && parts == 2 && per_wave < pkv::kMaxQueryTiles;
+    if (pair) {
+        p.pair_tags = reinterpret_cast<uint64_t *>(
+            static_cast<char *>(workspace) +
+            mq_pair_tags_offset(num_seqs, num_queries, num_heads, head_dim, max_context_len,
+                                part));
+        p.epoch = next_pair_epoch();
+    }
     int rc = launch(kern, dim3((unsigned)waves), dim3(pkv::kWave), &p, stream);
-    if (rc != PKV_OK || !split)
+    if (rc != PKV_OK || !split || pair)
         return rc;
     pkv::MergeParams mp;
     mp.out = p.out;
@@ -889,10 +940,8 @@ size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int
     if (num_seqs <= 0 || num_queries <= 0 || num_heads <= 0 || head_dim <= 0 ||
         max_context_len <= 0 || partition_size <= 0)
         return 0;
-    return partials_bytes((int32_t)((int64_t)num_seqs * num_queries > INT32_MAX
-                                               ? INT32_MAX
-                                               : (int64_t)num_seqs * num_queries),
-                                 num_heads, head_dim, max_context_len, partition_size);
+    return mq_workspace_bytes(num_seqs, num_queries, num_heads, head_dim, max_context_len,
+                              partition_size);
 }
 
 int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,

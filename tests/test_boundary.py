@@ -163,6 +163,12 @@ def test_decode_mq_checks(L):
     assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 256) == 0
     rows = 4 * 3 * 8 * 4
     assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 64) == rows * 64 * 4 + rows * 8
+    # exactly two partitions: the partials (256-byte aligned), then one 8-byte
+    # pair tag per (sequence, head) bound
+    rows2 = 4 * 3 * 8 * 2
+    parts2 = -(-(rows2 * 64 * 4) // 256) * 256 + rows2 * 8
+    assert pkv.mq_workspace_size(4, 3, 8, 64, 256, 128) == (
+        -(-parts2 // 256) * 256 + -(-(4 * 8 * 8) // 256) * 256)
 
 
 def decode_prefix(L, out=A, q=A, kc=A, vc=A, bt=A, cl=A, scale=0.125, dt=0, ks=1.0, vs=1.0,

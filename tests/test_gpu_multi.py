@@ -95,7 +95,9 @@ def test_fp8_pools(name):
     run_case(spec, 256, f"{name} small fp8")
 
 
-@pytest.mark.parametrize("partition", [32, 256])
+# 512: two partitions of the longest context (1,000 tokens), merged inside
+# the multi-query kernel, against the plain decode's merge launch.
+@pytest.mark.parametrize("partition", [32, 256, 512])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_one_query_is_plain_decode(kv, partition):
     spec = W.Spec("q1", B=4, N=32, K=8, H=128, ctx=[1000, 37, 600, 1], seed=57, kv_dtype=kv)
@@ -111,7 +113,7 @@ def test_one_query_is_plain_decode(kv, partition):
     assert torch.equal(mq[:, 0], plain)
 
 
-@pytest.mark.parametrize("partition", [32, 512])
+@pytest.mark.parametrize("partition", [32, 512, 544])   # 544: two partitions, merged in-kernel
 def test_verification_is_sequential_decoding(partition):
     Q = 6
     spec = W.Spec("seq", B=4, N=64, K=8, H=128, ctx=[700, 33, 1030, 6], queries=Q, seed=59)
@@ -127,3 +129,18 @@ def test_verification_is_sequential_decoding(partition):
         H.gpu_decode(one, gi, w, partition=partition)
         torch.cuda.synchronize()
         assert torch.equal(multi[:, i], one), f"query {i} differs from its sequential step"
+
+
+@pytest.mark.parametrize("Q,N,K", [(2, 8, 2), (5, 8, 2), (6, 64, 8), (3, 64, 4)],
+                         ids=["1tile", "2tiles", "3tiles", "3tiles-g16"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_two_partitions_merged_in_kernel(Q, N, K, kv):
+    """max_context_len spans exactly two partitions: the second partition wave
+    of each (sequence, KV head) merges both partials.  Contexts inside the
+    first partition (finished by its wave alone), at its end, just past it,
+    and at the end of the second, including contexts shorter than Q."""
+    part = 256
+    ctx = [1, 3, 40, 255, 256, 257, 300, 511, 512, 2 * part]
+    spec = W.Spec("pair", B=len(ctx), N=N, K=K, H=128, ctx=ctx, queries=Q, seed=61,
+                  kv_dtype=kv)
+    run_case(spec, part, f"two partitions Q={Q} N={N} K={K} {kv}")
