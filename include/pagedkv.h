@@ -137,7 +137,11 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  *                  max_context_len are treated as max_context_len, negative
  *                  values as 0; a sequence of length 0 yields zeros.
  *   scale          softmax scale applied to q . k (1/sqrt(head_dim) on the
- *                  pages).
+ *                  pages); any finite value.  A negative scale is applied
+ *                  by negating the query (exact in bf16); a magnitude
+ *                  below FLT_MIN (zero included) acts as FLT_MIN, which for
+ *                  scores below 2^100 in magnitude gives every position the
+ *                  same weight, as zero does.
  *   num_kv_heads   K; num_heads (N) must be a multiple with N/K <= 16.
  *   block_size     must be 16.
  *   max_blocks_per_seq   row stride of block_tables.

@@ -49,16 +49,29 @@ __device__ __forceinline__ float load_coherent(const float *p)
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Maximum of scores, NaN-propagating (IEEE maximum): gfx950 has it as one
+// three-operand instruction that needs no canonicalised inputs, where fmaxf
+// (maxNum) costs an extra canonicalising max per operand that the compiler
+// cannot prove canonical (matrix-core results, lane exchanges).  Masked
+// positions are -inf, so a NaN here is a NaN score, which spoils its column
+// either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max8(const float (&x)[8])
+{
+    return vmax(vmax(vmax(vmax(x[0], x[1]), x[2]), vmax(vmax(x[3], x[4]), x[5])),
+                vmax(x[6], x[7]));
+}
+
 // Lane-pair reductions across the four 16-lane rows with VALU permutes
 // (no LDS round trip): max / sum of v over lanes l, l^16, l^32, l^48.
 __device__ __forceinline__ float max_over_rows(float v)
 {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                     false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                     false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float sum_over_rows(float v)

@@ -64,7 +64,10 @@ struct DecodeParams {
     const void *value_cache;      // [num_blocks][K][H][16]  (Fmt::Elem)
     const int32_t *block_tables;  // [B][max_blocks]
     const int32_t *context_lens;  // [B]
-    float scale_log2;             // scale * log2(e) (times k_scale for FP8 pools)
+    float scale_log2;             // |scale| * log2(e) (times k_scale for FP8 pools),
+                                  // at least FLT_MIN
+    uint32_t q_sign;              // 0x80008000 when the scale is negative (the
+                                  // query's signs are flipped on load), else 0
     float out_scale;              // factor on every written o: 1, or v_scale for FP8 pools
     int32_t num_heads;            // N
     int32_t num_kv_heads;         // K
@@ -190,11 +193,13 @@ __device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 1, s), q, s1, 0, 0, 0);
     }
     // Lane (col, quad) now holds the scores of tokens 8quad + e, e = 0..7.
+    // The softmax scale (never negative) goes on after the maximum, and into
+    // the exponent's argument with one fused multiply-add.
     float x[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        x[i] = s0[i] * scale_log2;
-        x[4 + i] = s1[i] * scale_log2;
+        x[i] = s0[i];
+        x[4 + i] = s1[i];
     }
     u32x4 vmask = {~0u, ~0u, ~0u, ~0u};
     if (kTail) {   // rem - head < 32 tokens valid
@@ -208,22 +213,21 @@ __device__ __forceinline__ void attend_chunk(const typename Fmt::template Regs<H
         for (int w = 0; w < 4; ++w)
             vmask[w] = (2 * w < valid ? 0x0000FFFFu : 0u) | (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
     }
-    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mx = max_over_rows(mx);
-    const float m_new = fmaxf(m, mx);
+    float mx = max8(x);
+    mx = max_over_rows(mx) * scale_log2;
+    const float m_new = vmax(m, mx);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first chunk
 
-    bf16x8 p_hi, p_lo;
-    float psum = 0.f;
+    float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(x[e] - m_new);
-        psum += p;
-        const __bf16 hi = (__bf16)p;
-        p_hi[e] = hi;
-        p_lo[e] = (__bf16)(p - (float)hi);
-    }
+    for (int e = 0; e < 8; ++e)
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m_new));
+    float psum = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e)
+        psum += p[e];
+    bf16x8 p_hi, p_lo;
+    split_bf16(p, p_hi, p_lo);
     l = l * alpha + psum;
     m = m_new;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -332,7 +336,7 @@ void decode_kernel(DecodeParams p)
             u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
             if (!live)
                 raw = u32x4{0u, 0u, 0u, 0u};
-            qf[s] = as_bf16x8(raw);
+            qf[s] = as_bf16x8(raw ^ p.q_sign);
         }
     }
 

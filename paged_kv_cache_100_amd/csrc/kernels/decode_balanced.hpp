@@ -578,7 +578,7 @@ void decode_balanced_kernel(BalancedParams p)
         if (k == 0 || ap.j == 0) {
 #pragma unroll
             for (int s = 0; s < H / 32; ++s)
-                qcur[s] = r.q[s];
+                qcur[s] = r.q[s] ^ d.q_sign;
             if constexpr (kFixed) {
                 const int a = ap.fc + ap.j;
                 pidx = a / pc;

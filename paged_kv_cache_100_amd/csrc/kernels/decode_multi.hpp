@@ -79,11 +79,13 @@ __device__ __forceinline__ void attend_chunk_multi(typename Fmt::template Regs<H
             s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 0, s), q, s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::key(r, 1, s), q, s1, 0, 0, 0);
         }
+        // Raw scores: the scale (never negative) goes on after the maximum
+        // and into the exponent's argument, as in attend_chunk.
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = s0[i] * scale_log2;
-            x[4 + i] = s1[i] * scale_log2;
+            x[i] = s0[i];
+            x[4 + i] = s1[i];
         }
         if (kMasked && mask_scores) {
 #pragma unroll
@@ -91,24 +93,23 @@ __device__ __forceinline__ void attend_chunk_multi(typename Fmt::template Regs<H
                 if (tok0 + e >= lim[t])
                     x[e] = -INFINITY;
         }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = max_over_rows(mx);
-        const float m_new = fmaxf(m[t], mx);
+        float mx = max8(x);
+        mx = max_over_rows(mx) * scale_log2;
+        const float m_new = vmax(m[t], mx);
         // A column that has seen no position yet keeps m = -inf; exponentials
         // are then taken against 0 (all of them are 0).
         const float m_ref = (kMasked && m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m[t] - m_ref);
-        bf16x8 p_hi, p_lo;
-        float psum = 0.f;
+        float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(x[e] - m_ref);
-            psum += p;
-            const __bf16 hi = (__bf16)p;
-            p_hi[e] = hi;
-            p_lo[e] = (__bf16)(p - (float)hi);
-        }
+        for (int e = 0; e < 8; ++e)
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -m_ref));
+        float psum = p[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e)
+            psum += p[e];
+        bf16x8 p_hi, p_lo;
+        split_bf16(p, p_hi, p_lo);
         l[t] = l[t] * alpha + psum;
         m[t] = m_new;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -213,7 +214,7 @@ void decode_multi_kernel(DecodeParams p)
             u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
             if (!live[t])
                 raw = u32x4{0u, 0u, 0u, 0u};
-            q_lds[(t * (H / 32) + s) * kWave + lane] = raw;
+            q_lds[(t * (H / 32) + s) * kWave + lane] = raw ^ p.q_sign;
         }
     }
 

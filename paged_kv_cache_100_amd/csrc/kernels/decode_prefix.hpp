@@ -125,7 +125,7 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
             u32x4 raw = load16(qr + Fmt::dim_offset(s, quad));
             if (mcol[t] < 0)
                 raw = u32x4{0u, 0u, 0u, 0u};
-            q_lds[(t * (H / 32) + s) * kWave + lane] = raw;
+            q_lds[(t * (H / 32) + s) * kWave + lane] = raw ^ d.q_sign;
         }
     }
 

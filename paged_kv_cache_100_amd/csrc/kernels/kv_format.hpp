@@ -32,6 +32,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
+// p = hi + lo with hi = bf16(p) and lo = bf16(p - hi), for eight values.  hi
+// is rounded in pairs; its fp32 value is read back from the packed bits (the
+// low half shifted up, the high half masked), not converted value by value.
+__device__ __forceinline__ void split_bf16(const float (&p)[8], bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        hi[e] = (__bf16)p[e];
+    const u32x4 bits = __builtin_bit_cast(u32x4, hi);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        lo[2 * w] = (__bf16)(p[2 * w] - __uint_as_float(bits[w] << 16));
+        lo[2 * w + 1] = (__bf16)(p[2 * w + 1] - __uint_as_float(bits[w] & 0xFFFF0000u));
+    }
+}
+
 // 8-byte load with the non-temporal hint.
 __device__ __forceinline__ u32x2 load8_stream(const void *p)
 {

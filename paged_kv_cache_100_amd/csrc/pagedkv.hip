@@ -2,6 +2,7 @@
 // kernel launches.  Declarations and their documentation: include/pagedkv.h.
 #include <hip/hip_runtime.h>
 
+#include <float.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -180,6 +181,21 @@ PrefixLayout prefix_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_h
     off = align256(off + (size_t)num_seqs * 4);
     L.total = off;
     return L;
+}
+
+// The kernels take the softmax scale in log2 units as a positive number: they
+// apply it to a chunk's maximum score and fuse it into each exponent.  A
+// negative scale is carried by flipping the query's signs (exact in bf16:
+// every score changes sign).  A magnitude below FLT_MIN, zero included, is
+// raised to FLT_MIN: for any score below 2^100 in magnitude the exponents
+// then stay within 2^-26 of 0 and round to weight 1, which is what a zero
+// scale gives.
+void set_softmax_scale(pkv::DecodeParams &p, float scale, float k_scale)
+{
+    float s = scale * k_scale * 1.4426950408889634f;
+    p.q_sign = s < 0.f ? 0x80008000u : 0u;
+    s = fabsf(s);
+    p.scale_log2 = s < FLT_MIN ? FLT_MIN : s;
 }
 
 // Waves the decode kernel keeps resident: one per SIMD, four SIMDs per CU.
@@ -517,7 +533,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.value_cache = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    set_softmax_scale(p, scale, k_scale);
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
@@ -1005,7 +1021,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.value_cache = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    set_softmax_scale(p, scale, k_scale);
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
@@ -1136,7 +1152,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     p.value_cache = value_cache;
     p.block_tables = block_tables;
     p.context_lens = context_lens;
-    p.scale_log2 = scale * k_scale * 1.4426950408889634f;
+    set_softmax_scale(p, scale, k_scale);
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
