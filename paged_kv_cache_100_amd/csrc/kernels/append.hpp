@@ -6,14 +6,16 @@
 // rows at the next position).  In the paged cache the "next position" of a
 // token is its slot, physical_block * 16 + offset, resolved by the caller.
 //
-// One thread moves 8 consecutive head-dim values (16 bytes) of one (token,
-// KV head): a single 16-byte store for the key row, and eight 2-byte stores
-// down the value tile's columns (value tiles are stored transposed, [H][16]),
-// so a token dirties every 128-byte line of its value tile (32 at H = 128).
-// The decode that follows reads those lines more slowly the more of them the
-// append wrote (its key rows, two lines per token, cost next to nothing);
-// writing the value elements with non-temporal stores sends them toward
-// memory at once and takes part of that cost off the decode.
+// One wave per (token, KV head).  Lane l moves head dims 2l and 2l + 1 of the
+// key row (one 4-byte store each; the wave writes the row's 2H bytes
+// contiguously) and head dims l + 64j of the value.  Value tiles are stored
+// transposed ([H][16]), so a token's value elements are 2 bytes in each of H
+// rows of 32 bytes: one store instruction of the wave writes 64 consecutive
+// rows, four elements in each 128-byte line it touches -- the most one token
+// puts in a line (a thread per 8 dims, storing down its rows, put one).  The
+// decode that follows reads the lines the append wrote more slowly the more
+// of them are freshly written; the value elements go out with non-temporal
+// stores, which send them toward memory at once.
 #pragma once
 
 #include "common.hpp"
@@ -31,48 +33,54 @@ struct AppendParams {
     int64_t num_slots;             // num_blocks * 16
 };
 
-// Makes the two row loads complete before the slot test: left alone, the
+// Makes the row loads complete before the slot test: left alone, the
 // compiler moves them behind it and the thread waits for two memory round
 // trips (slot, then rows) instead of one.
-__device__ __forceinline__ void keep_loaded(const u32x4 &a, const u32x4 &b)
+__device__ __forceinline__ void keep_loaded(uint32_t a, uint32_t b)
 {
     asm volatile("" : : "v"(a), "v"(b));
+}
+
+// (token * K + head) of this wave: the grid is 4-wave workgroups.
+__device__ __forceinline__ uint64_t append_row()
+{
+    return (uint64_t)blockIdx.x * 4 + threadIdx.x / kWave;
 }
 
 template <int H>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
 {
-    constexpr int kChunks = H / 8;   // 16-byte pieces per row
-    // The host guarantees T * K * H / 8 < 2^31: 32-bit index arithmetic.
-    const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t total = (uint32_t)p.num_tokens * p.num_kv_heads * kChunks;
-    if (gid >= total)
+    constexpr int kVals = H / kWave;                 // value dims per lane
+    const uint64_t row = append_row();
+    if (row >= (uint64_t)p.num_tokens * p.num_kv_heads)
         return;
-    const int c = (int)(gid % kChunks);
-    const uint32_t row = gid / kChunks;            // token * K + head
-    const int g = (int)(row % (uint32_t)p.num_kv_heads);
-    const uint32_t i = row / (uint32_t)p.num_kv_heads;
+    const int lane = threadIdx.x % kWave;
+    const int g = (int)(row % (uint64_t)p.num_kv_heads);
+    const uint64_t i = row / (uint64_t)p.num_kv_heads;
+    const bool key_lane = 2 * lane < H;
 
-    // The rows' loads do not depend on the slot: issue all three together.
-    const int64_t src = (int64_t)row * H + 8 * c;
-    const u32x4 kk = load16(p.k + src);
-    const u32x4 vv = load16(p.v + src);
+    // The rows' loads do not depend on the slot: issue them all together.
+    const uint16_t *krow = p.k + row * H;
+    const uint16_t *vrow = p.v + row * H;
+    const uint32_t kk = key_lane ? *reinterpret_cast<const uint32_t *>(krow + 2 * lane) : 0u;
+    uint16_t vv[kVals];
+#pragma unroll
+    for (int j = 0; j < kVals; ++j)
+        vv[j] = vrow[lane + kWave * j];
     const int64_t slot = p.slot_mapping[i];
-    keep_loaded(kk, vv);
+    keep_loaded(kk, (uint32_t)vv[0] | ((uint32_t)vv[kVals - 1] << 16));
     if (slot < 0 || slot >= p.num_slots)
         return;                                    // padding or outside the pool
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
     const int64_t tile = blk * p.num_kv_heads + g; // (block, head) tile index
 
-    store16(p.key_cache + (tile * kBlockSize + off) * H + 8 * c, kk);
-    uint16_t *dst = p.value_cache + (tile * H + 8 * c) * kBlockSize + off;
+    if (key_lane)
+        *reinterpret_cast<uint32_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane) = kk;
+    uint16_t *dst = p.value_cache + tile * H * kBlockSize + off;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t word = vv[e >> 1];
-        __builtin_nontemporal_store((uint16_t)((e & 1) ? (word >> 16) : (word & 0xFFFFu)),
-                                    dst + e * kBlockSize);
-    }
+    for (int j = 0; j < kVals; ++j)
+        __builtin_nontemporal_store(vv[j], dst + (lane + kWave * j) * kBlockSize);
 }
 
 // ---------------------------------------------------------------- FP8 ----
@@ -114,47 +122,43 @@ __device__ __forceinline__ uint32_t quantize_pair(uint32_t word, float inv)
     return codes | nan_bytes;
 }
 
-// Eight bf16 values (16 bytes) -> eight codes (8 bytes, same order).
-__device__ __forceinline__ u32x2 quantize8(u32x4 x, float inv)
-{
-    u32x2 r;
-    r[0] = quantize_pair(x[0], inv) | (quantize_pair(x[1], inv) << 16);
-    r[1] = quantize_pair(x[2], inv) | (quantize_pair(x[3], inv) << 16);
-    return r;
-}
-
+// The lane layout of append_kernel; key codes go out two per lane (2-byte
+// stores, the row's H bytes contiguously), value codes one byte per store.
 template <int H>
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params p)
 {
-    constexpr int kChunks = H / 8;   // 8-value pieces per row
-    const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-    const uint32_t total = (uint32_t)p.num_tokens * p.num_kv_heads * kChunks;
-    if (gid >= total)
+    constexpr int kVals = H / kWave;
+    const uint64_t row = append_row();
+    if (row >= (uint64_t)p.num_tokens * p.num_kv_heads)
         return;
-    const int c = (int)(gid % kChunks);
-    const uint32_t row = gid / kChunks;
-    const int g = (int)(row % (uint32_t)p.num_kv_heads);
-    const uint32_t i = row / (uint32_t)p.num_kv_heads;
+    const int lane = threadIdx.x % kWave;
+    const int g = (int)(row % (uint64_t)p.num_kv_heads);
+    const uint64_t i = row / (uint64_t)p.num_kv_heads;
+    const bool key_lane = 2 * lane < H;
 
-    const int64_t src = (int64_t)row * H + 8 * c;
-    const u32x4 kk = load16(p.k + src);
-    const u32x4 vv = load16(p.v + src);
+    const uint16_t *krow = p.k + row * H;
+    const uint16_t *vrow = p.v + row * H;
+    const uint32_t kk = key_lane ? *reinterpret_cast<const uint32_t *>(krow + 2 * lane) : 0u;
+    uint16_t vv[kVals];
+#pragma unroll
+    for (int j = 0; j < kVals; ++j)
+        vv[j] = vrow[lane + kWave * j];
     const int64_t slot = p.slot_mapping[i];
-    keep_loaded(kk, vv);
+    keep_loaded(kk, (uint32_t)vv[0] | ((uint32_t)vv[kVals - 1] << 16));
     if (slot < 0 || slot >= p.num_slots)
         return;
     const int64_t blk = slot / kBlockSize;
     const int off = (int)(slot % kBlockSize);
     const int64_t tile = blk * p.num_kv_heads + g;
 
-    const u32x2 kq = quantize8(kk, p.k_inv);
-    *reinterpret_cast<u32x2 *>(p.key_cache + (tile * kBlockSize + off) * H + 8 * c) = kq;
-
-    const u32x2 vq = quantize8(vv, p.v_inv);
-    uint8_t *dst = p.value_cache + (tile * H + 8 * c) * kBlockSize + off;
+    if (key_lane)
+        *reinterpret_cast<uint16_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane) =
+            (uint16_t)quantize_pair(kk, p.k_inv);
+    uint8_t *dst = p.value_cache + tile * H * kBlockSize + off;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        __builtin_nontemporal_store((uint8_t)(vq[e >> 2] >> (8 * (e & 3))), dst + e * kBlockSize);
+    for (int j = 0; j < kVals; ++j)
+        __builtin_nontemporal_store((uint8_t)quantize_pair(vv[j], p.v_inv),
+                                    dst + (lane + kWave * j) * kBlockSize);
 }
 
 }  // namespace pkv

@@ -279,14 +279,14 @@ int check_append(const void *k, const void *v, const int64_t *slot_mapping, void
         (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
         return PKV_ERR_ALIGN;
     if ((int64_t)num_tokens * num_kv_heads * (head_dim / 8) + 256 > INT32_MAX)
-        return PKV_ERR_SHAPE;                      // the kernels index threads in 32 bits
+        return PKV_ERR_SHAPE;                      // bounds the append grid, T * K / 4
     return PKV_OK;
 }
 
-dim3 append_grid(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim)
+// One wave per (token, KV head), four per 256-thread workgroup.
+dim3 append_grid(int32_t num_tokens, int32_t num_kv_heads)
 {
-    const int64_t threads = (int64_t)num_tokens * num_kv_heads * (head_dim / 8);
-    return dim3((unsigned)ceil_div(threads, 256));
+    return dim3((unsigned)ceil_div((int64_t)num_tokens * num_kv_heads, 4));
 }
 
 // An FP8 pool scale: finite, positive, with a finite fp32 inverse.
@@ -825,7 +825,7 @@ int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, v
     p.num_slots = num_blocks * PKV_BLOCK_SIZE;
     const void *kern = head_dim == 128 ? (const void *)pkv::append_kernel<128>
                                        : (const void *)pkv::append_kernel<64>;
-    return launch(kern, append_grid(num_tokens, num_kv_heads, head_dim), dim3(256), &p, stream);
+    return launch(kern, append_grid(num_tokens, num_kv_heads), dim3(256), &p, stream);
 }
 
 int paged_kv_append_fp8(const void *k, const void *v, const int64_t *slot_mapping,
@@ -854,7 +854,7 @@ int paged_kv_append_fp8(const void *k, const void *v, const int64_t *slot_mappin
     p.num_slots = num_blocks * PKV_BLOCK_SIZE;
     const void *kern = head_dim == 128 ? (const void *)pkv::append_fp8_kernel<128>
                                        : (const void *)pkv::append_fp8_kernel<64>;
-    return launch(kern, append_grid(num_tokens, num_kv_heads, head_dim), dim3(256), &p, stream);
+    return launch(kern, append_grid(num_tokens, num_kv_heads), dim3(256), &p, stream);
 }
 
 size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
