@@ -14,7 +14,7 @@
 // rows, four elements in each 128-byte line it touches -- the most one token
 // puts in a line (a thread per 8 dims, storing down its rows, put one).  The
 // decode that follows reads the lines the append wrote more slowly the more
-// of them are freshly written; the value elements go out with non-temporal
+// of them are freshly written; keys and values go out with non-temporal
 // stores, which send them toward memory at once.
 #pragma once
 
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
     const int64_t tile = blk * p.num_kv_heads + g; // (block, head) tile index
 
     if (key_lane)
-        *reinterpret_cast<uint32_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane) = kk;
+        __builtin_nontemporal_store(
+            kk, reinterpret_cast<uint32_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane));
     uint16_t *dst = p.value_cache + tile * H * kBlockSize + off;
 #pragma unroll
     for (int j = 0; j < kVals; ++j)
