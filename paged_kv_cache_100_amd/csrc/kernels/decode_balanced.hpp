@@ -350,6 +350,31 @@ void decode_balanced_kernel(BalancedParams p)
                     total_seq += wave_sum(seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]));
             }
         T = (int64_t)uniform(total_seq) * K;
+        // Wave 0 also stores the schedule's per-sequence chunk offsets and
+        // T, as schedule_kernel does for larger batches: the merge launch
+        // then reads two values per segment instead of scanning every
+        // context length in each of its waves.
+        if (wv == 0) {
+            int carry0 = 0;
+#pragma unroll
+            for (int t = 0; t < kTiles; ++t) {
+                if (t * kWave >= B)
+                    break;
+                int nc;
+                if constexpr (kPrefix)
+                    nc = nc_lane(t);
+                else
+                    nc = seg_chunks<kPrefix>(d, t * kWave + lane, cx[t]);
+                const int incl = wave_inclusive_scan(nc, lane);
+                if (t * kWave + lane < B)
+                    p.chunk_start[t * kWave + lane] = carry0 + incl - nc;
+                carry0 += __shfl(incl, kWave - 1);
+            }
+            if (lane == 0) {
+                p.total_chunks[0] = (int32_t)T;
+                p.chunk_start[B] = carry0;
+            }
+        }
         if (T == 0)
             return;
         c_begin = wave_begin(wv, T, p.log2_waves);
@@ -674,7 +699,6 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
 {
     constexpr int kLanesPerHead = kWave / Gp;
     constexpr int kVals = H / kLanesPerHead;      // values per lane (multiple of 4)
-    constexpr int kTiles = kInlineScheduleSeqs / kWave;
     // Pieces per memory round trip: up to 8, within about 128 registers of rows.
     constexpr int kBatch = kVals / 4 >= 8 ? 4 : 8;
     const DecodeParams &d = p.d;
@@ -685,36 +709,13 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(BalancedParams p)
     const int h0 = (lane % kLanesPerHead) * kVals;
     const bool live = g < d.group;
     const int K = d.num_kv_heads;
-    const int B = p.num_seqs;
     const int lg = p.log2_waves;
 
-    int nc;
-    int64_t T, seq_first;                 // total chunks, chunk_start[b]
-    if (p.inline_schedule) {
-        int c[kTiles];
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            const int bb = t * kWave + lane;
-            c[t] = bb < B ? seg_chunks<kPrefix>(d, bb, seq_ctx(d, bb)) : 0;
-        }
-        int total = 0, before = 0, mine = 0;
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) {
-            if (t * kWave >= B)              // tiles past the batch hold zeros
-                break;
-            total += wave_sum(c[t]);
-            if (t * kWave < b)               // tiles wholly past b add nothing
-                before += wave_sum(t * kWave + lane < b ? c[t] : 0);
-            mine = (t == b / kWave) ? __shfl(c[t], b % kWave) : mine;
-        }
-        nc = mine;
-        T = (int64_t)total * K;
-        seq_first = before;
-    } else {
-        nc = seg_chunks<kPrefix>(d, b, seq_ctx_uniform(d, b));
-        T = scalar_load(p.total_chunks);
-        seq_first = scalar_load(p.chunk_start + b);
-    }
+    // The schedule's sequence offsets and T, stored by schedule_kernel or
+    // (batches it does not run for) by the decode launch's wave 0.
+    const int nc = seg_chunks<kPrefix>(d, b, seq_ctx_uniform(d, b));
+    const int64_t T = scalar_load(p.total_chunks);
+    const int64_t seq_first = scalar_load(p.chunk_start + b);
     int n_pre = 0;                        // prefix partials of this row
     if constexpr (kPrefix)
         n_pre = uniform((stored_shared_tokens(d, b) + d.part - 1) / d.part);
