@@ -77,7 +77,8 @@ typedef enum pkv_status {
 } pkv_status;
 
 /* Supported shapes (compile-time kernel variants). */
-#define PKV_BLOCK_SIZE 16          /* tokens per cache block                      */
+#define PKV_BLOCK_SIZE 16          /* tokens per cache block (the usual size)     */
+#define PKV_BLOCK_SIZE_LARGE 32    /* the other block size built in               */
 #define PKV_MAX_GROUP 16           /* largest N / K (query heads per KV head)     */
 #define PKV_PARTITION_GRAIN 32     /* partition sizes are multiples of this       */
 #define PKV_MAX_PARTITION 1024
@@ -103,7 +104,7 @@ typedef enum pkv_status {
  * lands is unspecified).  A slot >= num_blocks * block_size is skipped (the
  * kernel never writes outside the pools).
  * Checks: NULL pointers (when num_tokens > 0), sizes, head_dim in {64, 128},
- * block_size == 16, 16-byte alignment of k, v, key_cache, value_cache.
+ * block_size 16 or 32, 16-byte alignment of k, v, key_cache, value_cache.
  * Cites: the lesson's Build-It step 1 (write at the next position) in the
  * paged form of its PagedAttention section.
  */
@@ -143,7 +144,8 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  *                  scores below 2^100 in magnitude gives every position the
  *                  same weight, as zero does.
  *   num_kv_heads   K; num_heads (N) must be a multiple with N/K <= 16.
- *   block_size     must be 16.
+ *   block_size     16 or 32 (tokens per block; the kernels read 32-token
+ *                  chunks: two blocks of 16 or one of 32).
  *   max_blocks_per_seq   row stride of block_tables.
  *   max_context_len      host-known upper bound of context_lens, at most
  *                  max_blocks_per_seq * block_size.

@@ -25,7 +25,7 @@ computation runs in the library's HIP kernels.  The library must be built
                                    context_lens, scale, num_kv_heads, block_size)
 
 Layouts: k, v [T, K, H] bf16; slot_mapping [T] int64; key_cache
-[num_blocks, K, 16, H]; value_cache [num_blocks, K, H, 16] (bf16, or for the
+[num_blocks, K, bs, H]; value_cache [num_blocks, K, H, bs], bs 16 or 32 (bf16, or for the
 ``_fp8`` calls one-byte OCP FP8 E4M3 codes as uint8 or float8_e4m3fn, one
 scale per pool); q [B, N, H] bf16; out [B, N, H] float32; block_tables
 [B, max_blocks] int32; context_lens [B] int32.

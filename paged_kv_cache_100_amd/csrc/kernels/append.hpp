@@ -26,11 +26,11 @@ struct AppendParams {
     const uint16_t *k;             // [T][K][H]
     const uint16_t *v;             // [T][K][H]
     const int64_t *slot_mapping;   // [T]
-    uint16_t *key_cache;           // [num_blocks][K][16][H]
-    uint16_t *value_cache;         // [num_blocks][K][H][16]
+    uint16_t *key_cache;           // [num_blocks][K][BS][H]
+    uint16_t *value_cache;         // [num_blocks][K][H][BS]
     int32_t num_tokens;
     int32_t num_kv_heads;
-    int64_t num_slots;             // num_blocks * 16
+    int64_t num_slots;             // num_blocks * BS
 };
 
 // Makes the row loads complete before the slot test: left alone, the
@@ -47,7 +47,7 @@ __device__ __forceinline__ uint64_t append_row()
     return (uint64_t)blockIdx.x * 4 + threadIdx.x / kWave;
 }
 
-template <int H>
+template <int H, int BS = kBlockSize>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
 {
     constexpr int kVals = H / kWave;                 // value dims per lane
@@ -71,17 +71,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p)
     keep_loaded(kk, (uint32_t)vv[0] | ((uint32_t)vv[kVals - 1] << 16));
     if (slot < 0 || slot >= p.num_slots)
         return;                                    // padding or outside the pool
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
+    const int64_t blk = slot / BS;
+    const int off = (int)(slot % BS);
     const int64_t tile = blk * p.num_kv_heads + g; // (block, head) tile index
 
     if (key_lane)
         __builtin_nontemporal_store(
-            kk, reinterpret_cast<uint32_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane));
-    uint16_t *dst = p.value_cache + tile * H * kBlockSize + off;
+            kk, reinterpret_cast<uint32_t *>(p.key_cache + (tile * BS + off) * H + 2 * lane));
+    uint16_t *dst = p.value_cache + tile * H * BS + off;
 #pragma unroll
     for (int j = 0; j < kVals; ++j)
-        __builtin_nontemporal_store(vv[j], dst + (lane + kWave * j) * kBlockSize);
+        __builtin_nontemporal_store(vv[j], dst + (lane + kWave * j) * BS);
 }
 
 // ---------------------------------------------------------------- FP8 ----
@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t quantize_pair(uint32_t word, float inv)
 
 // The lane layout of append_kernel; key codes go out two per lane (2-byte
 // stores, the row's H bytes contiguously), value codes one byte per store.
-template <int H>
+template <int H, int BS = kBlockSize>
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params p)
 {
     constexpr int kVals = H / kWave;
@@ -148,18 +148,18 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendFp8Params p)
     keep_loaded(kk, (uint32_t)vv[0] | ((uint32_t)vv[kVals - 1] << 16));
     if (slot < 0 || slot >= p.num_slots)
         return;
-    const int64_t blk = slot / kBlockSize;
-    const int off = (int)(slot % kBlockSize);
+    const int64_t blk = slot / BS;
+    const int off = (int)(slot % BS);
     const int64_t tile = blk * p.num_kv_heads + g;
 
     if (key_lane)
-        *reinterpret_cast<uint16_t *>(p.key_cache + (tile * kBlockSize + off) * H + 2 * lane) =
+        *reinterpret_cast<uint16_t *>(p.key_cache + (tile * BS + off) * H + 2 * lane) =
             (uint16_t)quantize_pair(kk, p.k_inv);
-    uint8_t *dst = p.value_cache + tile * H * kBlockSize + off;
+    uint8_t *dst = p.value_cache + tile * H * BS + off;
 #pragma unroll
     for (int j = 0; j < kVals; ++j)
         __builtin_nontemporal_store((uint8_t)quantize_pair(vv[j], p.v_inv),
-                                    dst + (lane + kWave * j) * kBlockSize);
+                                    dst + (lane + kWave * j) * BS);
 }
 
 }  // namespace pkv

@@ -95,6 +95,9 @@ struct DecodeParams {
     // second (that one merges both partials); null = merge_parts_kernel merges.
     uint64_t *pair_tags = nullptr;
     uint64_t epoch = 0;           // this call's tag value (never 0)
+    // Tokens per cache block (16 or 32).  The host picks the kernels built
+    // for it; the kernels take it as a template parameter, not from here.
+    int32_t block_size = kBlockSize;
 };
 
 // First position a sequence of ctx tokens attends (sliding window), else 0.
@@ -151,10 +154,34 @@ __device__ __forceinline__ int clamp_block(int id, int64_t num_blocks)
 struct ChunkIds {
     int raw0, raw1;
 };
+// The block ids of chunk jj (32 tokens) from a table row of nblk entries:
+// two 16-token blocks, or one 32-token block (then raw1 = raw0).
+template <int BS = kBlockSize>
 __device__ __forceinline__ ChunkIds load_chunk_ids(const int32_t *row, int jj, int nblk)
 {
-    const int e = 2 * jj;   // e < nblk
-    return ChunkIds{scalar_load(row + e), scalar_load(row + min(e + 1, nblk - 1))};
+    static_assert(BS == 16 || BS == 32, "16- or 32-token blocks");
+    if constexpr (BS == 32) {
+        const int id = scalar_load(row + jj);
+        return ChunkIds{id, id};
+    } else {
+        const int e = 2 * jj;   // e < nblk
+        return ChunkIds{scalar_load(row + e), scalar_load(row + min(e + 1, nblk - 1))};
+    }
+}
+
+// Element offsets, from a chunk's block offsets o0 / o1 (each the start of a
+// (block, KV head) tile), of its second 16 tokens in the key and value
+// tiles: the second block's tile with 16-token blocks; with 32-token blocks
+// the same tile, 16 key rows further and 16 elements into every value row.
+template <int BS, int H>
+__device__ __forceinline__ uint64_t key_hi(uint64_t o1)
+{
+    return BS == 32 ? o1 + 16 * H : o1;
+}
+template <int BS>
+__device__ __forceinline__ uint64_t value_hi(uint64_t o1)
+{
+    return BS == 32 ? o1 + 16 : o1;
 }
 
 // clamp_block's bound as an unsigned 32-bit value: ids are int32, so
@@ -166,8 +193,8 @@ __device__ __forceinline__ uint32_t id_bound(int64_t num_blocks)
 }
 
 // Element offset of the block with id `raw` (block 0 if raw is outside
-// [0, num_blocks)) in a pool of block_elems = K * 16 * H elements per block.
-// The host keeps K * 16 * H below 2^31, so one 32 x 32-bit product serves.
+// [0, num_blocks)) in a pool of block_elems = K * BS * H elements per block.
+// The host keeps K * BS * H below 2^31, so one 32 x 32-bit product serves.
 __device__ __forceinline__ uint64_t block_offset(int raw, uint32_t bound, uint32_t block_elems)
 {
     const uint32_t id = (uint32_t)raw < bound ? (uint32_t)raw : 0u;
@@ -287,8 +314,8 @@ __device__ __forceinline__ void run_ring(int total, Buf (&buf)[kRing], Issue &&i
 // One wave per (KV head, sequence) when a single partition (at most 1,024
 // tokens) covers every context: the wave normalises and writes its rows.
 // Several partitions run on the persistent waves of decode_balanced.hpp.
-// Grid: (1, K, B).
-template <class Fmt, int H>
+// Grid: (1, K, B).  BS: tokens per cache block (16 or 32).
+template <class Fmt, int H, int BS = kBlockSize>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_kernel(DecodeParams p)
 {
@@ -304,7 +331,7 @@ void decode_kernel(DecodeParams p)
     // length is known (every entry up to the table row's end is in bounds),
     // so the two loads overlap; entries past the last block are unused.
     const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks;
-    const int table_avail = min(p.part / kBlockSize, p.max_blocks);
+    const int table_avail = min(p.part / BS, p.max_blocks);
     int my_id = 0;
     if (lane < table_avail)
         my_id = table[lane];
@@ -325,7 +352,7 @@ void decode_kernel(DecodeParams p)
         return;
     }
     const int end = min(p.part, ctx);
-    const int n_blocks = (end - 1) / kBlockSize + 1;
+    const int n_blocks = (end - 1) / BS + 1;
     my_id = clamp_block(my_id, p.num_blocks);
 
     bf16x8 qf[H / 32];
@@ -340,7 +367,7 @@ void decode_kernel(DecodeParams p)
         }
     }
 
-    const int64_t tile_elems = (int64_t)kBlockSize * H;              // one (block, head) tile
+    const int64_t tile_elems = (int64_t)BS * H;                      // one (block, head) tile
     const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
     using Elem = typename Fmt::Elem;
     using Regs = typename Fmt::template Regs<H>;
@@ -350,17 +377,19 @@ void decode_kernel(DecodeParams p)
     // Chunks start at cbeg: the 32-token boundary at or below the window
     // start (0 without a window).
     const int cbeg = __builtin_amdgcn_readfirstlane(lo - lo % kChunk);
-    const int boff = cbeg / kBlockSize;             // table entries before cbeg
+    const int boff = cbeg / BS;                     // table entries before cbeg
     const int head = lo - cbeg;                      // masked leading positions of chunk 0
 
     // Issue the loads of chunk ci (tokens cbeg + 32ci ...); its second block
     // is addressed only if the chunk reaches into it.
     auto issue = [&](Regs &r, int ci) {
-        const int k0 = boff + 2 * ci;
+        const int k0 = boff + (kChunk / BS) * ci;
         const int id0 = __builtin_amdgcn_readlane(my_id, k0);
-        const int id1 = (k0 + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, k0 + 1) : id0;
-        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
-                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+        const int id1 = (BS == 16 && k0 + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, k0 + 1)
+                                                        : id0;
+        const uint64_t o0 = (uint64_t)id0 * block_elems, o1 = (uint64_t)id1 * block_elems;
+        Fmt::template load<H, BS>(r, kbase + o0, kbase + key_hi<BS, H>(o1), vbase + o0,
+                                  vbase + value_hi<BS>(o1), col, quad);
     };
 
     float m = -INFINITY, l = 0.f;

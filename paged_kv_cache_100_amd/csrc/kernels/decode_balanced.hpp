@@ -267,7 +267,8 @@ struct BalancedBuf {
 // ones; they share the stage's LDS.  For small batches they also store the
 // shared spans for the merge, which the persistent waves compute for
 // themselves.
-template <class Fmt, int H, bool kFixed = false, bool kPrefix = false, int kGroupTiles = 0>
+template <class Fmt, int H, bool kFixed = false, bool kPrefix = false, int kGroupTiles = 0,
+          int BS = kBlockSize>
 __global__ __launch_bounds__(kWave * kGroupWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_balanced_kernel(BalancedParams p)
 {
@@ -287,7 +288,7 @@ void decode_balanced_kernel(BalancedParams p)
         static_assert(kPrefix && kGroupTiles * (H / 32) * kWave * 16 <= kStageBytes,
                       "group queries fit the stage");
         if (wv >= p.num_waves) {
-            prefix_group_wave<Fmt, H, kGroupTiles>(d, p.prefix_parts, wv - p.num_waves,
+            prefix_group_wave<Fmt, H, kGroupTiles, BS>(d, p.prefix_parts, wv - p.num_waves,
                                                    reinterpret_cast<u32x4 *>(stage_o),
                                                    p.inline_schedule != 0);
             return;
@@ -457,7 +458,7 @@ void decode_balanced_kernel(BalancedParams p)
     start.j = uniform(st.z);
     start.ctx = min(max(uniform(st.w), 0), d.max_ctx);
     start.row = d.block_tables + (int64_t)start.b * d.max_blocks;
-    start.nblk = (start.ctx + kBlockSize - 1) / kBlockSize;
+    start.nblk = (start.ctx + BS - 1) / BS;
     if constexpr (kPrefix) {
         start.nc = nc_at(start.b, start.ctx);
         start.fc = fc_at(start.b, start.ctx);
@@ -498,7 +499,7 @@ void decode_balanced_kernel(BalancedParams p)
         q.b = nx.x;
         q.ctx = nx.y;
         q.row = d.block_tables + (int64_t)q.b * d.max_blocks;
-        q.nblk = (q.ctx + kBlockSize - 1) / kBlockSize;
+        q.nblk = (q.ctx + BS - 1) / BS;
         if constexpr (kPrefix) {
             q.nc = nc_at(q.b, q.ctx);
             q.fc = fc_at(q.b, q.ctx);
@@ -508,7 +509,7 @@ void decode_balanced_kernel(BalancedParams p)
         }
     };
 
-    constexpr uint32_t tile_elems = kBlockSize * H;
+    constexpr uint32_t tile_elems = BS * H;
     const uint32_t block_elems = (uint32_t)K * tile_elems;   // < 2^31 (K <= 65535)
     const uint32_t id_lim = id_bound(d.num_blocks);
     const Elem *kcache = static_cast<const Elem *>(d.key_cache);
@@ -517,14 +518,14 @@ void decode_balanced_kernel(BalancedParams p)
     // ---- issue side: its own cursor; each chunk's two block ids are loaded
     // one chunk ahead (load_chunk_ids) ----
     Pos ip = start;
-    ChunkIds ids = load_chunk_ids(ip.row, ip.fc + ip.j, ip.nblk);
+    ChunkIds ids = load_chunk_ids<BS>(ip.row, ip.fc + ip.j, ip.nblk);
     auto issue = [&](Buf &r, int k) {
         // ip is chunk k; ids are its blocks
         const uint64_t head_off = (uint32_t)ip.kvh * tile_elems;
         const uint64_t o0 = head_off + block_offset(ids.raw0, id_lim, block_elems);
         const uint64_t o1 = head_off + block_offset(ids.raw1, id_lim, block_elems);
-        Fmt::template load<H>(r.kv, kcache + o0, kcache + o1, vcache + o0, vcache + o1, col,
-                              quad);
+        Fmt::template load<H, BS>(r.kv, kcache + o0, kcache + key_hi<BS, H>(o1), vcache + o0,
+                                  vcache + value_hi<BS>(o1), col, quad);
         if (k == 0 || ip.j == 0) {    // the chunk opens a segment: bring its queries
             // Columns past the group repeat its last query; their results are
             // never stored.
@@ -536,7 +537,7 @@ void decode_balanced_kernel(BalancedParams p)
         }
         if (k + 1 < total) {          // step to chunk k + 1 and fetch its block ids
             next_pos(ip);
-            ids = load_chunk_ids(ip.row, ip.fc + ip.j, ip.nblk);
+            ids = load_chunk_ids<BS>(ip.row, ip.fc + ip.j, ip.nblk);
         }
     };
 

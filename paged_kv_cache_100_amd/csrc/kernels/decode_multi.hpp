@@ -129,7 +129,7 @@ __device__ __forceinline__ void attend_chunk_multi(typename Fmt::template Regs<H
 // Grid: one dimension of kXcds * col_groups * ceil(items / kXcds) waves.
 // Workgroup id L -> XCD L % 8, slot j = L / 8 on it; column group j % CG of
 // item (j / CG) * 8 + L % 8; item = (b * K + kvh) * parts + partition.
-template <class Fmt, int H, int kTiles, bool kSplit>
+template <class Fmt, int H, int kTiles, bool kSplit, int BS = kBlockSize>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_multi_kernel(DecodeParams p)
 {
@@ -150,7 +150,7 @@ void decode_multi_kernel(DecodeParams p)
     const int G = p.group;
 
     const int start = part_idx * p.part;
-    const int first_block = start / kBlockSize;
+    const int first_block = start / BS;
     const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks + first_block;
 
     const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
@@ -200,7 +200,7 @@ void decode_multi_kernel(DecodeParams p)
         return;
     }
     const int end = min(start + p.part, ctx);
-    const int n_blocks = (end - 1) / kBlockSize - first_block + 1;
+    const int n_blocks = (end - 1) / BS - first_block + 1;
     const int n_chunks = (end - start + kChunk - 1) / kChunk;
 
     // The query fragments live in this wave's LDS (each lane reads back only
@@ -218,7 +218,7 @@ void decode_multi_kernel(DecodeParams p)
         }
     }
 
-    constexpr uint32_t tile_elems = kBlockSize * H;
+    constexpr uint32_t tile_elems = BS * H;
     const uint32_t block_elems = (uint32_t)p.num_kv_heads * tile_elems;   // < 2^31
     const uint32_t id_lim = id_bound(p.num_blocks);
     using Elem = typename Fmt::Elem;
@@ -228,13 +228,14 @@ void decode_multi_kernel(DecodeParams p)
 
     // A chunk's two block ids are loaded one chunk ahead (load_chunk_ids), so
     // a partition may span any number of blocks.
-    ChunkIds ids = load_chunk_ids(table, 0, n_blocks);
+    ChunkIds ids = load_chunk_ids<BS>(table, 0, n_blocks);
     auto issue = [&](Regs &r, int ci) {
         const uint64_t o0 = block_offset(ids.raw0, id_lim, block_elems);
         const uint64_t o1 = block_offset(ids.raw1, id_lim, block_elems);
-        Fmt::template load<H>(r, kbase + o0, kbase + o1, vbase + o0, vbase + o1, col, quad);
+        Fmt::template load<H, BS>(r, kbase + o0, kbase + key_hi<BS, H>(o1), vbase + o0,
+                                  vbase + value_hi<BS>(o1), col, quad);
         if (ci + 1 < n_chunks)
-            ids = load_chunk_ids(table, ci + 1, n_blocks);
+            ids = load_chunk_ids<BS>(table, ci + 1, n_blocks);
     };
 
     float m[kTiles], l[kTiles];

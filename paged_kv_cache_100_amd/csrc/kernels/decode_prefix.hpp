@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kWave) void prefix_spans_kernel(DecodeParams d)
 // prefix_parts: partitions per member row, ceil(max shared span / P), with
 // d.part = P.  q_lds: kTiles * (H / 32) * 64 16-byte slots of LDS.
 // store_spans: waves L < ceil(B / 64) store S_b of sequences 64 L + lane.
-template <class Fmt, int H, int kTiles>
+template <class Fmt, int H, int kTiles, int BS = kBlockSize>
 __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int prefix_parts, int L,
                                                   u32x4 *q_lds, bool store_spans)
 {
@@ -76,9 +76,9 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
     // a partition holds, within the table row), then the partition's
     // positions within the lead's shared span.
     const int start = part_idx * d.part;
-    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + start / kBlockSize;
+    const int32_t *table = d.block_tables + (int64_t)lead * d.max_blocks + start / BS;
     int my_id = 0;
-    if (lane < d.part / kBlockSize && start / kBlockSize + lane < d.max_blocks)
+    if (lane < d.part / BS && start / BS + lane < d.max_blocks)
         my_id = clamp_block(table[lane], d.num_blocks);
     const int prefix = d.prefix_tokens[grp];
     const int ctx_lead = min(max(d.context_lens[lead], 0), d.max_ctx);
@@ -86,7 +86,7 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
     if (start >= span)
         return;
     const int end = min(start + d.part, span);
-    const int n_blocks = (end - start) / kBlockSize;
+    const int n_blocks = (end - start) / BS;
 
     // Column t of this lane: member m, head g; lim: the end of the member's
     // shared positions (a multiple of the chunk).  Only the member's sequence
@@ -129,18 +129,20 @@ __device__ __forceinline__ void prefix_group_wave(const DecodeParams &d, int pre
         }
     }
 
-    const int64_t tile_elems = (int64_t)kBlockSize * H;
+    const int64_t tile_elems = (int64_t)BS * H;
     const int64_t block_elems = (int64_t)d.num_kv_heads * tile_elems;
     using Elem = typename Fmt::Elem;
     using Regs = typename Fmt::template Regs<H>;
     const Elem *kbase = static_cast<const Elem *>(d.key_cache) + kvh * tile_elems;
     const Elem *vbase = static_cast<const Elem *>(d.value_cache) + kvh * tile_elems;
     auto issue = [&](Regs &r, int ci) {
-        const int id0 = __builtin_amdgcn_readlane(my_id, 2 * ci);
-        const int id1 = (2 * ci + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, 2 * ci + 1)
-                                                : id0;
-        Fmt::template load<H>(r, kbase + id0 * block_elems, kbase + id1 * block_elems,
-                              vbase + id0 * block_elems, vbase + id1 * block_elems, col, quad);
+        const int k0 = (kChunk / BS) * ci;
+        const int id0 = __builtin_amdgcn_readlane(my_id, k0);
+        const int id1 = (BS == 16 && k0 + 1 < n_blocks) ? __builtin_amdgcn_readlane(my_id, k0 + 1)
+                                                        : id0;
+        const uint64_t o0 = (uint64_t)id0 * block_elems, o1 = (uint64_t)id1 * block_elems;
+        Fmt::template load<H, BS>(r, kbase + o0, kbase + key_hi<BS, H>(o1), vbase + o0,
+                                  vbase + value_hi<BS>(o1), col, quad);
     };
 
     float m[kTiles], l[kTiles];

@@ -69,9 +69,10 @@ struct KvBf16 {
 
     __device__ static __forceinline__ int dim_offset(int s, int quad) { return 32 * s + 8 * quad; }
 
-    // k_lo / v_lo: the (block, KV head) tiles of the chunk's first block;
-    // k_hi / v_hi: those of its second block.
-    template <int H>
+    // k_lo / v_lo: the chunk's first 16 tokens (their first key row, their
+    // first element of every value row); k_hi / v_hi: its last 16 (key_hi,
+    // value_hi).  BS, the tokens per block, is the value rows' length.
+    template <int H, int BS = kBlockSize>
     __device__ static __forceinline__ void load(Regs<H> &r, const Elem *k_lo, const Elem *k_hi,
                                                 const Elem *v_lo, const Elem *v_hi, int col,
                                                 int quad)
@@ -86,7 +87,7 @@ struct KvBf16 {
         const Elem *vb = (quad >> 1) ? v_hi : v_lo;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
-            r.v[c] = load16_stream(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
+            r.v[c] = load16_stream(vb + (16 * c + col) * BS + 8 * (quad & 1));
     }
 
     template <int H>
@@ -164,7 +165,7 @@ struct KvFp8 {
         return 64 * (s >> 1) + 16 * quad + 8 * (s & 1);
     }
 
-    template <int H>
+    template <int H, int BS = kBlockSize>
     __device__ static __forceinline__ void load(Regs<H> &r, const Elem *k_lo, const Elem *k_hi,
                                                 const Elem *v_lo, const Elem *v_hi, int col,
                                                 int quad)
@@ -179,7 +180,7 @@ struct KvFp8 {
         const Elem *vb = (quad >> 1) ? v_hi : v_lo;
 #pragma unroll
         for (int c = 0; c < H / 16; ++c)
-            r.v[c] = load8_stream(vb + (16 * c + col) * kBlockSize + 8 * (quad & 1));
+            r.v[c] = load8_stream(vb + (16 * c + col) * BS + 8 * (quad & 1));
     }
 
     template <int H>

@@ -25,6 +25,7 @@ constexpr int kVersionMinor = 6;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_head_dim(int32_t h) { return h == 64 || h == 128; }
+bool supported_block_size(int32_t bs) { return bs == 16 || bs == 32; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -269,7 +270,7 @@ int check_append(const void *k, const void *v, const int64_t *slot_mapping, void
 {
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
         return PKV_ERR_SHAPE;
-    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PKV_ERR_UNSUPPORTED;
     if (num_tokens == 0)
         return PKV_OK;
@@ -367,25 +368,35 @@ int persistent_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int3
         if (rc != PKV_OK)
             return rc;
     }
-    const void *dk = head_dim == 128
-                         ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, false>
-                         : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, false>;
+    const bool bs32 = p.block_size == 32;
+    const void *dk =
+        head_dim == 128
+            ? (bs32 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, false, 0, 32>
+                    : (const void *)pkv::decode_balanced_kernel<Fmt, 128, true, false, 0, 16>)
+            : (bs32 ? (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, false, 0, 32>
+                    : (const void *)pkv::decode_balanced_kernel<Fmt, 64, true, false, 0, 16>);
     return launch(dk, dim3((unsigned)ceil_div(bp.num_waves, pkv::kGroupWaves)),
                   dim3(pkv::kWave * pkv::kGroupWaves), &bp, stream);   // the full chip
 }
 
-// Token-balanced kernel of the shared-prefix path for a head dim and the
-// group waves' tiles (0: no group waves in the grid; else 1 to 4).
-template <class Fmt, int H>
-const void *balanced_prefix_kernel(int tiles)
+// Token-balanced kernel of the shared-prefix path for a head dim, block size
+// and the group waves' tiles (0: no group waves in the grid; else 1 to 4).
+template <class Fmt, int H, int BS>
+const void *balanced_prefix_kernel_bs(int tiles)
 {
     switch (tiles) {
-    case 0: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 0>;
-    case 1: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 1>;
-    case 2: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 2>;
-    case 3: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 3>;
-    default: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 4>;
+    case 0: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 0, BS>;
+    case 1: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 1, BS>;
+    case 2: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 2, BS>;
+    case 3: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 3, BS>;
+    default: return (const void *)pkv::decode_balanced_kernel<Fmt, H, false, true, 4, BS>;
     }
+}
+template <class Fmt, int H>
+const void *balanced_prefix_kernel(int tiles, int block_size)
+{
+    return block_size == 32 ? balanced_prefix_kernel_bs<Fmt, H, 32>(tiles)
+                            : balanced_prefix_kernel_bs<Fmt, H, 16>(tiles);
 }
 
 // Token-balanced decode: schedule (large batches), persistent decode, merge
@@ -439,11 +450,16 @@ int balanced_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32_
     }
     const void *dk;
     if constexpr (kPrefix)
-        dk = head_dim == 128 ? balanced_prefix_kernel<Fmt, 128>(group_tiles)
-                             : balanced_prefix_kernel<Fmt, 64>(group_tiles);
+        dk = head_dim == 128 ? balanced_prefix_kernel<Fmt, 128>(group_tiles, p.block_size)
+                             : balanced_prefix_kernel<Fmt, 64>(group_tiles, p.block_size);
     else
-        dk = head_dim == 128 ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, false>
-                             : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, false>;
+        dk = head_dim == 128
+                 ? (p.block_size == 32
+                        ? (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, false, 0, 32>
+                        : (const void *)pkv::decode_balanced_kernel<Fmt, 128, false, false, 0, 16>)
+                 : (p.block_size == 32
+                        ? (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, false, 0, 32>
+                        : (const void *)pkv::decode_balanced_kernel<Fmt, 64, false, false, 0, 16>);
     // Four-wave workgroups for a full chip of waves; a trimmed grid (small
     // problems) takes one or two waves per workgroup, so it spreads over the
     // CUs instead of filling a quarter or half of them.
@@ -474,13 +490,13 @@ int check_decode(float *out, const void *q, const void *key_cache, const void *v
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         max_context_len < 0 || num_blocks < 0 || window < 0)
         return PKV_ERR_SHAPE;
-    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PKV_ERR_UNSUPPORTED;
     if (num_heads % num_kv_heads != 0)
         return PKV_ERR_SHAPE;
     if (num_heads / num_kv_heads > PKV_MAX_GROUP)
         return PKV_ERR_UNSUPPORTED;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
         return PKV_ERR_SHAPE;
     if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
         return PKV_ERR_SHAPE;
@@ -537,6 +553,7 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
+    p.block_size = block_size;
     p.group = num_heads / num_kv_heads;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
@@ -578,8 +595,12 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     p.num_parts = (int32_t)parts;
     if (!split) {
         const dim3 grid(1u, (unsigned)num_kv_heads, (unsigned)num_seqs);
-        const void *kern = head_dim == 128 ? (const void *)pkv::decode_kernel<Fmt, 128>
-                                           : (const void *)pkv::decode_kernel<Fmt, 64>;
+        const bool bs32 = block_size == 32;
+        const void *kern =
+            head_dim == 128 ? (bs32 ? (const void *)pkv::decode_kernel<Fmt, 128, 32>
+                                    : (const void *)pkv::decode_kernel<Fmt, 128, 16>)
+                            : (bs32 ? (const void *)pkv::decode_kernel<Fmt, 64, 32>
+                                    : (const void *)pkv::decode_kernel<Fmt, 64, 16>);
         return launch(kern, grid, dim3(pkv::kWave), &p, stream);
     }
     int rc = persistent_launch<Fmt>(p, head_dim, num_seqs, num_heads, num_kv_heads,
@@ -602,20 +623,27 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
     return launch_merge(mp, head_dim, num_kv_heads, num_seqs, stream);
 }
 
-// Multi-query decode: kernel for a head dim, tiles per wave (1 to 4) and split.
-template <class Fmt, int H>
-const void *multi_kernel(int tiles, bool split)
+// Multi-query decode: kernel for a head dim, block size, tiles per wave (1 to
+// 4) and split.
+template <class Fmt, int H, int BS>
+const void *multi_kernel_bs(int tiles, bool split)
 {
     switch (tiles) {
-    case 1: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 1, true>
-                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 1, false>;
-    case 2: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 2, true>
-                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 2, false>;
-    case 3: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 3, true>
-                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 3, false>;
-    default: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 4, true>
-                          : (const void *)pkv::decode_multi_kernel<Fmt, H, 4, false>;
+    case 1: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 1, true, BS>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 1, false, BS>;
+    case 2: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 2, true, BS>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 2, false, BS>;
+    case 3: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 3, true, BS>
+                         : (const void *)pkv::decode_multi_kernel<Fmt, H, 3, false, BS>;
+    default: return split ? (const void *)pkv::decode_multi_kernel<Fmt, H, 4, true, BS>
+                          : (const void *)pkv::decode_multi_kernel<Fmt, H, 4, false, BS>;
     }
+}
+template <class Fmt, int H>
+const void *multi_kernel(int tiles, bool split, int block_size)
+{
+    return block_size == 32 ? multi_kernel_bs<Fmt, H, 32>(tiles, split)
+                            : multi_kernel_bs<Fmt, H, 16>(tiles, split);
 }
 
 // Tiles per wave of the shared-prefix group waves: the fewest (most waves,
@@ -657,8 +685,8 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     p.col_groups = (int32_t)ceil_div(tiles, pkv::kTilesPerWave);
     p.num_seqs = num_seqs;
     const int per_wave = tiles < pkv::kTilesPerWave ? tiles : pkv::kTilesPerWave;
-    const void *kern = head_dim == 128 ? multi_kernel<Fmt, 128>(per_wave, split)
-                                       : multi_kernel<Fmt, 64>(per_wave, split);
+    const void *kern = head_dim == 128 ? multi_kernel<Fmt, 128>(per_wave, split, p.block_size)
+                                       : multi_kernel<Fmt, 64>(per_wave, split, p.block_size);
     const int64_t items = parts * num_kv_heads * num_seqs;
     const int64_t waves = ceil_div(items, pkv::kXcds) * pkv::kXcds * p.col_groups;
     if (waves > INT32_MAX)
@@ -822,9 +850,12 @@ int paged_kv_append(const void *k, const void *v, const int64_t *slot_mapping, v
     p.value_cache = static_cast<uint16_t *>(value_cache);
     p.num_tokens = num_tokens;
     p.num_kv_heads = num_kv_heads;
-    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
-    const void *kern = head_dim == 128 ? (const void *)pkv::append_kernel<128>
-                                       : (const void *)pkv::append_kernel<64>;
+    p.num_slots = num_blocks * block_size;
+    const bool bs32 = block_size == 32;
+    const void *kern = head_dim == 128 ? (bs32 ? (const void *)pkv::append_kernel<128, 32>
+                                               : (const void *)pkv::append_kernel<128, 16>)
+                                       : (bs32 ? (const void *)pkv::append_kernel<64, 32>
+                                               : (const void *)pkv::append_kernel<64, 16>);
     return launch(kern, append_grid(num_tokens, num_kv_heads), dim3(256), &p, stream);
 }
 
@@ -851,9 +882,12 @@ int paged_kv_append_fp8(const void *k, const void *v, const int64_t *slot_mappin
     p.v_inv = 1.0f / v_scale;
     p.num_tokens = num_tokens;
     p.num_kv_heads = num_kv_heads;
-    p.num_slots = num_blocks * PKV_BLOCK_SIZE;
-    const void *kern = head_dim == 128 ? (const void *)pkv::append_fp8_kernel<128>
-                                       : (const void *)pkv::append_fp8_kernel<64>;
+    p.num_slots = num_blocks * block_size;
+    const bool bs32 = block_size == 32;
+    const void *kern = head_dim == 128 ? (bs32 ? (const void *)pkv::append_fp8_kernel<128, 32>
+                                               : (const void *)pkv::append_fp8_kernel<128, 16>)
+                                       : (bs32 ? (const void *)pkv::append_fp8_kernel<64, 32>
+                                               : (const void *)pkv::append_fp8_kernel<64, 16>);
     return launch(kern, append_grid(num_tokens, num_kv_heads), dim3(256), &p, stream);
 }
 
@@ -975,13 +1009,13 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
         return PKV_ERR_SHAPE;
     if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
         return PKV_ERR_UNSUPPORTED;
-    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PKV_ERR_UNSUPPORTED;
     if (num_heads % num_kv_heads != 0)
         return PKV_ERR_SHAPE;
     if ((int64_t)num_queries * (num_heads / num_kv_heads) > PKV_MAX_QUERY_ROWS)
         return PKV_ERR_UNSUPPORTED;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
         return PKV_ERR_SHAPE;
     if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
         return PKV_ERR_SHAPE;
@@ -1025,6 +1059,7 @@ int paged_decode_attention_mq(float *out, const void *q, const void *key_cache,
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
+    p.block_size = block_size;
     p.group = num_heads / num_kv_heads;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
@@ -1099,7 +1134,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
         return PKV_ERR_SHAPE;
     if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
         return PKV_ERR_UNSUPPORTED;
-    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PKV_ERR_UNSUPPORTED;
     if (num_heads % num_kv_heads != 0)
         return PKV_ERR_SHAPE;
@@ -1107,7 +1142,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_members * (num_heads / num_kv_heads) > PKV_MAX_PREFIX_ROWS)
         return PKV_ERR_UNSUPPORTED;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
         return PKV_ERR_SHAPE;
     if ((int64_t)max_context_len + partition_size > INT32_MAX)   // partition ends fit in int
         return PKV_ERR_SHAPE;
@@ -1156,6 +1191,7 @@ int paged_decode_attention_prefix(float *out, const void *q, const void *key_cac
     p.out_scale = v_scale;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
+    p.block_size = block_size;
     p.group = num_heads / num_kv_heads;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
@@ -1191,7 +1227,7 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *src_
         return PKV_ERR_SHAPE;
     if (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3)
         return PKV_ERR_UNSUPPORTED;
-    if (!supported_head_dim(head_dim) || block_size != PKV_BLOCK_SIZE)
+    if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
         return PKV_ERR_UNSUPPORTED;
     if (num_pairs == 0)
         return PKV_OK;
@@ -1208,7 +1244,7 @@ int paged_kv_copy_blocks(void *key_cache, void *value_cache, const int32_t *src_
     p.value_cache = static_cast<uint8_t *>(value_cache);
     p.src = src_blocks;
     p.dst = dst_blocks;
-    p.block_bytes = (int64_t)num_kv_heads * PKV_BLOCK_SIZE * head_dim *
+    p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim *
                     (kv_dtype == PKV_KV_BF16 ? 2 : 1);
     p.num_blocks = num_blocks;
     const int64_t slices = ceil_div(p.block_bytes, (int64_t)pkv::kCopyThreads * 16);

@@ -62,7 +62,8 @@ def test_append_checks(L):
     assert append(L, T=-1) == SHAPE
     assert append(L, K=0) == SHAPE
     assert append(L, H=96) == UNSUP
-    assert append(L, bs=32) == UNSUP
+    assert append(L, bs=8) == UNSUP
+    assert append(L, bs=64) == UNSUP
     assert append(L, kc=MIS) == ALIGN
     assert append(L, slots=A + 4) == ALIGN
 
@@ -84,6 +85,7 @@ def test_decode_checks(L):
     assert decode(L, H=80) == UNSUP
     assert decode(L, bs=8) == UNSUP
     assert decode(L, maxctx=257) == SHAPE                 # > max_blocks * block_size
+    assert decode(L, bs=32, maxctx=513) == SHAPE          # > 16 blocks of 32
     assert decode(L, part=48) == SHAPE                    # not a multiple of 32
     assert decode(L, part=2048) == SHAPE                  # above the largest partition
     assert decode(L, scale=float("inf")) == SHAPE
@@ -286,7 +288,7 @@ def test_noalloc_checks(L):
     assert noalloc(L, K=0) == SHAPE
     assert noalloc(L, N=6, K=4) == SHAPE
     assert noalloc(L, H=96) == UNSUP
-    assert noalloc(L, bs=32) == UNSUP
+    assert noalloc(L, bs=64) == UNSUP
     assert noalloc(L, part=48) == SHAPE
     assert noalloc(L, q=MIS) == ALIGN
     # 65,535 sequences of 64 heads, token-balanced: far more than 64 MiB of pieces.

@@ -6,7 +6,8 @@ context lengths that mix empty contexts, one-token contexts, exact multiples
 of the block and of the 32-token chunk, and arbitrary lengths up to 1,500,
 a partitioning (token-balanced or fixed partitions of 32 to 1,024 tokens),
 bf16 or FP8 pools, and for a third of the cases a sliding window; the
-multi-query cases add 2 to 6 query tokens per sequence.  The append is
+multi-query cases add 2 to 6 query tokens per sequence.  A third set of
+cases repeats the draws with blocks of 32 tokens.  The append is
 checked bit-exact on the whole pools and every output row against the
 oracle (the lesson's step-2 softmax, gathered through the block table).
 """
@@ -40,7 +41,7 @@ def draw_contexts(rng, B):
     return picks
 
 
-def draw(seed, queries=1):
+def draw(seed, queries=1, bs=16):
     rng = random.Random(seed)
     G = rng.choice([1, 2, 4, 8, 16])
     K = rng.choice([1, 2, 4, 8]) if G < 16 else rng.choice([1, 2])
@@ -56,19 +57,20 @@ def draw(seed, queries=1):
     else:
         part = rng.choice([0, 0, 0, 32, 64, 96, 256, 1024])
         window = rng.choice([0, 0, rng.randint(1, 600)])
-    spec = W.Spec(f"random{seed}", B=B, N=G * K, K=K, H=Hd, ctx=ctx,
-                  max_blocks=(max(ctx) + 15) // 16 + 3, seed=seed, kv_dtype=kv, queries=queries)
+    spec = W.Spec(f"random{seed}", B=B, N=G * K, K=K, H=Hd, bs=bs, ctx=ctx,
+                  max_blocks=(max(ctx) + bs - 1) // bs + 3, seed=seed, kv_dtype=kv,
+                  queries=queries)
     return spec, part, window
 
 
 def describe(spec, part, window):
-    return (f"B={spec.B} N={spec.N} K={spec.K} H={spec.H} {spec.kv_dtype} Q={spec.queries} "
+    return (f"B={spec.B} N={spec.N} K={spec.K} H={spec.H} bs={spec.bs} {spec.kv_dtype} "
+            f"Q={spec.queries} "
             f"partition={part} window={window} ctx={list(spec.ctx)[:10]}")
 
 
-@pytest.mark.parametrize("seed", range(7000, 7200))
-def test_single_query(seed):
-    spec, part, window = draw(seed)
+def single_query(seed, bs):
+    spec, part, window = draw(seed, bs=bs)
     what = f"random {seed}: {describe(spec, part, window)}"
     H.log(f"case {what}")
     w = W.make(spec)
@@ -87,10 +89,9 @@ def test_single_query(seed):
     H.assert_parity(out.cpu().numpy(), ref, what)
 
 
-@pytest.mark.parametrize("seed", range(7300, 7360))
-def test_multi_query(seed):
+def multi_query(seed, bs):
     Q = random.Random(seed).randint(2, 6)
-    spec, part, _ = draw(seed, queries=Q)
+    spec, part, _ = draw(seed, queries=Q, bs=bs)
     what = f"random mq {seed}: {describe(spec, part, 0)}"
     H.log(f"case {what}")
     w = W.make(spec)
@@ -98,3 +99,23 @@ def test_multi_query(seed):
     out, g = H.gpu_step_mq(w, part)
     H.assert_append_exact(g, inp, what)
     H.assert_parity(out.numpy(), ref, what)
+
+
+@pytest.mark.parametrize("seed", range(7000, 7200))
+def test_single_query(seed):
+    single_query(seed, 16)
+
+
+@pytest.mark.parametrize("seed", range(7300, 7360))
+def test_multi_query(seed):
+    multi_query(seed, 16)
+
+
+@pytest.mark.parametrize("seed", range(7400, 7480))
+def test_single_query_blocks_of_32(seed):
+    single_query(seed, 32)
+
+
+@pytest.mark.parametrize("seed", range(7500, 7530))
+def test_multi_query_blocks_of_32(seed):
+    multi_query(seed, 32)
