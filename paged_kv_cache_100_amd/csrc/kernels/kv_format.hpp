@@ -147,8 +147,10 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1)
 
 struct KvFp8 {
     using Elem = uint8_t;
-    // An FP8 chunk is 32 registers per lane.  Rings of 5 and 4 (16 and 12
-    // KiB in flight per wave) measured as fast as deeper ones (up to 8 and 5).
+    // An FP8 chunk is 32 registers per lane.  The fixed-partition ring of 5
+    // (32 KiB in flight per wave) measured as fast as deeper ones (up to 8);
+    // the token-balanced kernel runs at least as fast with 2 (one chunk in
+    // flight while one is computed) as with 3 or 4.
     static constexpr int kRing = 5;
     static constexpr int kBalancedRing = 2;
 
