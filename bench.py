@@ -24,6 +24,7 @@ workload on this host.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -218,7 +219,12 @@ def measure(args, workload: str, K: int, warmup: int, probe: dict) -> dict:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     t0 = time.time()
-    w = W.make(workload, poison=False)
+    spec = W.SPECS[workload]
+    if args.block_size and args.block_size != spec.bs:
+        # same contexts, tables sized for the other block size
+        mb = -(-spec.max_blocks * spec.bs // args.block_size) if spec.max_blocks else None
+        spec = dataclasses.replace(spec, bs=args.block_size, max_blocks=mb)
+    w = W.make(spec, poison=False)
     s = w.spec
     gen_s = time.time() - t0
     g = w.to(dev)
@@ -361,7 +367,8 @@ def measure(args, workload: str, K: int, warmup: int, probe: dict) -> dict:
     achieved = nbytes[alg_key] / (roof_ms * 1e-3) / 1e9
     value = nbytes["kv"] / (ms_per_step * 1e-3) / 1e9
     name = workload + ("_prefix" if prefix else "") + \
-        (f"_window{args.window}" if args.window > 0 else "")
+        (f"_window{args.window}" if args.window > 0 else "") + \
+        (f"_bs{s.bs}" if s.bs != W.SPECS[workload].bs else "")
     traffic = traffic_from_profile(name)
     del g, workspace, out
     torch.cuda.empty_cache()
@@ -417,6 +424,8 @@ def main() -> int:
                          "prefixes)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend each sequence's last W positions (0 = all)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per cache block, 16 or 32 (default: the workload's own, 16)")
     ap.add_argument("--cold", action="store_true",
                     help="also time each attention call after a cache-evicting read "
                          "(always done for K/V working sets under 512 MB)")

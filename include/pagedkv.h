@@ -37,6 +37,11 @@
  *   - `stream` is a hipStream_t passed as `void*` (NULL = the null stream).
  *     Calls only enqueue work on that stream; they never synchronise, so
  *     buffers must stay alive until the stream has run the work.
+ *   - Calls can be captured into a HIP graph: they enqueue only kernel
+ *     launches (no memset, copy or allocation), and a replay reads the
+ *     device buffers as they are at replay time (context lengths, block
+ *     tables, queries may change between replays within the sizes given at
+ *     capture).
  *   - Every argument check happens on the host before any launch.  The return
  *     value is PKV_OK (0) or a negative pkv_status; nothing is enqueued when
  *     a check fails.  Values stored in device memory (block ids, slots,
@@ -274,7 +279,9 @@ int paged_decode_attention_fp8(float *out, const void *q,
  * exchange of a per-call 64-bit tag in the workspace (a process-wide
  * counter from a random start), so the workspace needs no clearing; the
  * merge takes the partitions in order with the merge launch's arithmetic, so
- * the result is the same whichever wave merges.
+ * the result is the same whichever wave merges.  A call made while its
+ * stream is being captured into a graph takes the merge launch instead (a
+ * replay repeats the captured tag), with the same result.
  */
 size_t paged_decode_mq_workspace_size(int32_t num_seqs, int32_t num_queries, int32_t num_heads,
                                       int32_t head_dim, int32_t max_context_len,

@@ -255,6 +255,19 @@ const void *merge_pieces_for(int head_dim, int group)
                            : merge_pieces_h<64, kPrefix>(group);
 }
 
+// True when `stream` is being captured into a graph (or its state cannot be
+// read).  A graph replays each launch with the arguments fixed at capture,
+// so a launch that relies on a fresh per-call value must not be captured.
+bool stream_capturing(void *stream)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
 int launch(const void *kernel, dim3 grid, dim3 block, void *params, void *stream)
 {
     void *args[] = {params};
@@ -692,8 +705,11 @@ int decode_mq_launch(pkv::DecodeParams &p, int head_dim, int32_t num_seqs, int32
     if (waves > INT32_MAX)
         return PKV_ERR_SHAPE;
     // Two partitions: the second partition wave of each pair merges (no
-    // merge launch).
-    const bool pair = split && parts == 2 && per_wave < pkv::kMaxQueryTiles;
+    // merge launch).  The pair tags need a new value per call, which a graph
+    // replay would not bring, so a captured call takes the merge launch (same
+    // arithmetic, same result).
+    const bool pair = split && parts == 2 && per_wave < pkv::kMaxQueryTiles &&
+                      !stream_capturing(stream);
     if (pair) {
         p.pair_tags = reinterpret_cast<uint64_t *>(
             static_cast<char *>(workspace) +

@@ -38,13 +38,15 @@ def run_pair(w, partition):
     return got.cpu(), ref.cpu()
 
 
+@pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("partition", [0, 64])
-def test_two_calls_match_workspace_call(partition):
-    big = W.small("llama3_70b_ragged_b100")
-    small = W.Spec("noalloc small", B=5, N=32, K=8, H=128, ctx=[1, 300, 47, 0, 129], seed=71)
+def test_two_calls_match_workspace_call(partition, bs):
+    big = W.small("llama3_70b_ragged_b100", bs=bs, max_blocks=96 * 16 // bs)
+    small = W.Spec("noalloc small", B=5, N=32, K=8, H=128, bs=bs, ctx=[1, 300, 47, 0, 129],
+                   seed=71)
     for spec in (big, small):
         w = W.make(spec)
-        H.log(f"case noalloc {spec.name} B={spec.B} partition={partition} "
+        H.log(f"case noalloc {spec.name} B={spec.B} bs={bs} partition={partition} "
               f"ctx={w.context_lens.tolist()[:8]}")
         got, ref = run_pair(w, partition)
         assert torch.equal(got, ref), "differs from paged_decode_attention"
