@@ -172,18 +172,24 @@ def cpu_baseline(w, budget_s: float = 12.0, window: int = 0) -> dict:
                       f"{spent:.1f} s"}
 
 
+PROBE_READ_BYTES = 4 << 30      # streaming-read probe (the achievable read bandwidth)
+PROBE_COPY_BYTES = 1 << 30      # copy probe (scales the write counter)
+
+
 def probe_bandwidth(pkv, torch, dev) -> dict:
-    """Achievable bandwidth: a 1 GiB streaming read in the decode kernels'
-    access pattern, and a 1 GiB plain copy (their known sizes also scale the
-    HBM byte counters in a profiler run of this script)."""
-    probe_bytes = 1 << 30
-    probe_src = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
-    probe_dst = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
-    sink = pkv.stream_read(probe_src)
-    pkv.stream_copy(probe_src, probe_dst)
+    """Achievable bandwidth: the fastest of five 4 GiB streaming reads in the
+    decode kernels' access pattern (long enough that its start-up and tail
+    weigh less than the decode's), and a 1 GiB plain copy (median of five).
+    Their known sizes also scale the HBM byte counters in a profiler run of
+    this script."""
+    read_src = torch.empty(PROBE_READ_BYTES, dtype=torch.uint8, device=dev)
+    copy_src = read_src[:PROBE_COPY_BYTES]
+    copy_dst = torch.empty(PROBE_COPY_BYTES, dtype=torch.uint8, device=dev)
+    sink = pkv.stream_read(read_src)
+    pkv.stream_copy(copy_src, copy_dst)
     torch.cuda.synchronize()
 
-    def median_ms(fn, reps=5):
+    def times_ms(fn, reps=5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ts = []
         for _ in range(reps):
@@ -192,12 +198,12 @@ def probe_bandwidth(pkv, torch, dev) -> dict:
             e1.record()
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+        return sorted(ts)
 
-    read = probe_bytes / (median_ms(lambda: pkv.stream_read(probe_src, sink)) * 1e-3) / 1e9
-    copy = 2 * probe_bytes / (median_ms(lambda: pkv.stream_copy(probe_src, probe_dst))
-                              * 1e-3) / 1e9
-    del probe_src, probe_dst
+    read = PROBE_READ_BYTES / (times_ms(lambda: pkv.stream_read(read_src, sink))[0] * 1e-3) / 1e9
+    copy_t = times_ms(lambda: pkv.stream_copy(copy_src, copy_dst))
+    copy = 2 * PROBE_COPY_BYTES / (copy_t[len(copy_t) // 2] * 1e-3) / 1e9
+    del read_src, copy_src, copy_dst
     return {"read": read, "copy": copy}
 
 
