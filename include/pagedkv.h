@@ -181,8 +181,16 @@ size_t paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t 
  * access; that sequence's result is unspecified).
  * Arithmetic: bf16 inputs, fp32 accumulation (matrix cores for q.K^T and
  * P.V, with P carried as a two-term bf16 sum), fp32 output.  The result is
- * bit-deterministic for given inputs, partition_size and device: no atomics,
- * and the reduction order depends only on logical positions.
+ * bit-deterministic for given inputs, partition_size, max_context_len and
+ * device: no atomics, and the reduction order depends only on logical
+ * positions and the kernels the host picks.  With partition_size 0, a batch
+ * whose num_seqs * num_kv_heads pairs, four waves each, fit one round of the
+ * device's waves (4 per compute unit) and whose max_context_len spans at
+ * most 256 KiB of keys and values per pair (512 tokens of bf16 at head_dim
+ * 128, 1,024 of FP8 or at head_dim 64) runs as one launch (a workgroup per
+ * pair merging its four waves' partial results in LDS); otherwise on the
+ * persistent token-balanced kernel.  Within each, a larger max_context_len gives the same bits; the
+ * two agree to rounding (about 1e-6 relative).
  */
 int paged_decode_attention(float *out, const void *q,
                            const void *key_cache, const void *value_cache,

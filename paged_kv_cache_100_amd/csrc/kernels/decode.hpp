@@ -426,6 +426,159 @@ void decode_kernel(DecodeParams p)
         *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = acc[c] * inv;
 }
 
+// Small batches, one launch: a workgroup of kSplitWaves waves per (KV head,
+// sequence).  Wave w attends chunks [n w / kSplitWaves, n (w + 1) /
+// kSplitWaves) of the n chunks from the window start, then the waves' partial
+// results (running maximum m, sum l, unnormalised output o, per query column)
+// are combined through LDS by the log-sum-exp rule of the split-K merge:
+// M = max m_w, out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, taken in
+// wave order.  No partials go to global memory and no merge launch follows,
+// which is what a small batch spends most of its time on.  The host uses it
+// when the batch's (sequence, KV head) pairs times kSplitWaves fit one round
+// of waves and a context holds at most kSplitMaxBytes of keys and values
+// (and at most kSplitMaxChunks chunks, so each wave's block ids fit its
+// lanes): a workgroup runs on one compute unit, and past that size one
+// unit's share of the bandwidth makes it slower than spreading the pair over
+// the chip.
+constexpr int kSplitWaves = 4;
+constexpr int kSplitMaxChunks = 32 * kSplitWaves;
+constexpr int64_t kSplitMaxBytes = 256 * 1024;
+
+template <class Fmt, int H, int BS = kBlockSize>
+__global__ __launch_bounds__(kWave * kSplitWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_split_kernel(DecodeParams p)
+{
+    const int kvh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = threadIdx.x % kWave;
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+    const bool live = col < p.group;
+    const int n = kvh * p.group + col;
+    float *o = p.out + ((int64_t)b * p.num_heads + n) * H;
+
+    const int ctx = min(max(scalar_load(p.context_lens + b), 0), p.max_ctx);
+    if (ctx == 0) {                       // empty sequence: zeros (every wave leaves here)
+        if (wv == 0 && live)
+#pragma unroll
+            for (int c = 0; c < H / 16; ++c)
+                *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = f32x4{0.f, 0.f, 0.f, 0.f};
+        return;
+    }
+    const int lo = window_start(p, ctx);
+    const int cbeg = lo - lo % kChunk;    // chunks start at the 32-token boundary below lo
+    const int head = lo - cbeg;           // masked leading positions of chunk 0
+    const int n_full = (ctx - cbeg) / kChunk;
+    const int tail_rem = ctx - cbeg - n_full * kChunk;
+    const int total = n_full + (tail_rem != 0);
+    const int c0 = total * wv / kSplitWaves;
+    const int n_chunks = total * (wv + 1) / kSplitWaves - c0;
+
+    // This wave's block ids, one per lane (at most 32 chunks: 64 blocks of 16).
+    const int bfirst = (cbeg + kChunk * c0) / BS;
+    const int n_blocks = (ctx - 1) / BS + 1;
+    const int32_t *table = p.block_tables + (int64_t)b * p.max_blocks;
+    int my_id = 0;
+    if (bfirst + lane < n_blocks)
+        my_id = table[bfirst + lane];
+    my_id = clamp_block(my_id, p.num_blocks);
+
+    bf16x8 qf[H / 32];
+    {
+        const uint16_t *qrow = p.q + ((int64_t)b * p.num_heads + (live ? n : 0)) * H;
+#pragma unroll
+        for (int s = 0; s < H / 32; ++s) {
+            u32x4 raw = load16(qrow + Fmt::dim_offset(s, quad));
+            if (!live)
+                raw = u32x4{0u, 0u, 0u, 0u};
+            qf[s] = as_bf16x8(raw ^ p.q_sign);
+        }
+    }
+
+    const int64_t tile_elems = (int64_t)BS * H;
+    const int64_t block_elems = (int64_t)p.num_kv_heads * tile_elems;
+    using Elem = typename Fmt::Elem;
+    using Regs = typename Fmt::template Regs<H>;
+    const Elem *kbase = static_cast<const Elem *>(p.key_cache) + kvh * tile_elems;
+    const Elem *vbase = static_cast<const Elem *>(p.value_cache) + kvh * tile_elems;
+
+    auto issue = [&](Regs &r, int ci) {
+        const int k0 = (kChunk / BS) * ci;    // table entry of the chunk, from bfirst
+        const int id0 = __builtin_amdgcn_readlane(my_id, k0);
+        const int id1 = (BS == 16 && bfirst + k0 + 1 < n_blocks)
+                            ? __builtin_amdgcn_readlane(my_id, k0 + 1)
+                            : id0;
+        const uint64_t o0 = (uint64_t)id0 * block_elems, o1 = (uint64_t)id1 * block_elems;
+        Fmt::template load<H, BS>(r, kbase + o0, kbase + key_hi<BS, H>(o1), vbase + o0,
+                                  vbase + value_hi<BS>(o1), col, quad);
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[H / 16];
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c)
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto qfrag = [&](int s) { return qf[s]; };
+    auto attend = [&](const Regs &r, int ci) {
+        const int g = c0 + ci;                // chunk index from cbeg
+        const bool front = g == 0 && head > 0;
+        if (g < n_full && !front)
+            attend_chunk<Fmt, H, false>(r, qfrag, kChunk, 0, quad, p.scale_log2, m, l, acc);
+        else
+            attend_chunk<Fmt, H, true>(r, qfrag, g < n_full ? kChunk : tail_rem,
+                                       front ? head : 0, quad, p.scale_log2, m, l, acc);
+    };
+    if (n_chunks > 0) {
+        Regs ring[Fmt::kRing];
+        run_ring<Fmt::kRing>(n_chunks, ring, issue, attend);
+    }
+    l = sum_over_rows(l);                 // each lane summed its own 8 tokens per chunk
+
+    // Partials to LDS: acc[c] holds O^T[16c + 4quad + i][col], i = 0..3; m
+    // and l are the same in the four quads of a column.
+    __shared__ float s_m[kSplitWaves][16];
+    __shared__ float s_l[kSplitWaves][16];
+    __shared__ f32x4 s_o[kSplitWaves][H / 16][kWave];
+    if (quad == 0) {
+        s_m[wv][col] = m;
+        s_l[wv][col] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c)
+        s_o[wv][c][lane] = acc[c];
+    __syncthreads();
+
+    // Wave w combines the output tiles c = w, w + kSplitWaves, ...
+    float mw[kSplitWaves];
+    float big = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+        mw[w] = s_m[w][col];
+        big = mw[w] > -INFINITY ? fmaxf(big, mw[w]) : big;
+    }
+    float e[kSplitWaves];
+    float den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSplitWaves; ++w) {
+        e[w] = mw[w] > -INFINITY ? __builtin_amdgcn_exp2f(mw[w] - big) : 0.f;
+        den += e[w] * s_l[w][col];
+    }
+    if (!live)
+        return;
+    const float inv = den > 0.f ? p.out_scale / den : 0.f;
+#pragma unroll
+    for (int c = 0; c < H / 16; ++c) {
+        if (c % kSplitWaves != wv)
+            continue;
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kSplitWaves; ++w)
+            sum += s_o[w][c][lane] * e[w];
+        *reinterpret_cast<f32x4 *>(o + 16 * c + 4 * quad) = sum * inv;
+    }
+}
+
 struct MergeParams {
     float *out;                   // [B][Q][N][H]
     const float *part_o;          // [B][Q][N][P][H]

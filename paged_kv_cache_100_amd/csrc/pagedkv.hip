@@ -537,6 +537,17 @@ int check_decode(float *out, const void *q, const void *key_cache, const void *v
     return PKV_OK;
 }
 
+// The one-launch small-batch kernel for a head dim and block size.
+template <class Fmt>
+const void *split_kernel(int head_dim, int block_size)
+{
+    const bool bs32 = block_size == 32;
+    return head_dim == 128 ? (bs32 ? (const void *)pkv::decode_split_kernel<Fmt, 128, 32>
+                                   : (const void *)pkv::decode_split_kernel<Fmt, 128, 16>)
+                           : (bs32 ? (const void *)pkv::decode_split_kernel<Fmt, 64, 32>
+                                   : (const void *)pkv::decode_split_kernel<Fmt, 64, 16>);
+}
+
 template <class Fmt>
 int decode_impl(float *out, const void *q, const void *key_cache, const void *value_cache,
                 const int32_t *block_tables, const int32_t *context_lens, float scale,
@@ -594,6 +605,24 @@ int decode_impl(float *out, const void *q, const void *key_cache, const void *va
             return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace))
             return PKV_ERR_ALIGN;
+        // Small batches: when each (sequence, KV head) pair's workgroup fits
+        // one round of waves and reads at most kSplitMaxBytes, one launch
+        // whose workgroups merge in LDS.  A workgroup runs on one compute
+        // unit, whose share of the bandwidth bounds it: past that size the
+        // persistent kernel, spread over every unit, is faster even with its
+        // merge launch.
+        int log2_waves = 0;
+        const int rc = device_waves(&log2_waves);
+        if (rc != PKV_OK)
+            return rc;
+        const int64_t chunks = ceil_div(max_context_len, pkv::kChunk);
+        const int64_t chunk_bytes =
+            (int64_t)pkv::kChunk * head_dim * (int64_t)sizeof(typename Fmt::Elem) * 2;
+        if ((int64_t)num_seqs * num_kv_heads * pkv::kSplitWaves <= ((int64_t)1 << log2_waves) &&
+            chunks <= pkv::kSplitMaxChunks && chunks * chunk_bytes <= pkv::kSplitMaxBytes)
+            return launch(split_kernel<Fmt>(head_dim, block_size),
+                          dim3((unsigned)num_kv_heads, (unsigned)num_seqs),
+                          dim3(pkv::kWave * pkv::kSplitWaves), &p, stream);
         return balanced_launch<Fmt, false>(p, head_dim, num_seqs, num_kv_heads, L,
                                            static_cast<char *>(workspace), 0, stream);
     }
