@@ -84,6 +84,7 @@ def test_decode_checks(L):
     assert decode(L, N=64, K=2) == UNSUP                  # group of 32 > 16
     assert decode(L, H=80) == UNSUP
     assert decode(L, bs=8) == UNSUP
+    assert decode(L, B=65536) == SHAPE                    # past the merge grid's rows
     assert decode(L, maxctx=257) == SHAPE                 # > max_blocks * block_size
     assert decode(L, bs=32, maxctx=513) == SHAPE          # > 16 blocks of 32
     assert decode(L, part=48) == SHAPE                    # not a multiple of 32
