@@ -205,8 +205,10 @@ def _decode_args(out, q, key_cache, value_cache, block_tables, context_lens, num
     max_blocks = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = max_blocks * block_size
-    need = workspace_size(B, N, K, H, max_context_len, partition) if B and allocate else 0
-    if need and workspace is None:
+    # the size is only needed to allocate one (the library checks a given one)
+    need = (workspace_size(B, N, K, H, max_context_len, partition)
+            if B and allocate and workspace is None else 0)
+    if need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     pw, wbytes = 0, 0
     if workspace is not None:
@@ -319,8 +321,8 @@ def paged_decode_attention_mq(out: torch.Tensor, q: torch.Tensor, key_cache: tor
     max_blocks = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = max_blocks * block_size
-    need = mq_workspace_size(B, Q, N, H, max_context_len, partition) if B else 0
-    if need and workspace is None:
+    need = mq_workspace_size(B, Q, N, H, max_context_len, partition) if B and workspace is None else 0
+    if need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     pw, wbytes = 0, 0
     if workspace is not None:
